@@ -1,0 +1,172 @@
+#!/usr/bin/env python3
+"""Benchmark: MLA decode KV-cache GB/s and tokens/s at the DeepSeek-V3 shape.
+
+One step = the whole hot path over one batch: mla_cache_insert of the new
+token(s) (kv_a RMSNorm + RoPE + paged write) followed by mla_decode (query
+absorption, split-KV decode, merge + per-head projection).  Workload: batch
+64, q_len 1, 128 heads, every context 8192 positions, 64-position pages in a
+random block order, seeded synthetic bf16 data (see workloads.py).
+
+Prints ONE JSON line.  ``value`` is KV-cache bytes streamed per second
+(sum of context lengths x 1152 bytes / step time) with all inputs resident in
+HBM; ``roofline`` reports the split-KV decode kernel alone, timed with HIP
+events recorded by the library on the launch stream; ``cpu_baseline`` times the
+float64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, published
+WORKLOAD = "v3_b64_l8192"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-clock budget of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "decode_kernel_traffic.json"),
+                    help="HBM traffic of the decode kernel measured with rocprofv3 counters")
+    return ap.parse_args()
+
+
+def cpu_baseline(d, budget_s: float) -> dict:
+    """Time the float64 oracle (insert + expanded-form decode) sequence by
+    sequence until the budget is spent; scale to KV GB/s like the GPU figure."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import cache_insert, decode_expanded
+    import workloads as wl
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    eps = float(np.float32(wl.EPS))
+    t0 = time.perf_counter()
+    ref_cache = cache_insert(d["cache"], d["kv_a"], d["rms_w"], d["block_table"], d["seq_lens"],
+                             d["q_len"], eps, wl.ROPE_BASE, wl.LATENT)
+    t_insert = time.perf_counter() - t0
+    done, tokens, t_dec = 0, 0, 0.0
+    while done < d["batch"] and t_dec < budget_s:
+        t1 = time.perf_counter()
+        decode_expanded(d["q"], d["kv_b"], ref_cache, d["block_table"], d["seq_lens"], d["q_len"],
+                        batches=[done])
+        t_dec += time.perf_counter() - t1
+        tokens += int(d["seq_lens"][done])
+        done += 1
+    # insert cost is for the whole batch; charge the sampled share of it
+    t = t_dec + t_insert * done / d["batch"]
+    return {"value": round(tokens * wl.BYTES_PER_TOKEN / t / 1e9, 4), "unit": "GB/s",
+            "tokens_per_s": round(done * d["q_len"] / t, 3), "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {d['batch']} sequences ({tokens} cached positions, all "
+                      f"{d['heads']} heads) of {d['name']}: float64 expanded-form decode plus "
+                      f"its share of the insert, {t:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import mla_latent_kv_07_amd as mla
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    d = wl.make_workload(args.workload)
+    bsz, q_len, heads = d["batch"], d["q_len"], d["heads"]
+    seq_lens = d["seq_lens"]
+    max_len = int(seq_lens.max())
+    to = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+                    if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda())
+    cache, kv_a, rms_w = to(d["cache"]), to(d["kv_a"]), to(d["rms_w"])
+    q, kv_b = to(d["q"]), to(d["kv_b"])
+    bt, sl = to(d["block_table"]), to(d["seq_lens"])
+    out = torch.empty((bsz, q_len, heads, wl.VDIM), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.decode_workspace_bytes(heads, bsz, q_len, max_len), dtype=torch.uint8,
+                     device="cuda")
+    eps = float(np.float32(wl.EPS))
+
+    def step():
+        mla.cache_insert(kv_a, rms_w, bt, sl, cache, eps=eps, heads=heads)
+        mla.decode(q, kv_b, cache, bt, sl, max_len, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    mla.profile_enable(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms, calls = mla.profile_collect()
+    mla.profile_enable(0)
+    assert calls == args.steps
+    ms_step = wall * 1e3 / args.steps
+    kv_bytes = int(seq_lens.sum()) * wl.BYTES_PER_TOKEN
+    alg_bytes = wl.decode_bytes(seq_lens, bsz, q_len, heads, bt.numel())
+    alg_flops = wl.decode_flops(seq_lens, bsz, q_len, heads)
+    dec_ms = stage_ms["decode"] / calls
+    dec_gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic):
+        tr = json.load(open(args.traffic))
+        if tr.get("workload") == args.workload and tr.get("kernel_source_sha") == kernel_sha():
+            traffic = tr.get("bytes_per_launch")
+    result = {
+        "metric": "MLA decode KV-cache GB/s & tokens/s at V3 shape; % of HBM roofline",
+        "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": bsz, "q_len": q_len, "heads": heads,
+                   "context": "8192 each" if args.workload == WORKLOAD else "see workloads.py",
+                   "page": 64, "kv_lora": 512, "rope": 64, "step": "cache_insert + decode"},
+        "tokens_per_s": round(bsz * q_len / (ms_step * 1e-3), 1),
+        "alg_bytes_per_step": alg_bytes,
+        "alg_flops_per_step": alg_flops,
+        "step_alg_hbm_frac": round(alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "stage_ms": {k: round(v / calls, 4) for k, v in stage_ms.items()},
+        "roofline": {"kernel": "mla::decode_kernel (split-KV decode)", "bound": "hbm",
+                     "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "per_unit": "1152 B per cached position (576 bf16)",
+                     "units_per_launch": int(seq_lens.sum()),
+                     "mfma_tflops": round(2 * heads * wl.visible_pairs(seq_lens, q_len)
+                                          * (wl.ENTRY + wl.LATENT) / (dec_ms * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(2 * heads * wl.visible_pairs(seq_lens, q_len)
+                                        * (wl.ENTRY + wl.LATENT) / (dec_ms * 1e-3) / 1e12
+                                        / MFMA_BF16_PEAK_TFS, 4)},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def kernel_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("decode.hip", "mla_common.h"):
+        h.update(open(os.path.join(ROOT, "mla_latent_kv_07_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * mla.h — C ABI of libmla: DeepSeek Multi-head Latent Attention (MLA) decode
+ * over a paged latent KV cache, and the fused cache-insert step, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Operations follow these pages (titles and sections as the pages give them):
+ *   [V3-src] "深度解读DeepSeek：源码解读 DeepSeek-V3", section "MLA": the
+ *            listing of MLA.forward and its subsections "(a) Naive实现" and
+ *            "(b) 优化实现" (absorbed form: q_nope is multiplied by the first
+ *            qk_nope rows of each head's kv_b block, scores are taken against
+ *            the normalised latent plus the rope part, the softmax weights sum
+ *            the latent rows, and the result is multiplied by the last v_dim
+ *            rows of each head's block).
+ *   [V2L]    "DeepSeek-V2-Lite 模型结构详解", §四 RMSNorm (row rule, float32
+ *            arithmetic) and §五 MLA (one 576-number cache entry per token:
+ *            512 latent + 64 rope; the two absorption identities).
+ *   [TAGS]   the "DeepSeek" tag page: excerpt on the 1/sqrt(d_k) scale, and
+ *            excerpt on MLA under decode context parallelism (decode runs as
+ *            one shared latent head of width 576).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or retains them.  bf16 means IEEE
+ *     bfloat16 bit patterns (uint16), all tensors are dense row-major.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous: they only enqueue kernels.  Arguments are validated on the
+ *     host before anything is enqueued; a non-zero status means nothing ran.
+ *   - Values stored in device arrays (block_table entries, seq_lens) are the
+ *     caller's contract and are not checked: every used block id must lie in
+ *     [0, num_blocks), and q_len <= seq_lens[b] <= max_seq_len.
+ *   - Supported dimensions: kv_lora 512, rope 64, qk_nope 128, v_dim 128,
+ *     page 64, heads a multiple of 16 in [16, 128], 1 <= q_len <= 8.
+ *   - Thread safety: calls are re-entrant; two calls that share a workspace
+ *     or an output buffer must be ordered by the caller (same stream).
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,         /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,        /* a size argument is out of range or inconsistent */
+  MLA_ERR_UNSUPPORTED = 3,  /* dimensions this build does not implement */
+  MLA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
+  MLA_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+} mla_status;
+
+/* Model dimensions ([V3-src] MLA: kv_lora_rank, qk_rope_head_dim,
+ * qk_nope_head_dim, v_head_dim; `heads` = heads served by this call). */
+typedef struct {
+  int32_t heads;    /* H */
+  int32_t kv_lora;  /* latent width, must be 512 */
+  int32_t rope;     /* rope width, must be 64 */
+  int32_t qk_nope;  /* must be 128 */
+  int32_t v_dim;    /* must be 128 */
+  int32_t page;     /* tokens per cache block, must be 64 */
+} mla_dims;
+
+/*
+ * mla_cache_insert — write the q_len new tokens of each sequence into the
+ * paged cache ([V3-src] absorbed branch: the latent goes through kv_norm and
+ * k_pe through the rotary embedding before both are cached; [V2L] §五: the
+ * entry is latent followed by k_pe).
+ *
+ *   kv_a        bf16 [B, q_len, 576]  kv_a projection output of the new tokens
+ *   rms_w       bf16 [512]            kv_a RMSNorm weight
+ *   eps         RMSNorm epsilon, added inside the square root ([V2L] §四)
+ *   rope_base   RoPE frequency base; pair j of the 64-wide k_pe, taken as
+ *               (real, imaginary) = elements (2j, 2j+1), turns by
+ *               position * rope_base^(-2j/64)
+ *   block_table int32 [B, bt_stride]  physical block of each logical block
+ *   seq_lens    int32 [B]  cache length INCLUDING the new tokens; new token i
+ *               of sequence b sits at position seq_lens[b] - q_len + i
+ *   cache       bf16 [num_blocks, 64, 576], updated in place; only the
+ *               B*q_len addressed entries are written
+ *
+ * Latent: per row, sum of squares in a wide type, n = x / sqrt(mean + eps)
+ * rounded to bf16, then weight * n rounded to bf16 ([V2L] §四 precision
+ * rule).  k_pe: rotated in double precision, rounded once to bf16.
+ * B == 0 is a no-op returning MLA_OK.
+ */
+int mla_cache_insert(const mla_dims* dims, const void* kv_a, const void* rms_w,
+                     float eps, float rope_base, const int32_t* block_table,
+                     int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
+                     int32_t q_len, void* cache, int32_t num_blocks, void* stream);
+
+/*
+ * mla_decode_workspace_bytes — size in bytes of the device workspace
+ * mla_decode needs for these sizes (split plan, absorbed queries, per-split
+ * partial results).  `num_splits_hint` must match the value later passed to
+ * mla_decode.  Returns 0 for unsupported arguments.
+ */
+size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                  int32_t max_seq_len, int32_t num_splits_hint);
+
+/*
+ * mla_decode — absorbed MLA decode over the paged cache ([V3-src] "(b)
+ * 优化实现"; [TAGS] decode as one latent head; [V2L] §五 identities).
+ *
+ *   q           bf16 [B, q_len, H, 192]: q_nope (128) then q_pe (64), q_pe
+ *               already rotated to its position
+ *   kv_b        bf16 [H*256, 512]: kv_b_proj weight; rows h*256 + [0,128)
+ *               are head h's W_UK, rows h*256 + [128,256) its W_UV
+ *   cache       bf16 [num_blocks, 64, 576] (latent 512 then rope 64)
+ *   block_table int32 [B, bt_stride]; seq_lens int32 [B] (see insert)
+ *   max_seq_len host-side bound on every seq_lens[b] (sizes the plan)
+ *   softmax_scale  scale applied to q.k, normally 1/sqrt(qk_nope + rope)
+ *               ([TAGS] 1/sqrt(d_k), d_k = 128 + 64)
+ *   out         bf16 [B, q_len, H, 128]: per-head attention output before
+ *               the output projection
+ *   workspace   device buffer of at least mla_decode_workspace_bytes(...)
+ *   num_splits_hint  0 = balanced automatic split of each sequence across
+ *               the GPU; k > 0 = split every sequence into min(k, pages) parts
+ *               (k <= 64)
+ *
+ * Causality: new query i of sequence b attends to positions
+ * t <= seq_lens[b] - q_len + i (the triu(1) mask of the forward pass, moved
+ * to the cache offset).  Cache slots at positions >= seq_lens[b] are never
+ * used, whatever they hold.  Arithmetic: bf16 inputs, bf16 matrix-core
+ * products with fp32 accumulation, fp32 softmax statistics, bf16 output.
+ * B == 0 is a no-op returning MLA_OK.
+ */
+int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+               int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+               const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t max_seq_len,
+               float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+               int32_t num_splits_hint, void* stream);
+
+/*
+ * mla_profile_enable / mla_profile_collect — stage timing for benchmarks.
+ * While enabled (max_calls > 0), each mla_decode call records five HIP events
+ * on its stream: before the split planner, the query absorption, the split-KV
+ * decode kernel, the merge + projection kernel, and after it.  Events come
+ * from a pool of max_calls sets created here (hipEventCreate; no device
+ * memory); calls beyond the pool are not timed.  mla_profile_enable(0)
+ * releases the pool.  mla_profile_collect waits for the recorded events and
+ * writes, per stage, the summed milliseconds over the timed calls into
+ * stage_ms[4] (plan, absorb, decode, combine) and the call count into *calls,
+ * then empties the pool for reuse.  Not thread-safe; for benchmarks only.
+ */
+int mla_profile_enable(int32_t max_calls);
+int mla_profile_collect(double* stage_ms, int32_t* calls);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* mla_status_string(int status);
+
+/* ABI version of this header: 1. */
+int mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H */

@@ -1,0 +1,18 @@
+"""MI355X (gfx950) MLA latent-KV decode and cache insert.
+
+The compute lives in ``libmla.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/mla.h``).  This package is a thin ctypes binding with the
+same entry-point names; torch is used only for device memory and streams.
+"""
+from ._lib import (  # noqa: F401
+    MLAError,
+    abi_version,
+    cache_insert,
+    decode,
+    decode_workspace_bytes,
+    lib_path,
+    load,
+    profile_collect,
+    profile_enable,
+    status_string,
+)

@@ -1,0 +1,181 @@
+"""ctypes binding of libmla (argument marshalling only).
+
+Every step of the path runs in the HIP kernels of ``libmla.so``; this module
+checks tensor dtypes, shapes and devices, passes raw device pointers and the
+current HIP stream, and raises on a non-zero status.  There is no fallback:
+if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libmla.so"
+LATENT, ROPE, NOPE, VDIM, PAGE = 512, 64, 128, 128, 64
+
+_lib = None
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int32), ("kv_lora", ctypes.c_int32), ("rope", ctypes.c_int32),
+                ("qk_nope", ctypes.c_int32), ("v_dim", ctypes.c_int32), ("page", ctypes.c_int32)]
+
+
+def lib_path() -> str:
+    return os.path.join(PKG, LIB_NAME)
+
+
+def load() -> ctypes.CDLL:
+    """Load libmla.so (built by ``mla_latent_kv_07_amd/build.py``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python mla_latent_kv_07_amd/build.py`"
+                           " (the HIP library is required; there is no fallback)")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    DP = ctypes.POINTER(Dims)
+    lib.mla_cache_insert.argtypes = [DP, P, P, F, F, P, I32, P, I32, I32, P, I32, P]
+    lib.mla_cache_insert.restype = ctypes.c_int
+    lib.mla_decode_workspace_bytes.argtypes = [DP, I32, I32, I32, I32]
+    lib.mla_decode_workspace_bytes.restype = SZ
+    lib.mla_decode.argtypes = [DP, P, P, P, I32, P, I32, P, I32, I32, I32, F, P, P, SZ, I32, P]
+    lib.mla_decode.restype = ctypes.c_int
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_profile_enable.argtypes = [I32]
+    lib.mla_profile_enable.restype = ctypes.c_int
+    lib.mla_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I32)]
+    lib.mla_profile_collect.restype = ctypes.c_int
+    lib.mla_abi_version.argtypes = []
+    lib.mla_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().mla_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(load().mla_abi_version())
+
+
+def dims(heads: int) -> Dims:
+    return Dims(heads, LATENT, ROPE, NOPE, VDIM, PAGE)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(t, name, dtype, shape=None, device=None):
+    import torch
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+    return t
+
+
+def cache_insert(kv_a, rms_w, block_table, seq_lens, cache, *, eps: float = 1e-6,
+                 rope_base: float = 10000.0, heads: int = 16, stream=None) -> None:
+    """mla_cache_insert: kv_a bf16 [B, q_len, 576], rms_w bf16 [512],
+    block_table int32 [B, max_blocks], seq_lens int32 [B] (post-insert lengths),
+    cache bf16 [num_blocks, 64, 576] updated in place."""
+    import torch
+    bsz, q_len = kv_a.shape[0], kv_a.shape[1]
+    dev = cache.device
+    _check(kv_a, "kv_a", torch.bfloat16, (bsz, q_len, LATENT + ROPE), dev)
+    _check(rms_w, "rms_w", torch.bfloat16, (LATENT,), dev)
+    _check(block_table, "block_table", torch.int32, None, dev)
+    _check(seq_lens, "seq_lens", torch.int32, (bsz,), dev)
+    _check(cache, "cache", torch.bfloat16, (cache.shape[0], PAGE, LATENT + ROPE), dev)
+    d = dims(heads)
+    st = load().mla_cache_insert(ctypes.byref(d), _ptr(kv_a), _ptr(rms_w), eps, rope_base,
+                                 _ptr(block_table), block_table.shape[1], _ptr(seq_lens), bsz,
+                                 q_len, _ptr(cache), cache.shape[0], _stream(stream))
+    if st != 0:
+        raise MLAError(st, "mla_cache_insert")
+
+
+def decode_workspace_bytes(heads: int, batch: int, q_len: int, max_seq_len: int,
+                           num_splits_hint: int = 0) -> int:
+    d = dims(heads)
+    return int(load().mla_decode_workspace_bytes(ctypes.byref(d), batch, q_len, max_seq_len,
+                                                 num_splits_hint))
+
+
+def decode(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, *,
+           softmax_scale: float | None = None, out=None, workspace=None,
+           num_splits_hint: int = 0, stream=None):
+    """mla_decode: q bf16 [B, q_len, H, 192], kv_b bf16 [H*256, 512],
+    cache bf16 [num_blocks, 64, 576]; returns out bf16 [B, q_len, H, 128]."""
+    import torch
+    bsz, q_len, heads = q.shape[0], q.shape[1], q.shape[2]
+    dev = cache.device
+    _check(q, "q", torch.bfloat16, (bsz, q_len, heads, NOPE + ROPE), dev)
+    _check(kv_b, "kv_b", torch.bfloat16, (heads * (NOPE + VDIM), LATENT), dev)
+    _check(cache, "cache", torch.bfloat16, (cache.shape[0], PAGE, LATENT + ROPE), dev)
+    _check(block_table, "block_table", torch.int32, None, dev)
+    _check(seq_lens, "seq_lens", torch.int32, (bsz,), dev)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(NOPE + ROPE)
+    if out is None:
+        out = torch.empty((bsz, q_len, heads, VDIM), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (bsz, q_len, heads, VDIM), dev)
+    need = decode_workspace_bytes(heads, bsz, q_len, max_seq_len, num_splits_hint)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    d = dims(heads)
+    st = load().mla_decode(ctypes.byref(d), _ptr(q), _ptr(kv_b), _ptr(cache), cache.shape[0],
+                           _ptr(block_table), block_table.shape[1], _ptr(seq_lens), bsz, q_len,
+                           max_seq_len, softmax_scale, _ptr(out), _ptr(workspace),
+                           workspace.numel(), num_splits_hint, _stream(stream))
+    if st != 0:
+        raise MLAError(st, "mla_decode")
+    return out
+
+
+STAGES = ("plan", "absorb", "decode", "combine")
+
+
+def profile_enable(max_calls: int) -> None:
+    """Record HIP events around each stage of the next ``max_calls`` decodes."""
+    st = load().mla_profile_enable(int(max_calls))
+    if st != 0:
+        raise MLAError(st, "mla_profile_enable")
+
+
+def profile_collect() -> tuple[dict, int]:
+    """Summed milliseconds per stage over the timed decode calls, and their count."""
+    ms = (ctypes.c_double * 4)()
+    calls = ctypes.c_int32()
+    st = load().mla_profile_collect(ms, ctypes.byref(calls))
+    if st != 0:
+        raise MLAError(st, "mla_profile_collect")
+    return {k: ms[i] for i, k in enumerate(STAGES)}, int(calls.value)

@@ -1,0 +1,233 @@
+// libmla C ABI: argument validation, workspace layout and kernel sequencing.
+// See include/mla.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+#include <mutex>
+#include <vector>
+
+#include "../../include/mla.h"
+#include "mla_common.h"
+
+namespace {
+
+using namespace mla;
+
+constexpr int kMaxQLen = 8;
+constexpr int kMaxHint = 64;
+constexpr int kMaxBatch = 1 << 16;
+constexpr int kMaxSeqLen = 1 << 24;
+constexpr int kMaxDevices = 64;
+
+int device_cus() {
+  static std::once_flag once[kMaxDevices];
+  static int cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  std::call_once(once[dev], [dev] {
+    hipDeviceProp_t p;
+    cus[dev] = (hipGetDeviceProperties(&p, dev) == hipSuccess && p.multiProcessorCount > 0)
+                   ? p.multiProcessorCount
+                   : 256;
+  });
+  return cus[dev];
+}
+
+int check_dims(const mla_dims* d) {
+  if (!d) return MLA_ERR_NULL;
+  if (d->kv_lora != kLatent || d->rope != kRope || d->qk_nope != kNope || d->v_dim != kVdim ||
+      d->page != kPage)
+    return MLA_ERR_UNSUPPORTED;
+  if (d->heads < 16 || d->heads > 128 || d->heads % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  int max_items = 0;
+  int slots = 0;
+  DecodeConfig cfg{};
+  size_t off_header = 0, off_item_b = 0, off_item_p0 = 0, off_item_p1 = 0, off_seq_start = 0,
+         off_seq_count = 0, off_qabs = 0, off_opart = 0, off_lse = 0, total = 0;
+};
+
+// Workspace layout for one decode call (pure function of the sizes).
+Layout make_layout(int heads, int batch, int q_len, int hint) {
+  Layout L;
+  const int rows = heads * q_len;
+  L.cfg = decode_config(rows);
+  const int row_groups = rows / (16 * L.cfg.waves);
+  L.slots = device_cus() * L.cfg.wgs_per_cu / row_groups;
+  if (L.slots < 1) L.slots = 1;
+  L.max_items = hint > 0 ? batch * hint : batch + 4 * L.slots;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.off_header = take(64);
+  L.off_item_b = take(4 * (size_t)L.max_items);
+  L.off_item_p0 = take(4 * (size_t)L.max_items);
+  L.off_item_p1 = take(4 * (size_t)L.max_items);
+  L.off_seq_start = take(4 * (size_t)batch);
+  L.off_seq_count = take(4 * (size_t)batch);
+  L.off_qabs = take((size_t)batch * rows * kEntry * 2);
+  L.off_opart = take((size_t)L.max_items * rows * kLatent * 4);
+  L.off_lse = take((size_t)L.max_items * rows * 4);
+  L.total = off;
+  return L;
+}
+
+// Benchmark stage timing (mla_profile_enable / mla_profile_collect).
+struct Profile {
+  std::vector<hipEvent_t> ev;  // 5 per call
+  int max_calls = 0;
+  int used = 0;
+};
+Profile g_prof;
+
+void prof_mark(int call, int k, hipStream_t s) {
+  if (call >= 0) hipEventRecord(g_prof.ev[call * 5 + k], s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_profile_enable(int32_t max_calls) {
+  for (hipEvent_t e : g_prof.ev) hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.max_calls = 0;
+  g_prof.used = 0;
+  if (max_calls <= 0) return MLA_OK;
+  if (max_calls > 100000) return MLA_ERR_SHAPE;
+  g_prof.ev.resize((size_t)max_calls * 5);
+  for (auto& e : g_prof.ev)
+    if (hipEventCreate(&e) != hipSuccess) return MLA_ERR_HIP;
+  g_prof.max_calls = max_calls;
+  return MLA_OK;
+}
+
+int mla_profile_collect(double* stage_ms, int32_t* calls) {
+  if (!stage_ms || !calls) return MLA_ERR_NULL;
+  for (int k = 0; k < 4; ++k) stage_ms[k] = 0.0;
+  for (int c = 0; c < g_prof.used; ++c) {
+    if (hipEventSynchronize(g_prof.ev[c * 5 + 4]) != hipSuccess) return MLA_ERR_HIP;
+    for (int k = 0; k < 4; ++k) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, g_prof.ev[c * 5 + k], g_prof.ev[c * 5 + k + 1]) != hipSuccess)
+        return MLA_ERR_HIP;
+      stage_ms[k] += ms;
+    }
+  }
+  *calls = g_prof.used;
+  g_prof.used = 0;
+  return MLA_OK;
+}
+
+int mla_abi_version(void) { return 1; }
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "a size argument is out of range or inconsistent";
+    case MLA_ERR_UNSUPPORTED: return "unsupported dimensions (need kv_lora 512, rope 64, qk_nope 128, v_dim 128, page 64, heads 16..128 in steps of 16)";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP runtime error at kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int mla_cache_insert(const mla_dims* dims, const void* kv_a, const void* rms_w, float eps,
+                     float rope_base, const int32_t* block_table, int32_t bt_stride,
+                     const int32_t* seq_lens, int32_t batch, int32_t q_len, void* cache,
+                     int32_t num_blocks, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > kMaxBatch || q_len < 1 || q_len > kMaxQLen || bt_stride < 1 ||
+      num_blocks < 1)
+    return MLA_ERR_SHAPE;
+  if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(rope_base) || rope_base <= 0.f)
+    return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!kv_a || !rms_w || !block_table || !seq_lens || !cache) return MLA_ERR_NULL;
+  hipError_t e = launch_insert(static_cast<const uint16_t*>(kv_a),
+                               static_cast<const uint16_t*>(rms_w), eps, rope_base, block_table,
+                               bt_stride, seq_lens, batch, q_len, static_cast<uint16_t*>(cache),
+                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                  int32_t max_seq_len, int32_t num_splits_hint) {
+  if (check_dims(dims) != MLA_OK) return 0;
+  if (batch < 0 || batch > kMaxBatch || q_len < 1 || q_len > kMaxQLen || max_seq_len < q_len ||
+      max_seq_len > kMaxSeqLen || num_splits_hint < 0 || num_splits_hint > kMaxHint)
+    return 0;
+  return make_layout(dims->heads, batch, q_len, num_splits_hint).total;
+}
+
+int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+               int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+               const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t max_seq_len,
+               float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+               int32_t num_splits_hint, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > kMaxBatch || q_len < 1 || q_len > kMaxQLen || max_seq_len < q_len ||
+      max_seq_len > kMaxSeqLen || num_blocks < 1 || num_splits_hint < 0 ||
+      num_splits_hint > kMaxHint)
+    return MLA_ERR_SHAPE;
+  const int max_pages = (max_seq_len + kPage - 1) / kPage;
+  if (bt_stride < max_pages) return MLA_ERR_SHAPE;
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q || !kv_b || !cache || !block_table || !seq_lens || !out) return MLA_ERR_NULL;
+  if (!workspace) return MLA_ERR_WORKSPACE;
+  const int heads = dims->heads;
+  const Layout L = make_layout(heads, batch, q_len, num_splits_hint);
+  if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  PlanView plan;
+  plan.header = reinterpret_cast<int32_t*>(ws + L.off_header);
+  plan.item_b = reinterpret_cast<int32_t*>(ws + L.off_item_b);
+  plan.item_p0 = reinterpret_cast<int32_t*>(ws + L.off_item_p0);
+  plan.item_p1 = reinterpret_cast<int32_t*>(ws + L.off_item_p1);
+  plan.seq_start = reinterpret_cast<int32_t*>(ws + L.off_seq_start);
+  plan.seq_count = reinterpret_cast<int32_t*>(ws + L.off_seq_count);
+  uint16_t* q_abs = reinterpret_cast<uint16_t*>(ws + L.off_qabs);
+  float* o_part = reinterpret_cast<float*>(ws + L.off_opart);
+  float* lse_part = reinterpret_cast<float*>(ws + L.off_lse);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rows = heads * q_len;
+  // price of one item's partial rows (fp32 write + read) in cache pages
+  const float item_cost = (float)rows * kLatent * 4 * 2 / (float)kPageBytes;
+
+  const int pc = g_prof.used < g_prof.max_calls ? g_prof.used++ : -1;
+  prof_mark(pc, 0, s);
+  hipError_t e = launch_plan(seq_lens, batch, max_pages, L.slots, L.max_items, num_splits_hint,
+                             item_cost, plan, s);
+  prof_mark(pc, 1, s);
+  if (e == hipSuccess)
+    e = launch_qabsorb(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_b), heads,
+                       batch * q_len, q_abs, s);
+  prof_mark(pc, 2, s);
+  if (e == hipSuccess)
+    e = launch_decode(L.cfg, q_abs, static_cast<const uint16_t*>(cache), block_table, bt_stride,
+                      seq_lens, heads, q_len, softmax_scale * 1.4426950408889634f, plan,
+                      L.max_items, o_part, lse_part, s);
+  prof_mark(pc, 3, s);
+  if (e == hipSuccess)
+    e = launch_combine(o_part, lse_part, plan, static_cast<const uint16_t*>(kv_b), heads, q_len,
+                       batch, static_cast<uint16_t*>(out), s);
+  prof_mark(pc, 4, s);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Shared definitions of the gfx950 MLA kernels (device types, conversions,
+// constants, launch-wrapper declarations).  Internal to libmla.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Fixed model dimensions (DeepSeek MLA: kv_lora_rank 512, qk_rope_head_dim 64,
+// qk_nope_head_dim 128, v_head_dim 128) and the cache page of 64 tokens.
+constexpr int kLatent = 512;
+constexpr int kRope = 64;
+constexpr int kEntry = kLatent + kRope;        // 576 numbers per cached token
+constexpr int kEntryBytes = kEntry * 2;        // 1152 bytes in bf16
+constexpr int kNope = 128;
+constexpr int kVdim = 128;
+constexpr int kQk = kNope + kRope;             // 192
+constexpr int kPage = 64;
+constexpr int kPageBytes = kPage * kEntryBytes;  // 73728
+constexpr int kChunk16 = kEntryBytes / 16;     // 72 16-byte pieces per entry
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+// ---- bf16 conversions (bit-level, round to nearest even) -------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+// double -> bf16 with a single rounding: truncate to float, mark inexactness
+// in the lowest bit (round-to-odd), then round the float to bf16.  Float keeps
+// 16 more bits than bf16, so the odd bit cannot create a false tie.
+__device__ __forceinline__ uint16_t f64_to_bf16(double d) {
+  float f = __double2float_rz(d);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != d) u |= 1u;
+  return f32_to_bf16(__uint_as_float(u));
+}
+
+// ---- split plan layout inside the workspace ---------------------------------
+struct PlanView {
+  int32_t* header;      // [0] = number of work items
+  int32_t* item_b;      // [max_items] sequence of the item
+  int32_t* item_p0;     // [max_items] first page (logical)
+  int32_t* item_p1;     // [max_items] one past the last page
+  int32_t* seq_start;   // [B] first item of each sequence
+  int32_t* seq_count;   // [B] number of items of each sequence
+};
+
+// ---- launch wrappers (each returns hipGetLastError() of its launch) --------
+hipError_t launch_insert(const uint16_t* kv_a, const uint16_t* rms_w, float eps, float rope_base,
+                         const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
+                         int batch, int q_len, uint16_t* cache, hipStream_t stream);
+
+hipError_t launch_plan(const int32_t* seq_lens, int batch, int max_pages, int slots,
+                       int max_items, int splits_hint, float item_cost_pages, PlanView plan,
+                       hipStream_t stream);
+
+hipError_t launch_qabsorb(const uint16_t* q, const uint16_t* kv_b, int heads, int rows,
+                          uint16_t* q_abs, hipStream_t stream);
+
+struct DecodeConfig {
+  int waves;    // 16-row groups per workgroup
+  int chunk;    // tokens per LDS stage (32 or 64)
+  int lds_bytes;
+  int wgs_per_cu;
+};
+DecodeConfig decode_config(int rows_per_seq);
+
+hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const uint16_t* cache,
+                         const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
+                         int heads, int q_len, float scale_log2, PlanView plan, int max_items,
+                         float* o_part, float* lse_part, hipStream_t stream);
+
+hipError_t launch_combine(const float* o_part, const float* lse_part, PlanView plan,
+                          const uint16_t* kv_b, int heads, int q_len, int batch, uint16_t* out,
+                          hipStream_t stream);
+
+}  // namespace mla

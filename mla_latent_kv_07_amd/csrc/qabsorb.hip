@@ -1,0 +1,109 @@
+// Query absorption: q_abs[row, h] = [ q_nope[row, h] W_UK[h]  |  q_pe[row, h] ].
+//
+// "深度解读DeepSeek：源码解读 DeepSeek-V3", section MLA, "(b) 优化实现", first
+// einsum (bshd,hdc->bshc): q_nope times the first 128 rows of head h's kv_b
+// block; "DeepSeek-V2-Lite 模型结构详解" §五 gives the identity
+// q . (W_k c) = (W_k^T q) . c that moves W_UK to the query side.
+//
+// One workgroup per (head, 128 latent columns); W_UK[h][:, cols] (32 KB) is
+// staged in LDS and read as the MFMA A operand with the gfx950 transposing
+// LDS read (the contraction index d is W_UK's row index).  The query rows are
+// the B operand, straight from global memory.  Result rows are written with
+// 8-byte stores (4 consecutive latent columns per lane).
+#include "mla_common.h"
+
+namespace mla {
+
+constexpr int kQaCols = 128;                 // latent columns per workgroup
+constexpr int kQaStride = kQaCols * 2 + 32;  // padded LDS row of W_UK (bytes)
+
+__global__ __launch_bounds__(256) void qabsorb_kernel(const uint16_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ kv_b,
+                                                      int heads, int rows,
+                                                      uint16_t* __restrict__ q_abs) {
+  __shared__ __attribute__((aligned(16))) char w_lds[kNope * kQaStride];
+  const int h = blockIdx.x;
+  const int nc = blockIdx.y;  // column chunk
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+
+  // stage W_UK[h][d][nc*128 .. +128] for d < 128
+  const uint16_t* wuk = kv_b + (int64_t)h * (kNope + kVdim) * kLatent + nc * kQaCols;
+#pragma unroll
+  for (int k = 0; k < (kNope * kQaCols / 8) / 256; ++k) {
+    const int p = k * 256 + tid;
+    const int d = p >> 4;
+    const int c16 = p & 15;
+    *reinterpret_cast<u16x8*>(w_lds + d * kQaStride + c16 * 16) =
+        *reinterpret_cast<const u16x8*>(wuk + (int64_t)d * kLatent + c16 * 8);
+  }
+  // q_pe passes through unchanged (done once per head, by column chunk 0)
+  if (nc == 0) {
+    for (int p = tid; p < rows * 8; p += 256) {
+      const int r = p >> 3;
+      const int j = p & 7;
+      const int64_t row = (int64_t)r * heads + h;
+      *reinterpret_cast<u16x8*>(q_abs + row * kEntry + kLatent + j * 8) =
+          *reinterpret_cast<const u16x8*>(q + row * kQk + kNope + j * 8);
+    }
+  }
+  __syncthreads();
+
+  // A operands: W_UK^T tiles for this wave's 32 columns, all 4 k-steps of 32 d
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int s16 = lane & 15;
+  const int r = s16 >> 2;
+  const int qq = s16 & 3;
+  bf16x8 aw[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c0 = wave * 32 + mt * 16 + 4 * qq;
+      const int d0 = 32 * ks + 8 * g + r;
+      const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (MLA_LDS bf16x4*)((MLA_LDS char*)w_lds + d0 * kQaStride + c0 * 2));
+      const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (MLA_LDS bf16x4*)((MLA_LDS char*)w_lds + (d0 + 4) * kQaStride + c0 * 2));
+      aw[mt][ks] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+
+  for (int rt = 0; rt * 16 < rows; ++rt) {
+    const int rr = rt * 16 + n;
+    const int64_t row = (int64_t)rr * heads + h;
+    bf16x8 bq[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (rr < rows)
+        bq[ks] = *reinterpret_cast<const bf16x8*>(q + row * kQk + 32 * ks + 8 * g);
+      else
+        bq[ks] = bf16x8{};
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[mt][ks], bq[ks], acc, 0, 0, 0);
+      if (rr < rows) {
+        u16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(acc[i]);
+        *reinterpret_cast<u16x4*>(q_abs + row * kEntry + nc * kQaCols + wave * 32 + mt * 16 +
+                                  4 * g) = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_qabsorb(const uint16_t* q, const uint16_t* kv_b, int heads, int rows,
+                          uint16_t* q_abs, hipStream_t stream) {
+  hipLaunchKernelGGL(qabsorb_kernel, dim3(heads, kLatent / kQaCols), dim3(256), 0, stream, q,
+                     kv_b, heads, rows, q_abs);
+  return hipGetLastError();
+}
+
+}  // namespace mla
