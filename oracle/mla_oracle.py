@@ -230,13 +230,14 @@ def decode_expanded(q_bits: np.ndarray, kv_b_bits: np.ndarray, cache_bits: np.nd
         c, r = rows[:, :latent], rows[:, latent:latent + rope]
         q = q_all[b][:, heads, :]        # [q_len, h, nope + rope]
         scores = np.empty((q_len, len(heads), length))
+        q_h = np.ascontiguousarray(q.transpose(1, 2, 0))                  # [h, nope+rope, i]
         for t0 in range(0, length, chunk):
             t1 = min(length, t0 + chunk)
-            k_nope = np.einsum("tc,hdc->htd", c[t0:t1], w_uk)          # [h, t, nope]
+            k_nope = np.matmul(c[None, t0:t1], w_uk.transpose(0, 2, 1))  # [h, t, nope]
             k = np.concatenate(
                 [k_nope, np.broadcast_to(r[t0:t1][None], (len(heads), t1 - t0, rope))],
                 axis=-1)                                                  # [h, t, nope+rope]
-            scores[:, :, t0:t1] = np.einsum("ihd,htd->iht", q, k) * softmax_scale
+            scores[:, :, t0:t1] = np.matmul(k, q_h).transpose(2, 0, 1) * softmax_scale
         vis = _visible(length, q_len)[:, None, :]
         scores = np.where(vis, scores, -np.inf)
         mx = scores.max(axis=-1, keepdims=True)
@@ -244,12 +245,13 @@ def decode_expanded(q_bits: np.ndarray, kv_b_bits: np.ndarray, cache_bits: np.nd
         p = e / e.sum(axis=-1, keepdims=True)
         if return_probs:
             probs.append(p)
-        acc = np.zeros((q_len, len(heads), v_dim))
+        acc = np.zeros((len(heads), q_len, v_dim))
+        p_h = p.transpose(1, 0, 2)                                        # [h, i, t]
         for t0 in range(0, length, chunk):
             t1 = min(length, t0 + chunk)
-            v = np.einsum("tc,hdc->htd", c[t0:t1], w_uv)                # [h, t, v_dim]
-            acc += np.einsum("iht,htd->ihd", p[:, :, t0:t1], v)
-        out[bi] = acc
+            v = np.matmul(c[None, t0:t1], w_uv.transpose(0, 2, 1))      # [h, t, v_dim]
+            acc += np.matmul(p_h[:, :, t0:t1], v)                        # [h, i, v_dim]
+        out[bi] = acc.transpose(1, 0, 2)
     if return_probs:
         return out, probs
     return out
