@@ -9,7 +9,7 @@
 // 128 rows of head h's kv_b block; "DeepSeek-V2-Lite 模型结构详解" §五 gives
 // the identity that moves W_UV behind the weighted sum.
 //
-// One workgroup per (head, 64 query rows).  The merged latent rows are
+// One workgroup per (head, 32 query rows).  The merged latent rows are
 // rounded to bf16 into LDS, then D^T = W_UV o_lat^T runs on the bf16 MFMA
 // 16x16x32 with W_UV streamed from global memory (each head's 128 KB block is
 // read once per workgroup).
@@ -17,7 +17,7 @@
 
 namespace mla {
 
-constexpr int kCombRows = 64;                 // query rows per workgroup
+constexpr int kCombRows = 32;                 // query rows per workgroup
 constexpr int kCombRowBytes = kLatent * 2 + 16;  // padded LDS row (bank spread)
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
@@ -34,75 +34,118 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
 
-  // ---- merge: wave w handles rows w*16 .. w*16+15, lane covers 8 columns ----
-  for (int rr = 0; rr < kCombRows / 4; ++rr) {
-    const int lr = wave * (kCombRows / 4) + rr;
-    const int bi = row_base + lr;
-    u16x8 packed;
-    if (bi < total_rows) {
-      const int b = bi / q_len;
-      const int i = bi - b * q_len;
-      const int srow = i * heads + h;
-      const int s0 = plan.seq_start[b];
-      const int ns = plan.seq_count[b];
-      float mx = -INFINITY;
-      for (int s = 0; s < ns; ++s)
-        mx = fmaxf(mx, lse_part[(int64_t)(s0 + s) * rows_per_seq + srow]);
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      float wsum = 0.f;
-      for (int s = 0; s < ns; ++s) {
-        const int64_t r = (int64_t)(s0 + s) * rows_per_seq + srow;
-        const float lse = lse_part[r];
-        const float w = lse == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lse - mx);
-        wsum += w;
-        const f32x4* src = reinterpret_cast<const f32x4*>(o_part + r * kLatent + lane * 8);
-        const f32x4 v0 = src[0], v1 = src[1];
+  // ---- merge: wave w handles rows w*8 .. w*8+7; lane covers 8 columns -------
+  // Two rows at a time: their split weights are computed lane-parallel
+  // (lane s <-> split s, 64 splits at a time), then all their partial rows
+  // are loaded with independent loads before any is used.
+  constexpr int kRowsPerWave = kCombRows / 4;
+  for (int rr = 0; rr < kRowsPerWave; rr += 2) {
+    int s0[2], ns[2];
+    int64_t srow[2];
+    bool live[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[j] += w * v0[j];
-          acc[4 + j] += w * v1[j];
-        }
-      }
-      const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) packed[j] = f32_to_bf16(acc[j] * inv);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) packed[j] = 0;
+    for (int u = 0; u < 2; ++u) {
+      const int bi = row_base + wave * kRowsPerWave + rr + u;
+      live[u] = bi < total_rows;
+      const int b = live[u] ? bi / q_len : 0;
+      const int i = live[u] ? bi - b * q_len : 0;
+      srow[u] = i * heads + h;
+      s0[u] = plan.seq_start[b];
+      ns[u] = live[u] ? plan.seq_count[b] : 0;
     }
-    *reinterpret_cast<u16x8*>(olat + lr * kCombRowBytes + lane * 16) = packed;
+    float acc[2][8];
+    float wsum[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      wsum[u] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[u][j] = 0.f;
+    }
+    const int nmax = max(ns[0], ns[1]);
+    for (int sb = 0; sb < nmax; sb += 64) {
+      float w_l[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // weights of splits sb .. sb+63 relative to the max over ALL splits
+        float mx = -INFINITY;
+        for (int s = lane; s < ns[u]; s += 64)
+          mx = fmaxf(mx, lse_part[(int64_t)(s0[u] + s) * rows_per_seq + srow[u]]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        const int s_l = sb + lane;
+        const float lse =
+            s_l < ns[u] ? lse_part[(int64_t)(s0[u] + s_l) * rows_per_seq + srow[u]] : -INFINITY;
+        w_l[u] = lse == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lse - mx);
+      }
+      const int cnt = min(64, nmax - sb);
+      for (int s = 0; s < cnt; s += 4) {
+        f32x4 v[2][4][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const bool ok = s + k < cnt && sb + s + k < ns[u];
+            const int64_t r = (int64_t)(s0[u] + (ok ? sb + s + k : 0)) * rows_per_seq + srow[u];
+            const f32x4* src = reinterpret_cast<const f32x4*>(o_part + r * kLatent + lane * 8);
+            v[u][k][0] = ok ? src[0] : f32x4{0.f, 0.f, 0.f, 0.f};
+            v[u][k][1] = ok ? src[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float w = (s + k < cnt) ? __shfl(w_l[u], s + k, 64) : 0.f;
+            wsum[u] += w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              acc[u][j] += w * v[u][k][0][j];
+              acc[u][4 + j] += w * v[u][k][1][j];
+            }
+          }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float inv = wsum[u] > 0.f ? 1.f / wsum[u] : 0.f;
+      u16x8 packed;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) packed[j] = live[u] ? f32_to_bf16(acc[u][j] * inv) : 0;
+      const int lr = wave * kRowsPerWave + rr + u;
+      *reinterpret_cast<u16x8*>(olat + lr * kCombRowBytes + lane * 16) = packed;
+    }
   }
   __syncthreads();
 
-  // ---- projection: wave w computes d in [32w, 32w+32) for all 64 rows -------
+  // ---- projection: wave w computes d in [32w, 32w+32) for all 32 rows -------
   const int n = lane & 15;
   const int g = lane >> 4;
-  f32x4 acc[2][4];
+  constexpr int NT = kCombRows / 16;
+  f32x4 acc[2][NT];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint16_t* wuv = kv_b + ((int64_t)h * (kNope + kVdim) + kNope) * kLatent;
 #pragma unroll 4
   for (int ks = 0; ks < kLatent / 32; ++ks) {
-    bf16x8 av[2], bv[4];
+    bf16x8 av[2], bv[NT];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
       av[mt] = *reinterpret_cast<const bf16x8*>(wuv + (int64_t)(wave * 32 + mt * 16 + n) * kLatent +
                                                 32 * ks + 8 * g);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
       bv[nt] = *reinterpret_cast<const bf16x8*>(olat + (nt * 16 + n) * kCombRowBytes +
                                                 (32 * ks + 8 * g) * 2);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
         acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bv[nt], acc[mt][nt], 0, 0, 0);
   }
   // D^T[d][row]: lane holds d = 16mt + 4g + i of row n of tile nt
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     const int bi = row_base + nt * 16 + n;
     if (bi >= total_rows) continue;
     uint16_t* dst = out + ((int64_t)bi * heads + h) * kVdim + wave * 32;

@@ -10,26 +10,34 @@
 //
 // gfx950 mapping
 //   * One workgroup = one work item (a contiguous page range of one sequence)
-//     x one group of up to 128 query rows (row = query index * H + head).
-//     Each wavefront owns 16 rows.  All wavefronts share every cache chunk,
-//     so the cache is read from HBM once per row group.
-//   * Cache chunks (32 or 64 tokens, 36/72 KB) are copied HBM -> LDS by the
-//     direct-to-LDS global loads, double buffered; one barrier per chunk.
-//     In LDS the 16-byte pieces of each entry are XOR-swizzled by
-//     (row / 2) mod 8 so both read patterns below are free of bank conflicts.
+//     x one group of query rows (row = query index * H + head).  Each
+//     wavefront owns NH groups of 16 rows; all wavefronts share every cache
+//     chunk, which is read from HBM once per row group.
+//   * Chunks of 32 positions (36 KB) are copied HBM -> LDS by direct-to-LDS
+//     loads into an NBUF-deep ring; one barrier per chunk.  Every copy
+//     instruction moves 1 KB of contiguous cache bytes (whole 128-byte
+//     lines): per-lane scattered copies run at about half the HBM rate.
+//     In LDS, position r keeps its 1152-byte row; its 16-byte pieces are
+//     permuted inside each aligned group of 8 by swz(r) =
+//     2*(r & 3) + ((r >> 2) & 1), which makes both read patterns below free
+//     of bank conflicts on the 128-byte-per-clock LDS (8 consecutive rows x
+//     one piece per clock for the 16-byte score reads; 4 rows x two adjacent
+//     pieces per clock for the 8-byte transposing reads).
 //   * Scores are computed transposed, S^T = K Q^T, with the bf16 MFMA
-//     16x16x32: the cache tile is the A operand (16 positions x 8 features
-//     per lane, one 16-byte LDS read), the query the B operand held in
-//     registers for the whole launch.  The result leaves each lane with the
-//     scores of ONE head for 4 positions per 16-position tile, which is
-//     exactly the B-operand layout the P.V product needs: P never goes
-//     through LDS, and the softmax needs only two cross-lane reductions.
-//   * O^T = V^T P^T with the same MFMA; the V^T operand comes from LDS with
-//     the gfx950 transposing read (ds_read_b64_tr_b16).  The fp32 output
-//     accumulator of a lane belongs to one head, so the online-softmax
-//     rescale is a per-lane scalar.
-//   * Softmax statistics are fp32 in the log2 domain (scale * log2(e) folded
-//     into one multiply), P is rounded to bf16 for the MFMA.
+//     16x16x32: the cache tile is the A operand, the query the B operand
+//     held in registers for the whole launch.  Each lane ends up with the
+//     scores of ONE head for 4 positions per 16-position tile, exactly the
+//     B-operand layout of O^T = V^T P^T, so P never goes through LDS.  V^T
+//     comes from LDS through the transposing read (ds_read_b64_tr_b16).
+//   * The softmax of chunk j is scheduled under the score MFMAs of chunk j+1
+//     (software pipelining inside the wavefront), so the vector ALU work
+//     hides behind the matrix cores.
+//   * Online softmax in log2 units with a fixed reference per row: the first
+//     finite chunk max.  Probabilities are 2^(s - ref) and stay below
+//     2^kSlack; the fp32 accumulators are never rescaled.  If a later score
+//     exceeds ref + kSlack (never for well-scaled attention, but possible),
+//     the workgroup restarts the item: one pass for the exact row max, one
+//     pass with that max as the reference.
 // Output per work item: normalised fp32 rows [rows, 512] and their log2-sum-
 // exp, merged across items by the combine kernel.
 #include "mla_common.h"
@@ -43,6 +51,8 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   float* o_part;             // [max_items, rows_per_seq, 512]
   float* lse_part;           // [max_items, rows_per_seq]
+  const uint16_t* zero_row;  // 576 zeros: source of the copies of positions >= len
+  int* restart_flag;         // one int per workgroup (workgroup-local communication)
   PlanView plan;
   int bt_stride;
   int heads;
@@ -52,188 +62,200 @@ struct DecodeArgs {
   float scale_log2;
 };
 
-template <int NW, int CHUNK>
-struct DecodeShape {
-  static constexpr int kThreads = NW * 64;
-  static constexpr int kTiles = CHUNK / 16;                 // 16-position tiles per chunk
-  static constexpr int kBufBytes = CHUNK * kEntryBytes;     // one LDS stage
-  static constexpr int kPieces = CHUNK * kChunk16;          // 16-byte pieces per chunk
-  static constexpr int kPerLane = (kPieces + NW * 64 - 1) / (NW * 64);  // DMA loads per lane
-  static_assert(kPieces % 64 == 0, "whole wavefront-sized DMA instructions");
-  static_assert(CHUNK == 32 || CHUNK == 64, "chunk of 32 or 64 positions");
+constexpr int kChunk = 32;                     // positions per LDS stage
+constexpr int kBufBytes = kChunk * kEntryBytes;  // 36864
+constexpr float kSlack = 16.0f;                // log2 headroom above the reference max
+
+// Encoding of "s_waitcnt vmcnt(n)" (expcnt and lgkmcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int NW>
+struct Dma {
+  static constexpr int kInsts = kBufBytes / 1024;   // 36 wavefront-wide copies per chunk
+  static constexpr int kPerWave = kInsts / NW;
+  static_assert(kInsts % NW == 0, "copies split evenly over the wavefronts");
 };
 
-// Issue the direct-to-LDS copy of one chunk: LDS piece P (16 bytes) holds
-// global piece (P % 72) ^ swz(row) of entry row = P / 72.
-template <int NW, int CHUNK>
-__device__ __forceinline__ void load_chunk(MLA_LDS char* buf, const char* src, int wave,
-                                           int lane) {
-  using S = DecodeShape<NW, CHUNK>;
+// Piece permutation inside each aligned group of 8 pieces of row r.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Copy one chunk into the LDS ring slot `buf`.  Copy k fills LDS pieces
+// 64k .. 64k+63 (lane L -> piece Q = 64k + L of row Q / 72, slot Q % 72),
+// fetching global piece (Q % 72) ^ swz(row) of that row: the 64 lanes read
+// the same 1 KB of the chunk, permuted within 128-byte lines.  Rows >= nvalid
+// are copied from the zero row instead.
+template <int NW>
+__device__ __forceinline__ void load_chunk(MLA_LDS char* buf, const char* src, const char* zero,
+                                           int nvalid, int wave, int lane) {
+  // the empty asm keeps the per-lane addresses from being hoisted out of the
+  // chunk loop (registers are the scarce resource here)
+  asm volatile("" : "+v"(lane));
 #pragma unroll
-  for (int k = 0; k < S::kPerLane; ++k) {
-    const int base = (k * NW + wave) * 64;  // first piece of this instruction (wave-uniform)
-    if (S::kPieces % (NW * 64) != 0 && base >= S::kPieces) break;
-    const int p = base + lane;
-    const int row = p / kChunk16;
-    const int col = p - row * kChunk16;
-    const int gcol = col ^ ((row >> 1) & 7);
-    const char* g = src + row * kEntryBytes + gcol * 16;
-    __builtin_amdgcn_global_load_lds(g, buf + base * 16, 16, 0, 0);
+  for (int i = 0; i < Dma<NW>::kPerWave; ++i) {
+    const int k = i * NW + wave;
+    const int q = 64 * k + lane;
+    const int row = q / kChunk16;
+    const int col = q - row * kChunk16;
+    const int gcol = col ^ swz(row);
+    const char* g = (row < nvalid ? src + row * kEntryBytes : zero) + gcol * 16;
+    __builtin_amdgcn_global_load_lds(g, buf + k * 1024, 16, 0, 0);
   }
 }
 
-// One chunk of CHUNK positions starting at absolute position `t0`.
-// MASK: some position in the chunk is beyond this wave's causal limit `tmax`
-// (or beyond the sequence end `len`): scores there become -inf and the V
-// operand rows beyond `len` are zeroed (their slots may hold anything).
-template <int NW, int CHUNK, bool MASK>
-__device__ __forceinline__ void compute_chunk(const MLA_LDS char* buf, const bf16x8 (&qreg)[18],
-                                              f32x4 (&oacc)[32], float& m_run, float& l_run,
-                                              int lane, int t0, int tmax, int len,
-                                              float scale_log2) {
-  using S = DecodeShape<NW, CHUNK>;
-  constexpr int NT = S::kTiles;
-  const int n = lane & 15;
-  const int gq = lane >> 4;
-
-  // ---- scores: S^T[tile] = K[tile] Q^T over 18 k-steps of 32 features ------
-  // Software pipelined: the LDS reads of k-step ks + KPD are issued before the
-  // MFMAs of k-step ks; scheduling barriers keep the compiler from hoisting
-  // more reads (and spending more registers) than that.
-  f32x4 sacc[NT];
+// Scores of one chunk for the wavefront's NH row groups: sacc[h][t] holds
+// S^T for positions 16t..16t+15.  The LDS reads of k-step ks + KPD are issued
+// before the MFMAs of k-step ks.
+template <int NH>
+__device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_even,
+                                            int sbase_odd, const bf16x8 (&qreg)[NH][16],
+                                            const MLA_LDS char* const (&qrope)[2],
+                                            f32x4 (&sacc)[NH][2]) {
+  constexpr int KPD = 1;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  {
-    constexpr int KPD = NT >= 4 ? 1 : 2;  // k-steps of read-ahead
-    const int x = gq ^ ((n >> 1) & 7);
-    const int off_even = 16 * x;
-    const int off_odd = 16 * (x ^ 4) - 64;
-    const MLA_LDS char* rowp = buf + n * kEntryBytes;
-    auto kload = [&](int ks, int t) -> bf16x8 {
-      const int off = 64 * ks + ((ks & 1) ? off_odd : off_even);
-      return *reinterpret_cast<const MLA_LDS bf16x8*>(rowp + t * 16 * kEntryBytes + off);
-    };
-    bf16x8 kb[KPD + 1][NT];
+  for (int h = 0; h < NH; ++h)
 #pragma unroll
-    for (int ks = 0; ks < KPD; ++ks)
+    for (int t = 0; t < 2; ++t) sacc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // lane (row n, piece group gq) reads piece 4ks + gq of rows 16t + n:
+  // byte (16t + n)*1152 + 16*((4ks + gq) ^ swz(n)) = base(ks parity) + 64ks + 18432t
+  const MLA_LDS char* be = buf + sbase_even;
+  const MLA_LDS char* bo = buf + sbase_odd;
+  auto kload = [&](int ks, int t) -> bf16x8 {
+    return *reinterpret_cast<const MLA_LDS bf16x8*>((ks & 1 ? bo : be) + 64 * ks +
+                                                    16 * kEntryBytes * t);
+  };
+  // the rope quarter of the query (k-steps 16, 17) lives in LDS: row group h,
+  // k-step 16 + e of this lane at qrope[e] + h*2048
+  auto qload = [&](int h, int e) -> bf16x8 {
+    return *reinterpret_cast<const MLA_LDS bf16x8*>(qrope[e] + h * 2048);
+  };
+  bf16x8 kb[KPD + 1][2];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) kb[ks][t] = kload(ks, t);
+  for (int ks = 0; ks < KPD; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      if (ks + KPD < 18) {
+    for (int t = 0; t < 2; ++t) kb[ks][t] = kload(ks, t);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) kb[(ks + KPD) % (KPD + 1)][t] = kload(ks + KPD, t);
-      }
+  for (int ks = 0; ks < 18; ++ks) {
+    if (ks + KPD < 18) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks % (KPD + 1)][t], qreg[ks],
-                                                          sacc[t], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < 2; ++t) kb[(ks + KPD) % (KPD + 1)][t] = kload(ks + KPD, t);
     }
-  }
-
-  // ---- online softmax (log2 domain), per head = per lane column -----------
-  float mloc = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+    for (int h = 0; h < NH; ++h) {
+      const bf16x8 qb = ks < 16 ? qreg[h][ks < 16 ? ks : 0] : qload(h, ks - 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float s = sacc[t][i] * scale_log2;
-      if (MASK) {
-        const int pos = t0 + 16 * t + 4 * gq + i;
-        s = pos > tmax ? -INFINITY : s;
-      }
-      sacc[t][i] = s;
-      mloc = fmaxf(mloc, s);
-    }
-  }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-  const float m_new = fmaxf(m_run, mloc);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-  float psum = 0.f;
-  bf16x8 pk[NT / 2];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(sacc[t][i] - m_use);
-      psum += p;
-      pk[t >> 1][(t & 1) * 4 + i] = (__bf16)p;
-    }
-  }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-    for (int f = 0; f < 32; ++f) oacc[f] *= alpha;
-  }
-
-  // ---- O^T[f] += V^T[f] P^T, V^T read with the transposing LDS load --------
-  {
-    const int s16 = lane & 15;
-    const int r = s16 >> 2;
-    const int qq = s16 & 3;
-    const int y = (qq >> 1) ^ ((2 * gq + (r >> 1)) & 7);
-    const int half = (qq & 1) * 8;
-    int troff[4];
-#pragma unroll
-    for (int f4 = 0; f4 < 4; ++f4) troff[f4] = 16 * ((2 * f4) ^ y) + half;
-    const MLA_LDS char* rowp = buf + (4 * gq + r) * kEntryBytes;
-    // step = (kk, f); the lane's 8 k-slots are positions
-    // t0 + 32kk + 4gq + {0..3} and t0 + 32kk + 16 + 4gq + {0..3}
-    constexpr int NSTEP = (NT / 2) * 32;
-    constexpr int VPD = 3;  // steps of read-ahead
-    auto vload = [&](int step) -> bf16x8 {
-      const int kk = step >> 5;
-      const int f = step & 31;
-      const MLA_LDS char* p1 = rowp + (32 * kk) * kEntryBytes + 32 * (f & ~3) + troff[f & 3];
-      const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p1);
-      const bf16x4 a1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p1 + 16 * kEntryBytes));
-      return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    // MASK: zero the V elements of positions >= len (bit masks per k-step)
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 vkeep[NT / 2];
-    if (MASK) {
-#pragma unroll
-      for (int kk = 0; kk < NT / 2; ++kk) {
-        const int pa = t0 + 32 * kk + 4 * gq;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int p0 = pa + (d >> 1) * 16 + (d & 1) * 2;
-          vkeep[kk][d] = (p0 < len ? 0x0000ffffu : 0u) | (p0 + 1 < len ? 0xffff0000u : 0u);
-        }
-      }
-    }
-    bf16x8 vb[VPD + 1];
-#pragma unroll
-    for (int st = 0; st < VPD; ++st) vb[st] = vload(st);
-#pragma unroll
-    for (int st = 0; st < NSTEP; ++st) {
-      if (st + VPD < NSTEP) vb[(st + VPD) % (VPD + 1)] = vload(st + VPD);
-      const int kk = st >> 5;
-      const int f = st & 31;
-      bf16x8 a = vb[st % (VPD + 1)];
-      if (MASK) {
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        a = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, a) & vkeep[kk]);
-      }
-      oacc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[kk], oacc[f], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < 2; ++t)
+        sacc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks % (KPD + 1)][t], qb,
+                                                             sacc[h][t], 0, 0, 0);
     }
   }
 }
 
-template <int NW, int CHUNK>
+// Softmax of one chunk's scores (log2 units) into bf16 probabilities pk[h]
+// (the B operand of the P.V product).  Returns true if some row's chunk max
+// exceeds its reference by more than kSlack (the item must restart).
+template <int NH>
+__device__ __forceinline__ bool softmax_chunk(f32x4 (&sacc)[NH][2], bf16x8 (&pk)[NH],
+                                              float (&m_ref)[NH], float (&l_run)[NH],
+                                              const int (&lim)[NH], float scale_log2,
+                                              bool fixed_ref) {
+  // lim[h]: the lane's slot 16t + i is visible iff 16t + i <= lim[h]
+  bool restart = false;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = (16 * t + i > lim[h]) ? -INFINITY : sacc[h][t][i] * scale_log2;
+        sacc[h][t][i] = sc;
+        mloc = fmaxf(mloc, sc);
+      }
+    }
+    if (!fixed_ref) {
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      if (m_ref[h] == -INFINITY) m_ref[h] = mloc;
+      restart |= mloc > m_ref[h] + kSlack;
+    }
+    const float m_use = m_ref[h] == -INFINITY ? 0.f : m_ref[h];
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sacc[h][t][i] - m_use);
+        psum += p;
+        pk[h][t * 4 + i] = (__bf16)p;
+      }
+    }
+    l_run[h] += psum;
+  }
+  return restart;
+}
+
+// O^T[f] += V^T[f] P^T for the 32 feature tiles of 16; V^T via the
+// transposing LDS read, read-ahead of VPD steps.
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008;
+constexpr int kSgValu = 0x002;
+constexpr int kSgDsRead = 0x100;
+
+template <int NH>
+__device__ __forceinline__ void pv_chunk(const MLA_LDS char* buf, const int (&vbase)[4],
+                                         const bf16x8 (&pk)[NH], f32x4 (&oacc)[NH][32]) {
+  // feature tile f: byte vbase[f & 3] + 128*(f >> 2); second half +16 rows
+  bf16x8 vb[32];
+#pragma unroll
+  for (int f = 0; f < 32; ++f) {
+    const MLA_LDS char* p = buf + vbase[f & 3] + 128 * (f >> 2);
+    const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p);
+    const bf16x4 a1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p + 16 * kEntryBytes));
+    vb[f] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+#pragma unroll
+  for (int f = 0; f < 32; ++f)
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+      oacc[h][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[f], pk[h], oacc[h][f], 0, 0, 0);
+  // schedule: VPD feature tiles of reads ahead, then one tile of reads per
+  // tile of MFMAs (the reads of tile f + VPD overlap the MFMAs of tile f)
+  constexpr int VPD = 4;
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * VPD, 0);
+#pragma unroll
+  for (int f = 0; f < 32 - VPD; ++f) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, NH, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgMfma, NH * VPD, 0);
+}
+
+// Row max only (the first pass of a restart).
+template <int NH>
+__device__ __forceinline__ void max_chunk(const f32x4 (&sacc)[NH][2], float (&m)[NH],
+                                          const int (&lim)[NH], float scale_log2) {
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        mloc = fmaxf(mloc, (16 * t + i > lim[h]) ? -INFINITY : sacc[h][t][i] * scale_log2);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    m[h] = fmaxf(m[h], mloc);
+  }
+}
+
+template <int NW, int NH, int NBUF>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
-  using S = DecodeShape<NW, CHUNK>;
-  __shared__ __attribute__((aligned(1024))) char lds0_raw[S::kBufBytes];
-  __shared__ __attribute__((aligned(1024))) char lds1_raw[S::kBufBytes];
-  MLA_LDS char* lds0 = (MLA_LDS char*)lds0_raw;
-  MLA_LDS char* lds1 = (MLA_LDS char*)lds1_raw;
+  static_assert(NBUF >= 3 && NBUF * kBufBytes + NW * NH * 2048 <= 160 * 1024,
+                "LDS ring of NBUF chunks plus the query rope quarter");
+  // ring of NBUF chunks, then the rope quarter of the workgroup's query rows
+  __shared__ __attribute__((aligned(1024))) char lds_raw[NBUF * kBufBytes + NW * NH * 2048];
+  MLA_LDS char* lds = (MLA_LDS char*)lds_raw;
 
   // blockIdx -> (item, row group); the row groups of one item land on the
   // same XCD (block ids congruent mod 8) so their chunk reads share that L2.
@@ -252,98 +274,230 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int gq = lane >> 4;
-  const int row0 = (rg * NW + wave) * 16;       // first row of this wave in the sequence
-  const int qi = row0 / a.heads;                // query index shared by the 16 rows
-  const int tmax = len - a.q_len + qi;          // last visible position
+  const int row0 = (rg * NW + wave) * 16 * NH;  // first row of this wave in the sequence
+  int tmax[NH];                                 // last visible position per row group
+#pragma unroll
+  for (int h = 0; h < NH; ++h) tmax[h] = len - a.q_len + (row0 + 16 * h) / a.heads;
 
-  // query rows stay in registers: lane holds features 32ks + 8gq .. +8 of row n
-  bf16x8 qreg[18];
+  // per-lane LDS bases of the two read patterns (see the layout above)
+  const int xs = gq ^ swz(n);
+  const int sbase_even = n * kEntryBytes + 16 * xs;
+  const int sbase_odd = n * kEntryBytes + 16 * (xs ^ 4) - 64;
+  int vbase[4];
   {
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-        a.q_abs + ((int64_t)b * a.rows_per_seq + row0 + n) * kEntry + 8 * gq);
+    // transposing read: 16-lane group gq, lane 4r + qq supplies row 4gq + r,
+    // features 16f + 4qq .. +3 = piece 2f + (qq >> 1), half qq & 1
+    const int r4 = (lane & 15) >> 2;
+    const int qq = lane & 3;
+    const int row = 4 * gq + r4;
+    const int y = (qq >> 1) ^ swz(row);
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qreg[ks] = qp[4 * ks];
+    for (int f4 = 0; f4 < 4; ++f4)
+      vbase[f4] = row * kEntryBytes + 16 * ((2 * f4) ^ y) + 8 * (qq & 1);
   }
-  f32x4 oacc[32];
+
+  // query rows: the 512 latent features stay in registers (lane holds
+  // features 32ks + 8gq .. +8 of row n), the 64 rope features go to LDS
+  bf16x8 qreg[NH][16];
+  MLA_LDS char* qrope_w = lds + NBUF * kBufBytes + wave * NH * 2048;
 #pragma unroll
-  for (int f = 0; f < 32; ++f) oacc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int h = 0; h < NH; ++h) {
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+        a.q_abs + ((int64_t)b * a.rows_per_seq + row0 + 16 * h + n) * kEntry + 8 * gq);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qreg[h][ks] = qp[4 * ks];
+    // rope k-step e (0, 1), piece group gq -> slot (4e + gq) ^ (n & 7) of row n
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      *reinterpret_cast<MLA_LDS bf16x8*>(qrope_w + h * 2048 + n * 128 +
+                                         16 * ((4 * e + gq) ^ (n & 7))) = qp[4 * (16 + e)];
+  }
+  // per-lane read bases of the rope quarter, one per k-step
+  const MLA_LDS char* const qrope[2] = {qrope_w + n * 128 + 16 * (gq ^ (n & 7)),
+                                        qrope_w + n * 128 + 16 * ((4 + gq) ^ (n & 7))};
+  f32x4 oacc[NH][32];
+  float m_ref[NH], l_run[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+#pragma unroll
+    for (int f = 0; f < 32; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_ref[h] = -INFINITY;
+    l_run[h] = 0.f;
+  }
+  // restart flag of this workgroup (LDS is full): written by any wavefront,
+  // read by all after a barrier, which orders it within the workgroup
+  int* flag = a.restart_flag + blockIdx.x;
+  if (threadIdx.x == 0) __atomic_store_n(flag, 0, __ATOMIC_RELAXED);
 
   const int tok_begin = p0 * kPage;
   const int tok_end = min(p1 * kPage, len);
-  const int nchunks = (tok_end - tok_begin + CHUNK - 1) / CHUNK;
+  const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
   const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
   const char* cache = reinterpret_cast<const char*>(a.cache);
-  auto chunk_src = [&](int j) -> const char* {
-    const int t = tok_begin + j * CHUNK;
+  const char* zero = reinterpret_cast<const char*>(a.zero_row);
+  auto issue = [&](int j) {
+    const int t = tok_begin + j * kChunk;
     const int64_t blk = bt[t / kPage];
-    return cache + (blk * kPage + (t % kPage)) * (int64_t)kEntryBytes;
+    const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kEntryBytes;
+    load_chunk<NW>(lds + (j % NBUF) * kBufBytes, src, zero, len - t, wave, lane);
   };
-  auto run = [&](const MLA_LDS char* buf, int j) {
-    const int t0 = tok_begin + j * CHUNK;
-    if (t0 + CHUNK - 1 > tmax)
-      compute_chunk<NW, CHUNK, true>(buf, qreg, oacc, m_run, l_run, lane, t0, tmax, len,
-                                     a.scale_log2);
+  auto buf_of = [&](int j) -> const MLA_LDS char* { return lds + (j % NBUF) * kBufBytes; };
+  constexpr int kPer = Dma<NW>::kPerWave;
+  // visibility limit of chunk j for this lane, relative to its slot 16t + i
+  auto chunk_limits = [&](int j, int (&lim)[NH]) {
+    const int t0 = tok_begin + j * kChunk;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) lim[h] = tmax[h] - t0 - 4 * gq;
+  };
+  // wait until chunk j has landed, given that chunks up to `issued - 1` were issued
+  auto wait_for = [&](int j, int issued) {
+    if (issued - 1 - j >= 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
+    else if (issued - 1 - j == 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
     else
-      compute_chunk<NW, CHUNK, false>(buf, qreg, oacc, m_run, l_run, lane, t0, tmax, len,
-                                      a.scale_log2);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
 
-  if (nchunks > 0) load_chunk<NW, CHUNK>(lds0, chunk_src(0), wave, lane);
-  for (int j = 0; j < nchunks; j += 2) {
-    __builtin_amdgcn_s_waitcnt(0);
+  // ---- main pass: reference = first finite chunk max per row ---------------
+  // Ring: while chunk j's P.V and chunk j+1's scores run, chunks j+2 ..
+  // j+NBUF-2 are in flight; chunk j+NBUF-1 is issued into chunk j-1's slot.
+  // (a wavefront that needs a restart keeps going with a useless result;
+  // the flag is read once, after the pass)
+  bool restart = false;
+  {
+    int issued = 0;
+    for (; issued < NBUF - 1 && issued < nchunks; ++issued) issue(issued);
+    f32x4 sacc[NH][2];
+    bf16x8 pk[NH];
+    wait_for(0, issued);
     __syncthreads();
-    if (j + 1 < nchunks) load_chunk<NW, CHUNK>(lds1, chunk_src(j + 1), wave, lane);
-    run(lds0, j);
-    if (j + 1 >= nchunks) break;
-    __builtin_amdgcn_s_waitcnt(0);
+    score_chunk<NH>(buf_of(0), sbase_even, sbase_odd, qreg, qrope, sacc);
+    for (int j = 0; j < nchunks; ++j) {
+      const bool has_next = j + 1 < nchunks;
+      if (has_next) {
+        wait_for(j + 1, issued);
+        __syncthreads();  // chunk j+1 landed everywhere; chunk j-1's slot is free
+        if (issued < nchunks) issue(issued++);
+      }
+      int lim[NH];
+      chunk_limits(j, lim);
+      // softmax of chunk j overlaps the score MFMAs of chunk j+1 (for the
+      // last chunk the scores of its own slot are recomputed and dropped, so
+      // that both always sit in one basic block)
+      f32x4 snext[NH][2];
+      const bool need =
+          softmax_chunk<NH>(sacc, pk, m_ref, l_run, lim, a.scale_log2, false);
+      score_chunk<NH>(buf_of(has_next ? j + 1 : j), sbase_even, sbase_odd, qreg, qrope, snext);
+      if (__builtin_amdgcn_ballot_w64(need) != 0 && lane == 0)
+        __atomic_store_n(flag, 1, __ATOMIC_RELAXED);
+      pv_chunk<NH>(buf_of(j), vbase, pk, oacc);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        sacc[h][0] = snext[h][0];
+        sacc[h][1] = snext[h][1];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    if (j + 2 < nchunks) load_chunk<NW, CHUNK>(lds0, chunk_src(j + 2), wave, lane);
-    run(lds1, j + 1);
+    restart = restart || __atomic_load_n(flag, __ATOMIC_RELAXED);
+  }
+
+  // ---- restart (rare): exact row max, then a pass with it as the reference --
+  if (restart) {
+    float m_exact[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) m_exact[h] = -INFINITY;
+    for (int j = 0; j < nchunks; ++j) {
+      issue(j);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();
+      f32x4 sacc[NH][2];
+      int lim[NH];
+      chunk_limits(j, lim);
+      score_chunk<NH>(buf_of(j), sbase_even, sbase_odd, qreg, qrope, sacc);
+      max_chunk<NH>(sacc, m_exact, lim, a.scale_log2);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      m_ref[h] = m_exact[h];
+      l_run[h] = 0.f;
+#pragma unroll
+      for (int f = 0; f < 32; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int j = 0; j < nchunks; ++j) {
+      issue(j);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();
+      f32x4 sacc[NH][2];
+      bf16x8 pk[NH];
+      int lim[NH];
+      chunk_limits(j, lim);
+      score_chunk<NH>(buf_of(j), sbase_even, sbase_odd, qreg, qrope, sacc);
+      softmax_chunk<NH>(sacc, pk, m_ref, l_run, lim, a.scale_log2, true);
+      pv_chunk<NH>(buf_of(j), vbase, pk, oacc);
+      __syncthreads();
+    }
   }
 
   // ---- finalise: normalised rows and log2-sum-exp ---------------------------
-  float l = l_run;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  const float lse = l > 0.f ? m_run + __builtin_amdgcn_logf(l) : -INFINITY;
-  const int64_t orow = (int64_t)item * a.rows_per_seq + row0 + n;
-  float* op = a.o_part + orow * kLatent + 4 * gq;
 #pragma unroll
-  for (int f = 0; f < 32; ++f) *reinterpret_cast<f32x4*>(op + 16 * f) = oacc[f] * inv;
-  if (gq == 0) a.lse_part[orow] = lse;
+  for (int h = 0; h < NH; ++h) {
+    float l = l_run[h];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float lse = l > 0.f ? m_ref[h] + __builtin_amdgcn_logf(l) : -INFINITY;
+    const int64_t orow = (int64_t)item * a.rows_per_seq + row0 + 16 * h + n;
+    float* op = a.o_part + orow * kLatent + 4 * gq;
+#pragma unroll
+    for (int f = 0; f < 32; ++f) *reinterpret_cast<f32x4*>(op + 16 * f) = oacc[h][f] * inv;
+    if (gq == 0) a.lse_part[orow] = lse;
+  }
 }
 
 DecodeConfig decode_config(int rows_per_seq) {
   const int groups = rows_per_seq / 16;
   DecodeConfig c;
-  if (groups % 4 == 0) {
+  c.chunk = kChunk;
+  if (groups % 8 == 0) {
     c.waves = 4;
-    c.chunk = 64;
-  } else if (groups % 2 == 0) {
+    c.heads_per_wave = 2;
+    c.nbuf = 4;
+  } else if (groups % 4 == 0) {
     c.waves = 2;
-    c.chunk = 32;
+    c.heads_per_wave = 2;
+    c.nbuf = 4;
+  } else if (groups % 2 == 0) {
+    c.waves = 1;
+    c.heads_per_wave = 2;
+    c.nbuf = 4;
   } else {
     c.waves = 1;
-    c.chunk = 32;
+    c.heads_per_wave = 1;
+    c.nbuf = 4;
   }
-  c.lds_bytes = 2 * c.chunk * kEntryBytes;
-  c.wgs_per_cu = (160 * 1024) / c.lds_bytes;
+  c.lds_bytes = c.nbuf * kBufBytes + c.waves * c.heads_per_wave * 2048;
+  // each wavefront uses more than half a SIMD's registers: one per SIMD
+  c.wgs_per_cu = min((160 * 1024) / c.lds_bytes, 4 / c.waves);
   return c;
 }
 
-template <int NW, int CHUNK>
+template <int NW, int NH, int NBUF>
 static hipError_t launch_t(int grid, const DecodeArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<NW, CHUNK>), dim3(grid), dim3(NW * 64), 0, stream, args);
+  hipLaunchKernelGGL((decode_kernel<NW, NH, NBUF>), dim3(grid), dim3(NW * 64), 0, stream, args);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const uint16_t* cache,
                          const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
                          int heads, int q_len, float scale_log2, PlanView plan, int max_items,
-                         float* o_part, float* lse_part, hipStream_t stream) {
+                         float* o_part, float* lse_part, const uint16_t* zero_row,
+                         int* restart_flags, hipStream_t stream) {
   DecodeArgs args;
+  args.zero_row = zero_row;
+  args.restart_flag = restart_flags;
   args.q_abs = q_abs;
   args.cache = cache;
   args.block_table = block_table;
@@ -355,13 +509,14 @@ hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const u
   args.heads = heads;
   args.q_len = q_len;
   args.rows_per_seq = heads * q_len;
-  args.row_groups = args.rows_per_seq / (16 * cfg.waves);
+  args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
   args.scale_log2 = scale_log2;
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
-  if (cfg.waves == 4) return launch_t<4, 64>(grid, args, stream);
-  if (cfg.waves == 2) return launch_t<2, 32>(grid, args, stream);
-  return launch_t<1, 32>(grid, args, stream);
+  if (cfg.waves == 4) return launch_t<4, 2, 4>(grid, args, stream);
+  if (cfg.waves == 2) return launch_t<2, 2, 4>(grid, args, stream);
+  if (cfg.heads_per_wave == 2) return launch_t<1, 2, 4>(grid, args, stream);
+  return launch_t<1, 1, 4>(grid, args, stream);
 }
 
 }  // namespace mla

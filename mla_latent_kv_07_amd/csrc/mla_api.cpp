@@ -51,7 +51,8 @@ struct Layout {
   int slots = 0;
   DecodeConfig cfg{};
   size_t off_header = 0, off_item_b = 0, off_item_p0 = 0, off_item_p1 = 0, off_seq_start = 0,
-         off_seq_count = 0, off_qabs = 0, off_opart = 0, off_lse = 0, total = 0;
+         off_seq_count = 0, off_zero = 0, off_flags = 0, off_qabs = 0, off_opart = 0, off_lse = 0,
+         total = 0;
 };
 
 // Workspace layout for one decode call (pure function of the sizes).
@@ -59,7 +60,7 @@ Layout make_layout(int heads, int batch, int q_len, int hint) {
   Layout L;
   const int rows = heads * q_len;
   L.cfg = decode_config(rows);
-  const int row_groups = rows / (16 * L.cfg.waves);
+  const int row_groups = rows / (16 * L.cfg.waves * L.cfg.heads_per_wave);
   L.slots = device_cus() * L.cfg.wgs_per_cu / row_groups;
   if (L.slots < 1) L.slots = 1;
   L.max_items = hint > 0 ? batch * hint : batch + 4 * L.slots;
@@ -75,6 +76,8 @@ Layout make_layout(int heads, int batch, int q_len, int hint) {
   L.off_item_p1 = take(4 * (size_t)L.max_items);
   L.off_seq_start = take(4 * (size_t)batch);
   L.off_seq_count = take(4 * (size_t)batch);
+  L.off_zero = take(kEntryBytes);
+  L.off_flags = take(4 * ((size_t)L.max_items + 8) * row_groups);
   L.off_qabs = take((size_t)batch * rows * kEntry * 2);
   L.off_opart = take((size_t)L.max_items * rows * kLatent * 4);
   L.off_lse = take((size_t)L.max_items * rows * 4);
@@ -201,6 +204,7 @@ int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void
   plan.item_p1 = reinterpret_cast<int32_t*>(ws + L.off_item_p1);
   plan.seq_start = reinterpret_cast<int32_t*>(ws + L.off_seq_start);
   plan.seq_count = reinterpret_cast<int32_t*>(ws + L.off_seq_count);
+  plan.zero_row = reinterpret_cast<int32_t*>(ws + L.off_zero);
   uint16_t* q_abs = reinterpret_cast<uint16_t*>(ws + L.off_qabs);
   float* o_part = reinterpret_cast<float*>(ws + L.off_opart);
   float* lse_part = reinterpret_cast<float*>(ws + L.off_lse);
@@ -211,17 +215,17 @@ int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void
 
   const int pc = g_prof.used < g_prof.max_calls ? g_prof.used++ : -1;
   prof_mark(pc, 0, s);
-  hipError_t e = launch_plan(seq_lens, batch, max_pages, L.slots, L.max_items, num_splits_hint,
-                             item_cost, plan, s);
+  hipError_t e = launch_prep(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_b),
+                             heads, batch * q_len, q_abs, seq_lens, batch, max_pages, L.slots,
+                             L.max_items, num_splits_hint, item_cost, plan, s);
   prof_mark(pc, 1, s);
-  if (e == hipSuccess)
-    e = launch_qabsorb(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_b), heads,
-                       batch * q_len, q_abs, s);
   prof_mark(pc, 2, s);
   if (e == hipSuccess)
     e = launch_decode(L.cfg, q_abs, static_cast<const uint16_t*>(cache), block_table, bt_stride,
                       seq_lens, heads, q_len, softmax_scale * 1.4426950408889634f, plan,
-                      L.max_items, o_part, lse_part, s);
+                      L.max_items, o_part, lse_part,
+                      reinterpret_cast<const uint16_t*>(plan.zero_row),
+                      reinterpret_cast<int*>(ws + L.off_flags), s);
   prof_mark(pc, 3, s);
   if (e == hipSuccess)
     e = launch_combine(o_part, lse_part, plan, static_cast<const uint16_t*>(kv_b), heads, q_len,

@@ -5,25 +5,39 @@
 // block; "DeepSeek-V2-Lite 模型结构详解" §五 gives the identity
 // q . (W_k c) = (W_k^T q) . c that moves W_UK to the query side.
 //
+// The same launch also makes the split plan (plan.h) in one extra workgroup,
+// so the planner's latency hides under the absorption.
+//
 // One workgroup per (head, 128 latent columns); W_UK[h][:, cols] (32 KB) is
 // staged in LDS and read as the MFMA A operand with the gfx950 transposing
 // LDS read (the contraction index d is W_UK's row index).  The query rows are
 // the B operand, straight from global memory.  Result rows are written with
 // 8-byte stores (4 consecutive latent columns per lane).
 #include "mla_common.h"
+#include "plan.h"
 
 namespace mla {
 
 constexpr int kQaCols = 128;                 // latent columns per workgroup
 constexpr int kQaStride = kQaCols * 2 + 32;  // padded LDS row of W_UK (bytes)
 
-__global__ __launch_bounds__(256) void qabsorb_kernel(const uint16_t* __restrict__ q,
-                                                      const uint16_t* __restrict__ kv_b,
-                                                      int heads, int rows,
-                                                      uint16_t* __restrict__ q_abs) {
-  __shared__ __attribute__((aligned(16))) char w_lds[kNope * kQaStride];
-  const int h = blockIdx.x;
-  const int nc = blockIdx.y;  // column chunk
+constexpr int kPrepSmem = kNope * kQaStride > kPlanSmemBytes ? kNope * kQaStride : kPlanSmemBytes;
+static_assert(kPlanThreads == 256, "the plan runs on one 256-thread workgroup");
+
+// Blocks 0 .. 4H-1: absorption of head b/4, latent columns (b%4)*128 .. +128.
+// Block 4H: the split plan (independent work, hidden under the absorption).
+__global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ kv_b, int heads,
+                                                   int rows, uint16_t* __restrict__ q_abs,
+                                                   PlanArgs pa) {
+  __shared__ __attribute__((aligned(16))) char smem[kPrepSmem];
+  if (blockIdx.x == (unsigned)heads * (kLatent / kQaCols)) {
+    plan_block(pa, (MLA_LDS char*)smem);
+    return;
+  }
+  MLA_LDS char* w_lds = (MLA_LDS char*)smem;
+  const int h = blockIdx.x / (kLatent / kQaCols);
+  const int nc = blockIdx.x % (kLatent / kQaCols);  // column chunk
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -35,7 +49,7 @@ __global__ __launch_bounds__(256) void qabsorb_kernel(const uint16_t* __restrict
     const int p = k * 256 + tid;
     const int d = p >> 4;
     const int c16 = p & 15;
-    *reinterpret_cast<u16x8*>(w_lds + d * kQaStride + c16 * 16) =
+    *reinterpret_cast<MLA_LDS u16x8*>(w_lds + d * kQaStride + c16 * 16) =
         *reinterpret_cast<const u16x8*>(wuk + (int64_t)d * kLatent + c16 * 8);
   }
   // q_pe passes through unchanged (done once per head, by column chunk 0)
@@ -64,9 +78,9 @@ __global__ __launch_bounds__(256) void qabsorb_kernel(const uint16_t* __restrict
       const int c0 = wave * 32 + mt * 16 + 4 * qq;
       const int d0 = 32 * ks + 8 * g + r;
       const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (MLA_LDS bf16x4*)((MLA_LDS char*)w_lds + d0 * kQaStride + c0 * 2));
+          (MLA_LDS bf16x4*)(w_lds + d0 * kQaStride + c0 * 2));
       const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (MLA_LDS bf16x4*)((MLA_LDS char*)w_lds + (d0 + 4) * kQaStride + c0 * 2));
+          (MLA_LDS bf16x4*)(w_lds + (d0 + 4) * kQaStride + c0 * 2));
       aw[mt][ks] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   }
@@ -99,10 +113,13 @@ __global__ __launch_bounds__(256) void qabsorb_kernel(const uint16_t* __restrict
   }
 }
 
-hipError_t launch_qabsorb(const uint16_t* q, const uint16_t* kv_b, int heads, int rows,
-                          uint16_t* q_abs, hipStream_t stream) {
-  hipLaunchKernelGGL(qabsorb_kernel, dim3(heads, kLatent / kQaCols), dim3(256), 0, stream, q,
-                     kv_b, heads, rows, q_abs);
+hipError_t launch_prep(const uint16_t* q, const uint16_t* kv_b, int heads, int rows,
+                       uint16_t* q_abs, const int32_t* seq_lens, int batch, int max_pages,
+                       int slots, int max_items, int splits_hint, float item_cost_pages,
+                       PlanView plan, hipStream_t stream) {
+  PlanArgs pa{seq_lens, batch, max_pages, slots, max_items, splits_hint, item_cost_pages, plan};
+  hipLaunchKernelGGL(prep_kernel, dim3(heads * (kLatent / kQaCols) + 1), dim3(256), 0, stream, q,
+                     kv_b, heads, rows, q_abs, pa);
   return hipGetLastError();
 }
 

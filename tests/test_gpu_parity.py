@@ -227,3 +227,24 @@ def test_error_status_on_gpu():
                    dev(d["block_table"], torch), dev(d["seq_lens"], torch), 10,
                    workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
     assert ei.value.status == 4
+
+
+def test_decode_restart_on_score_jump():
+    """One late position scaled 20x makes some heads' scores jump far above the
+    first chunk's max; the kernel must restart those items (exact-max pass)
+    and still match the oracle.  Outputs are large here, so the max error is
+    taken relative to the largest output."""
+    torch = _torch()
+    say("[decode] large late score (restart path)")
+    d = wl.make_inputs(2, 1, 128, [300, 200], permute=True, seed=45)
+    cache = ref_cache(d)
+    for b, p in ((0, 250), (1, 70)):
+        row = cache[d["block_table"][b, p // 64], p % 64]
+        from oracle import bf16_bits_to_f64, f64_to_bf16_bits
+        row[:] = f64_to_bf16_bits(bf16_bits_to_f64(row) * 20.0)
+    got = run_decode(d, dev(cache, torch), torch)
+    ref = decode_expanded(d["q"], d["kv_b"], cache, d["block_table"], d["seq_lens"], 1)
+    mx, rr = errors(got, ref)
+    rel_max = mx / float(np.max(np.abs(ref)))
+    say(f"   max-abs/max|ref| {rel_max:.3e} rel-rms {rr:.3e}")
+    assert rel_max <= MAX_ABS and rr <= REL_RMS
