@@ -135,15 +135,16 @@ int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void
 
 /*
  * mla_profile_enable / mla_profile_collect — stage timing for benchmarks.
- * While enabled (max_calls > 0), each mla_decode call records five HIP events
- * on its stream: before the split planner, the query absorption, the split-KV
- * decode kernel, the merge + projection kernel, and after it.  Events come
- * from a pool of max_calls sets created here (hipEventCreate; no device
- * memory); calls beyond the pool are not timed.  mla_profile_enable(0)
- * releases the pool.  mla_profile_collect waits for the recorded events and
- * writes, per stage, the summed milliseconds over the timed calls into
- * stage_ms[4] (plan, absorb, decode, combine) and the call count into *calls,
- * then empties the pool for reuse.  Not thread-safe; for benchmarks only.
+ * While enabled (max_calls > 0), each mla_decode call records four HIP events
+ * on its stream: before the prep kernel (query absorption + split plan),
+ * before the split-KV decode kernel, before the merge + projection kernel, and
+ * after it.  Events come from a pool of max_calls sets created here
+ * (hipEventCreate; no device memory); calls beyond the pool are not timed.
+ * mla_profile_enable(0) releases the pool.  mla_profile_collect waits for the
+ * recorded events and writes, per stage, the summed milliseconds over the
+ * timed calls into stage_ms[3] (prep, decode, combine) and the call count into
+ * *calls, then empties the pool for reuse.  Each recorded event adds a few
+ * microseconds to the stage it closes.  Not thread-safe; for benchmarks only.
  */
 int mla_profile_enable(int32_t max_calls);
 int mla_profile_collect(double* stage_ms, int32_t* calls);

@@ -161,7 +161,7 @@ def decode(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, *,
     return out
 
 
-STAGES = ("plan", "absorb", "decode", "combine")
+STAGES = ("prep", "decode", "combine")
 
 
 def profile_enable(max_calls: int) -> None:
@@ -173,7 +173,7 @@ def profile_enable(max_calls: int) -> None:
 
 def profile_collect() -> tuple[dict, int]:
     """Summed milliseconds per stage over the timed decode calls, and their count."""
-    ms = (ctypes.c_double * 4)()
+    ms = (ctypes.c_double * len(STAGES))()
     calls = ctypes.c_int32()
     st = load().mla_profile_collect(ms, ctypes.byref(calls))
     if st != 0:

@@ -32,14 +32,18 @@
 //   * The softmax of chunk j is scheduled under the score MFMAs of chunk j+1
 //     (software pipelining inside the wavefront), so the vector ALU work
 //     hides behind the matrix cores.
-//   * Online softmax in log2 units with a fixed reference per row: the first
-//     finite chunk max.  Probabilities are 2^(s - ref) and stay below
-//     2^kSlack; the fp32 accumulators are never rescaled.  If a later score
-//     exceeds ref + kSlack (never for well-scaled attention, but possible),
-//     the workgroup restarts the item: one pass for the exact row max, one
-//     pass with that max as the reference.
+//   * Online softmax in log2 units (the query arrives pre-multiplied by
+//     softmax_scale * log2 e) with a fixed reference per row: the max of the
+//     item's first chunk, the only chunk that needs a cross-lane reduction.
+//     Later chunks compute p = 2^(s - ref) and check that each lane's chunk
+//     sum stays <= 2^16, which bounds every p; the fp32 accumulators are never
+//     rescaled.  If the check fails (never for well-scaled attention, but
+//     possible), the workgroup restarts the item: one pass for the exact row
+//     max, one pass with that max as the reference.
 // Output per work item: normalised fp32 rows [rows, 512] and their log2-sum-
 // exp, merged across items by the combine kernel.
+#include <type_traits>
+
 #include "mla_common.h"
 
 namespace mla {
@@ -47,11 +51,9 @@ namespace mla {
 struct DecodeArgs {
   const uint16_t* q_abs;     // [B * rows_per_seq, 576]
   const uint16_t* cache;     // [num_blocks, 64, 576]
-  const int32_t* block_table;
   const int32_t* seq_lens;
   float* o_part;             // [max_items, rows_per_seq, 512]
   float* lse_part;           // [max_items, rows_per_seq]
-  const uint16_t* zero_row;  // 576 zeros: source of the copies of positions >= len
   int* restart_flag;         // one int per workgroup (workgroup-local communication)
   PlanView plan;
   int bt_stride;
@@ -59,12 +61,11 @@ struct DecodeArgs {
   int q_len;
   int rows_per_seq;
   int row_groups;
-  float scale_log2;
 };
 
 constexpr int kChunk = 32;                     // positions per LDS stage
 constexpr int kBufBytes = kChunk * kEntryBytes;  // 36864
-constexpr float kSlack = 16.0f;                // log2 headroom above the reference max
+constexpr float kSlackPow = 65536.0f;          // 2^16: headroom above the reference max
 
 // Encoding of "s_waitcnt vmcnt(n)" (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -79,38 +80,55 @@ struct Dma {
 // Piece permutation inside each aligned group of 8 pieces of row r.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
-// Copy one chunk into the LDS ring slot `buf`.  Copy k fills LDS pieces
-// 64k .. 64k+63 (lane L -> piece Q = 64k + L of row Q / 72, slot Q % 72),
-// fetching global piece (Q % 72) ^ swz(row) of that row: the 64 lanes read
-// the same 1 KB of the chunk, permuted within 128-byte lines.  Rows >= nvalid
-// are copied from the zero row instead.
-template <int NW>
-__device__ __forceinline__ void load_chunk(MLA_LDS char* buf, const char* src, const char* zero,
-                                           int nvalid, int wave, int lane) {
-  // the empty asm keeps the per-lane addresses from being hoisted out of the
-  // chunk loop (registers are the scarce resource here)
-  asm volatile("" : "+v"(lane));
+// Per-lane source offsets of the wavefront's copies of one chunk.  Copy k
+// fills LDS pieces 64k .. 64k+63 (lane L -> piece Q = 64k + L, i.e. row Q / 72,
+// slot Q % 72) from piece (Q % 72) ^ swz(row) of that row: the 64 lanes read
+// the same contiguous 1 KB of the chunk, permuted within 128-byte lines.  The
+// offsets are the same for every chunk (a chunk is 36 KB of contiguous cache:
+// half a page), so they are computed once.
+template <int NW, int KP>
+__device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&off)[KP]) {
 #pragma unroll
-  for (int i = 0; i < Dma<NW>::kPerWave; ++i) {
+  for (int i = 0; i < KP; ++i) {
     const int k = i * NW + wave;
     const int q = 64 * k + lane;
     const int row = q / kChunk16;
     const int col = q - row * kChunk16;
-    const int gcol = col ^ swz(row);
-    const char* g = (row < nvalid ? src + row * kEntryBytes : zero) + gcol * 16;
-    __builtin_amdgcn_global_load_lds(g, buf + k * 1024, 16, 0, 0);
+    off[i] = (uint32_t)(row * kEntryBytes + 16 * (col ^ swz(row)));
   }
+}
+
+// Buffer descriptor word 3 for gfx9-family raw buffer loads.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Copy one chunk (36 KB at `src`, a wavefront-uniform address) into the LDS
+// ring slot `buf` (wavefront-uniform): buffer loads straight to LDS, with the
+// chunk as the buffer (scalar descriptor) and a 32-bit per-lane offset.
+template <int NW, int KP>
+__device__ __forceinline__ void load_chunk(MLA_LDS char* buf, const char* src,
+                                           const uint32_t* off, int wave) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, kBufBytes, kRsrcWord3);
+#pragma unroll
+  for (int i = 0; i < KP; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, buf + (i * NW + wave) * 1024, 16, off[i], 0, 0,
+                                             0);
 }
 
 // Scores of one chunk for the wavefront's NH row groups: sacc[h][t] holds
 // S^T for positions 16t..16t+15.  The LDS reads of k-step ks + KPD are issued
 // before the MFMAs of k-step ks.
+// Query k-steps kept in registers; k-steps kQReg..17 (the last 128 latent
+// features and the 64 rope features) are read from LDS.
+constexpr int kQReg = 12;
+constexpr int kQTailBytes = (18 - kQReg) * 64;  // per query row
+
 template <int NH>
 __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_even,
-                                            int sbase_odd, const bf16x8 (&qreg)[NH][16],
-                                            const MLA_LDS char* const (&qrope)[2],
+                                            int sbase_odd, const bf16x8 (&qreg)[NH][kQReg],
+                                            const MLA_LDS char* const (&qt)[2],
                                             f32x4 (&sacc)[NH][2]) {
-  constexpr int KPD = 1;
+  constexpr int KPD = 2;
 #pragma unroll
   for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -123,10 +141,10 @@ __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_e
     return *reinterpret_cast<const MLA_LDS bf16x8*>((ks & 1 ? bo : be) + 64 * ks +
                                                     16 * kEntryBytes * t);
   };
-  // the rope quarter of the query (k-steps 16, 17) lives in LDS: row group h,
-  // k-step 16 + e of this lane at qrope[e] + h*2048
+  // query k-step kQReg + e of row group h: qt[e & 1] + 64e + h*16*kQTailBytes
   auto qload = [&](int h, int e) -> bf16x8 {
-    return *reinterpret_cast<const MLA_LDS bf16x8*>(qrope[e] + h * 2048);
+    return *reinterpret_cast<const MLA_LDS bf16x8*>(qt[e & 1] + 64 * e +
+                                                    h * 16 * kQTailBytes);
   };
   bf16x8 kb[KPD + 1][2];
 #pragma unroll
@@ -141,7 +159,7 @@ __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_e
     }
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      const bf16x8 qb = ks < 16 ? qreg[h][ks < 16 ? ks : 0] : qload(h, ks - 16);
+      const bf16x8 qb = ks < kQReg ? qreg[h][ks < kQReg ? ks : 0] : qload(h, ks - kQReg);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         sacc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks % (KPD + 1)][t], qb,
@@ -150,33 +168,35 @@ __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_e
   }
 }
 
-// Softmax of one chunk's scores (log2 units) into bf16 probabilities pk[h]
-// (the B operand of the P.V product).  Returns true if some row's chunk max
-// exceeds its reference by more than kSlack (the item must restart).
-template <int NH>
+// Softmax of one chunk's scores (already scaled to log2 units: the query was
+// pre-multiplied by softmax_scale * log2(e)) into bf16 probabilities pk[h],
+// the B operand of the P.V product.
+//   FIRST: the chunk sets each row's reference m_ref = its max (cross-lane
+//          reduction over the 4 lanes of a head).  Later chunks reuse it.
+//   MASK:  slots beyond the row's causal limit / the sequence end get p = 0
+//          (lim[h]: the lane's slot 16t + i is visible iff 16t + i <= lim[h]).
+// Returns true if some probability may exceed 2^kSlack (sum check, see the
+// file header): the item must restart with an exact reference.
+template <int NH, bool FIRST, bool MASK>
 __device__ __forceinline__ bool softmax_chunk(f32x4 (&sacc)[NH][2], bf16x8 (&pk)[NH],
                                               float (&m_ref)[NH], float (&l_run)[NH],
-                                              const int (&lim)[NH], float scale_log2,
-                                              bool fixed_ref) {
-  // lim[h]: the lane's slot 16t + i is visible iff 16t + i <= lim[h]
+                                              const int (&lim)[NH]) {
   bool restart = false;
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    float mloc = -INFINITY;
+    if (MASK) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sc = (16 * t + i > lim[h]) ? -INFINITY : sacc[h][t][i] * scale_log2;
-        sacc[h][t][i] = sc;
-        mloc = fmaxf(mloc, sc);
-      }
+        for (int i = 0; i < 4; ++i)
+          sacc[h][t][i] = (16 * t + i > lim[h]) ? -INFINITY : sacc[h][t][i];
     }
-    if (!fixed_ref) {
+    if (FIRST) {
+      float mloc = fmaxf(fmaxf(fmaxf(sacc[h][0][0], sacc[h][0][1]), fmaxf(sacc[h][0][2], sacc[h][0][3])),
+                         fmaxf(fmaxf(sacc[h][1][0], sacc[h][1][1]), fmaxf(sacc[h][1][2], sacc[h][1][3])));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      if (m_ref[h] == -INFINITY) m_ref[h] = mloc;
-      restart |= mloc > m_ref[h] + kSlack;
+      m_ref[h] = mloc;
     }
     const float m_use = m_ref[h] == -INFINITY ? 0.f : m_ref[h];
     float psum = 0.f;
@@ -190,12 +210,12 @@ __device__ __forceinline__ bool softmax_chunk(f32x4 (&sacc)[NH][2], bf16x8 (&pk)
       }
     }
     l_run[h] += psum;
+    // every p <= psum, so psum <= 2^kSlack bounds them all (NaN/inf fail too)
+    if (!FIRST) restart |= !(psum <= kSlackPow);
   }
   return restart;
 }
 
-// O^T[f] += V^T[f] P^T for the 32 feature tiles of 16; V^T via the
-// transposing LDS read, read-ahead of VPD steps.
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgMfma = 0x008;
 constexpr int kSgValu = 0x002;
@@ -234,7 +254,7 @@ __device__ __forceinline__ void pv_chunk(const MLA_LDS char* buf, const int (&vb
 // Row max only (the first pass of a restart).
 template <int NH>
 __device__ __forceinline__ void max_chunk(const f32x4 (&sacc)[NH][2], float (&m)[NH],
-                                          const int (&lim)[NH], float scale_log2) {
+                                          const int (&lim)[NH]) {
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     float mloc = -INFINITY;
@@ -242,7 +262,7 @@ __device__ __forceinline__ void max_chunk(const f32x4 (&sacc)[NH][2], float (&m)
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        mloc = fmaxf(mloc, (16 * t + i > lim[h]) ? -INFINITY : sacc[h][t][i] * scale_log2);
+        mloc = fmaxf(mloc, (16 * t + i > lim[h]) ? -INFINITY : sacc[h][t][i]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
     m[h] = fmaxf(m[h], mloc);
@@ -250,11 +270,14 @@ __device__ __forceinline__ void max_chunk(const f32x4 (&sacc)[NH][2], float (&m)
 }
 
 template <int NW, int NH, int NBUF>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
-  static_assert(NBUF >= 3 && NBUF * kBufBytes + NW * NH * 2048 <= 160 * 1024,
-                "LDS ring of NBUF chunks plus the query rope quarter");
-  // ring of NBUF chunks, then the rope quarter of the workgroup's query rows
-  __shared__ __attribute__((aligned(1024))) char lds_raw[NBUF * kBufBytes + NW * NH * 2048];
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
+                                                         const int32_t* __restrict__ block_table) {
+  static_assert(NBUF >= 2 && NBUF <= 3 &&
+                    NBUF * kBufBytes + NW * NH * 16 * kQTailBytes <= 160 * 1024,
+                "LDS ring of NBUF chunks plus the query tail");
+  // ring of NBUF chunks, then the query k-steps kQReg..17 of the workgroup's rows
+  __shared__ __attribute__((aligned(1024))) char lds_raw[NBUF * kBufBytes +
+                                                         NW * NH * 16 * kQTailBytes];
   MLA_LDS char* lds = (MLA_LDS char*)lds_raw;
 
   // blockIdx -> (item, row group); the row groups of one item land on the
@@ -270,14 +293,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int p0 = a.plan.item_p0[item];
   const int p1 = a.plan.item_p1[item];
   const int len = a.seq_lens[b];
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it scalar
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int gq = lane >> 4;
   const int row0 = (rg * NW + wave) * 16 * NH;  // first row of this wave in the sequence
   int tmax[NH];                                 // last visible position per row group
+  int tmax_min = 0x7fffffff;
 #pragma unroll
-  for (int h = 0; h < NH; ++h) tmax[h] = len - a.q_len + (row0 + 16 * h) / a.heads;
+  for (int h = 0; h < NH; ++h) {
+    tmax[h] = len - a.q_len + (row0 + 16 * h) / a.heads;
+    tmax_min = min(tmax_min, tmax[h]);
+  }
 
   // per-lane LDS bases of the two read patterns (see the layout above)
   const int xs = gq ^ swz(n);
@@ -296,25 +323,32 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       vbase[f4] = row * kEntryBytes + 16 * ((2 * f4) ^ y) + 8 * (qq & 1);
   }
 
-  // query rows: the 512 latent features stay in registers (lane holds
-  // features 32ks + 8gq .. +8 of row n), the 64 rope features go to LDS
-  bf16x8 qreg[NH][16];
-  MLA_LDS char* qrope_w = lds + NBUF * kBufBytes + wave * NH * 2048;
+  // query rows: k-steps 0..kQReg-1 stay in registers (lane holds features
+  // 32ks + 8gq .. +8 of row n); k-steps kQReg..17 go to LDS, row r of the
+  // wavefront at qtail + r*kQTailBytes, piece p (16 B) at slot p ^ (r & 7)
+  bf16x8 qreg[NH][kQReg];
+  MLA_LDS char* qtail = lds + NBUF * kBufBytes + wave * NH * 16 * kQTailBytes;
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(
         a.q_abs + ((int64_t)b * a.rows_per_seq + row0 + 16 * h + n) * kEntry + 8 * gq);
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qreg[h][ks] = qp[4 * ks];
-    // rope k-step e (0, 1), piece group gq -> slot (4e + gq) ^ (n & 7) of row n
+    for (int ks = 0; ks < kQReg; ++ks) qreg[h][ks] = qp[4 * ks];
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
-      *reinterpret_cast<MLA_LDS bf16x8*>(qrope_w + h * 2048 + n * 128 +
-                                         16 * ((4 * e + gq) ^ (n & 7))) = qp[4 * (16 + e)];
+    for (int e = 0; e < 18 - kQReg; ++e)
+      *reinterpret_cast<MLA_LDS bf16x8*>(qtail + (16 * h + n) * kQTailBytes +
+                                         16 * ((4 * e + gq) ^ (n & 7))) = qp[4 * (kQReg + e)];
   }
-  // per-lane read bases of the rope quarter, one per k-step
-  const MLA_LDS char* const qrope[2] = {qrope_w + n * 128 + 16 * (gq ^ (n & 7)),
-                                        qrope_w + n * 128 + 16 * ((4 + gq) ^ (n & 7))};
+  // per-lane read bases: slot (4e + gq) ^ (n & 7) = 4(e ^ hb) + c with
+  // hb = (n >> 2) & 1, c = (gq ^ n) & 3, i.e. byte 64e + 16c + (e odd ? -64hb : 64hb)
+  const MLA_LDS char* qt[2];
+  {
+    const int hb = (n >> 2) & 1;
+    const int c = (gq ^ n) & 3;
+    const MLA_LDS char* rowq = qtail + n * kQTailBytes + 16 * c;
+    qt[0] = rowq + 64 * hb;
+    qt[1] = rowq - 64 * hb;
+  }
   f32x4 oacc[NH][32];
   float m_ref[NH], l_run[NH];
 #pragma unroll
@@ -332,16 +366,30 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   const int tok_begin = p0 * kPage;
   const int tok_end = min(p1 * kPage, len);
   const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
-  const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
+  // the last chunk of the sequence may end inside the chunk: its rows from
+  // `tail_rows` on hold other positions' slots (NaN sentinels, stale data)
+  // and are zeroed in LDS once the chunk has landed, before any wave reads it
+  const int tail_rows = tok_end - tok_begin - (nchunks - 1) * kChunk;
+  const int32_t* bt = block_table + (int64_t)b * a.bt_stride;  // scalar loads (restrict)
   const char* cache = reinterpret_cast<const char*>(a.cache);
-  const char* zero = reinterpret_cast<const char*>(a.zero_row);
+  uint32_t doff[Dma<NW>::kPerWave];
+  dma_offsets<NW>(wave, lane, doff);
   auto issue = [&](int j) {
     const int t = tok_begin + j * kChunk;
     const int64_t blk = bt[t / kPage];
     const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kEntryBytes;
-    load_chunk<NW>(lds + (j % NBUF) * kBufBytes, src, zero, len - t, wave, lane);
+    load_chunk<NW, Dma<NW>::kPerWave>(lds + (j % NBUF) * kBufBytes, src, doff, wave);
   };
   auto buf_of = [&](int j) -> const MLA_LDS char* { return lds + (j % NBUF) * kBufBytes; };
+  // after chunk j has landed in every wavefront's view (barrier passed)
+  auto fix_tail = [&](int j) {
+    if (j == nchunks - 1 && tail_rows < kChunk) {
+      MLA_LDS char* bp = lds + (j % NBUF) * kBufBytes;
+      for (int pc = tail_rows * kChunk16 + (int)threadIdx.x; pc < kChunk * kChunk16; pc += NW * 64)
+        *reinterpret_cast<MLA_LDS u16x8*>(bp + 16 * pc) = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      __syncthreads();
+    }
+  };
   constexpr int kPer = Dma<NW>::kPerWave;
   // visibility limit of chunk j for this lane, relative to its slot 16t + i
   auto chunk_limits = [&](int j, int (&lim)[NH]) {
@@ -349,19 +397,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < NH; ++h) lim[h] = tmax[h] - t0 - 4 * gq;
   };
-  // wait until chunk j has landed, given that chunks up to `issued - 1` were issued
+  // wait until chunk j has landed, given that chunks up to `issued - 1` were
+  // issued: at most the copies of the chunks issued after it may be pending
   auto wait_for = [&](int j, int issued) {
-    if (issued - 1 - j >= 2)
+    const int later = issued - 1 - j;
+    if (later >= 2)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
-    else if (issued - 1 - j == 1)
+    else if (later == 1)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
-
-  // ---- main pass: reference = first finite chunk max per row ---------------
-  // Ring: while chunk j's P.V and chunk j+1's scores run, chunks j+2 ..
-  // j+NBUF-2 are in flight; chunk j+NBUF-1 is issued into chunk j-1's slot.
+  // ---- main pass: reference = the first chunk's max per row ----------------
+  // Ring: while chunk j is computed, chunks j+1 .. j+NBUF-1 are in flight;
+  // chunk j+NBUF-1 is issued into chunk j-1's slot.
   // (a wavefront that needs a restart keeps going with a useless result;
   // the flag is read once, after the pass)
   bool restart = false;
@@ -370,33 +419,51 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
     for (; issued < NBUF - 1 && issued < nchunks; ++issued) issue(issued);
     f32x4 sacc[NH][2];
     bf16x8 pk[NH];
-    wait_for(0, issued);
-    __syncthreads();
-    score_chunk<NH>(buf_of(0), sbase_even, sbase_odd, qreg, qrope, sacc);
-    for (int j = 0; j < nchunks; ++j) {
-      const bool has_next = j + 1 < nchunks;
-      if (has_next) {
-        wait_for(j + 1, issued);
-        __syncthreads();  // chunk j+1 landed everywhere; chunk j-1's slot is free
-        if (issued < nchunks) issue(issued++);
-      }
+    // chunk j: scores, softmax, P.V
+    auto step = [&](auto first_c, auto mask_c, int j) -> bool {
+      constexpr bool kFirst = decltype(first_c)::value;
+      constexpr bool kMask = decltype(mask_c)::value;
       int lim[NH];
       chunk_limits(j, lim);
-      // softmax of chunk j overlaps the score MFMAs of chunk j+1 (for the
-      // last chunk the scores of its own slot are recomputed and dropped, so
-      // that both always sit in one basic block)
-      f32x4 snext[NH][2];
-      const bool need =
-          softmax_chunk<NH>(sacc, pk, m_ref, l_run, lim, a.scale_log2, false);
-      score_chunk<NH>(buf_of(has_next ? j + 1 : j), sbase_even, sbase_odd, qreg, qrope, snext);
+      // the phases stay in order: moving the next phase's LDS reads up would
+      // keep their registers live across this one
+      score_chunk<NH>(buf_of(j), sbase_even, sbase_odd, qreg, qt, sacc);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool need = softmax_chunk<NH, kFirst, kMask>(sacc, pk, m_ref, l_run, lim);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_chunk<NH>(buf_of(j), vbase, pk, oacc);
+      __builtin_amdgcn_sched_barrier(0);
+      return need;
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    // wait for chunk j; after the barrier chunk j-1's slot is free for the
+    // copy of chunk j + NBUF - 1
+    auto advance = [&](int j) {
+      wait_for(j, issued);
+      __syncthreads();
+      if (issued < nchunks) issue(issued++);
+      fix_tail(j);
+    };
+    auto flag_restart = [&](bool need) {
       if (__builtin_amdgcn_ballot_w64(need) != 0 && lane == 0)
         __atomic_store_n(flag, 1, __ATOMIC_RELAXED);
-      pv_chunk<NH>(buf_of(j), vbase, pk, oacc);
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        sacc[h][0] = snext[h][0];
-        sacc[h][1] = snext[h][1];
-      }
+    };
+    // chunk 0 sets the references (masked variant: it may be the last one);
+    // chunks from jm on reach past the causal limit of some row (or the
+    // sequence end) and take the masked variant; each range is its own loop
+    const int jm = max(1, min(nchunks, (tmax_min - tok_begin + 1) / kChunk));
+    if (nchunks > 0) {
+      advance(0);
+      flag_restart(step(T{}, T{}, 0));
+    }
+    for (int j = 1; j < jm; ++j) {
+      advance(j);
+      flag_restart(step(F{}, F{}, j));
+    }
+    for (int j = jm; j < nchunks; ++j) {
+      advance(j);
+      flag_restart(step(F{}, T{}, j));
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
@@ -412,11 +479,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       issue(j);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
+      fix_tail(j);
       f32x4 sacc[NH][2];
       int lim[NH];
       chunk_limits(j, lim);
-      score_chunk<NH>(buf_of(j), sbase_even, sbase_odd, qreg, qrope, sacc);
-      max_chunk<NH>(sacc, m_exact, lim, a.scale_log2);
+      score_chunk<NH>(buf_of(j), sbase_even, sbase_odd, qreg, qt, sacc);
+      max_chunk<NH>(sacc, m_exact, lim);
       __syncthreads();
     }
 #pragma unroll
@@ -430,12 +498,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
       issue(j);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
+      fix_tail(j);
       f32x4 sacc[NH][2];
       bf16x8 pk[NH];
       int lim[NH];
       chunk_limits(j, lim);
-      score_chunk<NH>(buf_of(j), sbase_even, sbase_odd, qreg, qrope, sacc);
-      softmax_chunk<NH>(sacc, pk, m_ref, l_run, lim, a.scale_log2, true);
+      score_chunk<NH>(buf_of(j), sbase_even, sbase_odd, qreg, qt, sacc);
+      softmax_chunk<NH, false, true>(sacc, pk, m_ref, l_run, lim);
       pv_chunk<NH>(buf_of(j), vbase, pk, oacc);
       __syncthreads();
     }
@@ -464,43 +533,43 @@ DecodeConfig decode_config(int rows_per_seq) {
   if (groups % 8 == 0) {
     c.waves = 4;
     c.heads_per_wave = 2;
-    c.nbuf = 4;
+    c.nbuf = 3;
   } else if (groups % 4 == 0) {
     c.waves = 2;
     c.heads_per_wave = 2;
-    c.nbuf = 4;
+    c.nbuf = 3;
   } else if (groups % 2 == 0) {
     c.waves = 1;
     c.heads_per_wave = 2;
-    c.nbuf = 4;
+    c.nbuf = 3;
   } else {
     c.waves = 1;
     c.heads_per_wave = 1;
-    c.nbuf = 4;
+    c.nbuf = 3;
   }
-  c.lds_bytes = c.nbuf * kBufBytes + c.waves * c.heads_per_wave * 2048;
+  c.lds_bytes = c.nbuf * kBufBytes + c.waves * c.heads_per_wave * 16 * kQTailBytes;
   // each wavefront uses more than half a SIMD's registers: one per SIMD
   c.wgs_per_cu = min((160 * 1024) / c.lds_bytes, 4 / c.waves);
   return c;
 }
 
 template <int NW, int NH, int NBUF>
-static hipError_t launch_t(int grid, const DecodeArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<NW, NH, NBUF>), dim3(grid), dim3(NW * 64), 0, stream, args);
+static hipError_t launch_t(int grid, const DecodeArgs& args, const int32_t* block_table,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<NW, NH, NBUF>), dim3(grid), dim3(NW * 64), 0, stream, args,
+                     block_table);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const uint16_t* cache,
                          const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
-                         int heads, int q_len, float scale_log2, PlanView plan, int max_items,
-                         float* o_part, float* lse_part, const uint16_t* zero_row,
+                         int heads, int q_len, PlanView plan, int max_items,
+                         float* o_part, float* lse_part,
                          int* restart_flags, hipStream_t stream) {
   DecodeArgs args;
-  args.zero_row = zero_row;
   args.restart_flag = restart_flags;
   args.q_abs = q_abs;
   args.cache = cache;
-  args.block_table = block_table;
   args.seq_lens = seq_lens;
   args.o_part = o_part;
   args.lse_part = lse_part;
@@ -510,13 +579,12 @@ hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const u
   args.q_len = q_len;
   args.rows_per_seq = heads * q_len;
   args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
-  args.scale_log2 = scale_log2;
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
-  if (cfg.waves == 4) return launch_t<4, 2, 4>(grid, args, stream);
-  if (cfg.waves == 2) return launch_t<2, 2, 4>(grid, args, stream);
-  if (cfg.heads_per_wave == 2) return launch_t<1, 2, 4>(grid, args, stream);
-  return launch_t<1, 1, 4>(grid, args, stream);
+  if (cfg.waves == 4) return launch_t<4, 2, 3>(grid, args, block_table, stream);
+  if (cfg.waves == 2) return launch_t<2, 2, 3>(grid, args, block_table, stream);
+  if (cfg.heads_per_wave == 2) return launch_t<1, 2, 3>(grid, args, block_table, stream);
+  return launch_t<1, 1, 3>(grid, args, block_table, stream);
 }
 
 }  // namespace mla

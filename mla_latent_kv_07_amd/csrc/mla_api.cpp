@@ -51,7 +51,7 @@ struct Layout {
   int slots = 0;
   DecodeConfig cfg{};
   size_t off_header = 0, off_item_b = 0, off_item_p0 = 0, off_item_p1 = 0, off_seq_start = 0,
-         off_seq_count = 0, off_zero = 0, off_flags = 0, off_qabs = 0, off_opart = 0, off_lse = 0,
+         off_seq_count = 0, off_flags = 0, off_qabs = 0, off_opart = 0, off_lse = 0,
          total = 0;
 };
 
@@ -76,7 +76,6 @@ Layout make_layout(int heads, int batch, int q_len, int hint) {
   L.off_item_p1 = take(4 * (size_t)L.max_items);
   L.off_seq_start = take(4 * (size_t)batch);
   L.off_seq_count = take(4 * (size_t)batch);
-  L.off_zero = take(kEntryBytes);
   L.off_flags = take(4 * ((size_t)L.max_items + 8) * row_groups);
   L.off_qabs = take((size_t)batch * rows * kEntry * 2);
   L.off_opart = take((size_t)L.max_items * rows * kLatent * 4);
@@ -87,14 +86,16 @@ Layout make_layout(int heads, int batch, int q_len, int hint) {
 
 // Benchmark stage timing (mla_profile_enable / mla_profile_collect).
 struct Profile {
-  std::vector<hipEvent_t> ev;  // 5 per call
+  std::vector<hipEvent_t> ev;  // kMarks per call
   int max_calls = 0;
   int used = 0;
 };
 Profile g_prof;
+constexpr int kStages = 3;  // prep, decode, combine
+constexpr int kMarks = kStages + 1;
 
 void prof_mark(int call, int k, hipStream_t s) {
-  if (call >= 0) hipEventRecord(g_prof.ev[call * 5 + k], s);
+  if (call >= 0) hipEventRecord(g_prof.ev[call * kMarks + k], s);
 }
 
 }  // namespace
@@ -108,7 +109,7 @@ int mla_profile_enable(int32_t max_calls) {
   g_prof.used = 0;
   if (max_calls <= 0) return MLA_OK;
   if (max_calls > 100000) return MLA_ERR_SHAPE;
-  g_prof.ev.resize((size_t)max_calls * 5);
+  g_prof.ev.resize((size_t)max_calls * kMarks);
   for (auto& e : g_prof.ev)
     if (hipEventCreate(&e) != hipSuccess) return MLA_ERR_HIP;
   g_prof.max_calls = max_calls;
@@ -117,12 +118,13 @@ int mla_profile_enable(int32_t max_calls) {
 
 int mla_profile_collect(double* stage_ms, int32_t* calls) {
   if (!stage_ms || !calls) return MLA_ERR_NULL;
-  for (int k = 0; k < 4; ++k) stage_ms[k] = 0.0;
+  for (int k = 0; k < kStages; ++k) stage_ms[k] = 0.0;
   for (int c = 0; c < g_prof.used; ++c) {
-    if (hipEventSynchronize(g_prof.ev[c * 5 + 4]) != hipSuccess) return MLA_ERR_HIP;
-    for (int k = 0; k < 4; ++k) {
+    if (hipEventSynchronize(g_prof.ev[c * kMarks + kStages]) != hipSuccess) return MLA_ERR_HIP;
+    for (int k = 0; k < kStages; ++k) {
       float ms = 0.f;
-      if (hipEventElapsedTime(&ms, g_prof.ev[c * 5 + k], g_prof.ev[c * 5 + k + 1]) != hipSuccess)
+      if (hipEventElapsedTime(&ms, g_prof.ev[c * kMarks + k], g_prof.ev[c * kMarks + k + 1]) !=
+          hipSuccess)
         return MLA_ERR_HIP;
       stage_ms[k] += ms;
     }
@@ -204,7 +206,6 @@ int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void
   plan.item_p1 = reinterpret_cast<int32_t*>(ws + L.off_item_p1);
   plan.seq_start = reinterpret_cast<int32_t*>(ws + L.off_seq_start);
   plan.seq_count = reinterpret_cast<int32_t*>(ws + L.off_seq_count);
-  plan.zero_row = reinterpret_cast<int32_t*>(ws + L.off_zero);
   uint16_t* q_abs = reinterpret_cast<uint16_t*>(ws + L.off_qabs);
   float* o_part = reinterpret_cast<float*>(ws + L.off_opart);
   float* lse_part = reinterpret_cast<float*>(ws + L.off_lse);
@@ -215,22 +216,23 @@ int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void
 
   const int pc = g_prof.used < g_prof.max_calls ? g_prof.used++ : -1;
   prof_mark(pc, 0, s);
+  // the absorbed query carries softmax_scale * log2(e): scores come out of the
+  // matrix cores in log2 units
   hipError_t e = launch_prep(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_b),
-                             heads, batch * q_len, q_abs, seq_lens, batch, max_pages, L.slots,
-                             L.max_items, num_splits_hint, item_cost, plan, s);
+                             heads, batch * q_len, softmax_scale * 1.4426950408889634f, q_abs,
+                             seq_lens, batch, max_pages, L.slots, L.max_items, num_splits_hint,
+                             item_cost, plan, s);
   prof_mark(pc, 1, s);
-  prof_mark(pc, 2, s);
   if (e == hipSuccess)
     e = launch_decode(L.cfg, q_abs, static_cast<const uint16_t*>(cache), block_table, bt_stride,
-                      seq_lens, heads, q_len, softmax_scale * 1.4426950408889634f, plan,
+                      seq_lens, heads, q_len, plan,
                       L.max_items, o_part, lse_part,
-                      reinterpret_cast<const uint16_t*>(plan.zero_row),
                       reinterpret_cast<int*>(ws + L.off_flags), s);
-  prof_mark(pc, 3, s);
+  prof_mark(pc, 2, s);
   if (e == hipSuccess)
     e = launch_combine(o_part, lse_part, plan, static_cast<const uint16_t*>(kv_b), heads, q_len,
                        batch, static_cast<uint16_t*>(out), s);
-  prof_mark(pc, 4, s);
+  prof_mark(pc, 3, s);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

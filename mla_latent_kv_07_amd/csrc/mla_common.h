@@ -55,7 +55,6 @@ struct PlanView {
   int32_t* item_p1;     // [max_items] one past the last page
   int32_t* seq_start;   // [B] first item of each sequence
   int32_t* seq_count;   // [B] number of items of each sequence
-  int32_t* zero_row;    // [288] = one cache entry of zeros, written by the planner
 };
 
 // ---- launch wrappers (each returns hipGetLastError() of its launch) --------
@@ -65,7 +64,8 @@ hipError_t launch_insert(const uint16_t* kv_a, const uint16_t* rms_w, float eps,
 
 // query absorption and the split plan, in one launch
 hipError_t launch_prep(const uint16_t* q, const uint16_t* kv_b, int heads, int rows,
-                       uint16_t* q_abs, const int32_t* seq_lens, int batch, int max_pages,
+                       float q_scale, uint16_t* q_abs, const int32_t* seq_lens, int batch,
+                       int max_pages,
                        int slots, int max_items, int splits_hint, float item_cost_pages,
                        PlanView plan, hipStream_t stream);
 
@@ -81,8 +81,8 @@ DecodeConfig decode_config(int rows_per_seq);
 
 hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const uint16_t* cache,
                          const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
-                         int heads, int q_len, float scale_log2, PlanView plan, int max_items,
-                         float* o_part, float* lse_part, const uint16_t* zero_row,
+                         int heads, int q_len, PlanView plan, int max_items,
+                         float* o_part, float* lse_part,
                          int* restart_flags, hipStream_t stream);
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, PlanView plan,

@@ -75,7 +75,6 @@ __device__ void plan_block(const PlanArgs& pa, MLA_LDS char* smem) {
     return b < kPlanShared ? sh_pages[b] : clamp_pages(seq_lens[b], max_pages);
   };
 
-  for (int k = t; k < kEntryBytes / 4; k += kPlanThreads) plan.zero_row[k] = 0;
   int local = 0;
   for (int b = t; b < batch; b += kPlanThreads) {
     const int p = clamp_pages(seq_lens[b], max_pages);

@@ -1,4 +1,6 @@
-// Query absorption: q_abs[row, h] = [ q_nope[row, h] W_UK[h]  |  q_pe[row, h] ].
+// Query absorption: q_abs[row, h] = c * [ q_nope[row, h] W_UK[h]  |  q_pe[row, h] ]
+// with c = softmax_scale * log2(e), so that the decode kernel's scores come
+// out of the matrix cores already in log2 units.
 //
 // "深度解读DeepSeek：源码解读 DeepSeek-V3", section MLA, "(b) 优化实现", first
 // einsum (bshd,hdc->bshc): q_nope times the first 128 rows of head h's kv_b
@@ -28,8 +30,8 @@ static_assert(kPlanThreads == 256, "the plan runs on one 256-thread workgroup");
 // Block 4H: the split plan (independent work, hidden under the absorption).
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ kv_b, int heads,
-                                                   int rows, uint16_t* __restrict__ q_abs,
-                                                   PlanArgs pa) {
+                                                   int rows, float q_scale,
+                                                   uint16_t* __restrict__ q_abs, PlanArgs pa) {
   __shared__ __attribute__((aligned(16))) char smem[kPrepSmem];
   if (blockIdx.x == (unsigned)heads * (kLatent / kQaCols)) {
     plan_block(pa, (MLA_LDS char*)smem);
@@ -52,14 +54,17 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
     *reinterpret_cast<MLA_LDS u16x8*>(w_lds + d * kQaStride + c16 * 16) =
         *reinterpret_cast<const u16x8*>(wuk + (int64_t)d * kLatent + c16 * 8);
   }
-  // q_pe passes through unchanged (done once per head, by column chunk 0)
+  // q_pe times the scale (done once per head, by column chunk 0)
   if (nc == 0) {
     for (int p = tid; p < rows * 8; p += 256) {
       const int r = p >> 3;
       const int j = p & 7;
       const int64_t row = (int64_t)r * heads + h;
-      *reinterpret_cast<u16x8*>(q_abs + row * kEntry + kLatent + j * 8) =
-          *reinterpret_cast<const u16x8*>(q + row * kQk + kNope + j * 8);
+      const u16x8 v = *reinterpret_cast<const u16x8*>(q + row * kQk + kNope + j * 8);
+      u16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16(bf16_to_f32(v[e]) * q_scale);
+      *reinterpret_cast<u16x8*>(q_abs + row * kEntry + kLatent + j * 8) = o;
     }
   }
   __syncthreads();
@@ -105,7 +110,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
       if (rr < rows) {
         u16x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(acc[i]);
+        for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(acc[i] * q_scale);
         *reinterpret_cast<u16x4*>(q_abs + row * kEntry + nc * kQaCols + wave * 32 + mt * 16 +
                                   4 * g) = v;
       }
@@ -114,12 +119,13 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 }
 
 hipError_t launch_prep(const uint16_t* q, const uint16_t* kv_b, int heads, int rows,
-                       uint16_t* q_abs, const int32_t* seq_lens, int batch, int max_pages,
+                       float q_scale, uint16_t* q_abs, const int32_t* seq_lens, int batch,
+                       int max_pages,
                        int slots, int max_items, int splits_hint, float item_cost_pages,
                        PlanView plan, hipStream_t stream) {
   PlanArgs pa{seq_lens, batch, max_pages, slots, max_items, splits_hint, item_cost_pages, plan};
   hipLaunchKernelGGL(prep_kernel, dim3(heads * (kLatent / kQaCols) + 1), dim3(256), 0, stream, q,
-                     kv_b, heads, rows, q_abs, pa);
+                     kv_b, heads, rows, q_scale, q_abs, pa);
   return hipGetLastError();
 }
 
