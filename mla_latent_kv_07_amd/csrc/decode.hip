@@ -13,25 +13,36 @@
 //     x one group of query rows (row = query index * H + head).  Each
 //     wavefront owns NH groups of 16 rows; all wavefronts share every cache
 //     chunk, which is read from HBM once per row group.
-//   * Chunks of 32 positions (36 KB) are copied HBM -> LDS by direct-to-LDS
-//     loads into an NBUF-deep ring; one barrier per chunk.  Every copy
-//     instruction moves 1 KB of contiguous cache bytes (whole 128-byte
-//     lines): per-lane scattered copies run at about half the HBM rate.
+//   * Chunks of 32 positions (36 KB, half a page) are copied HBM -> LDS by
+//     buffer loads straight to LDS into an NBUF-deep ring; one barrier per
+//     chunk.  Every copy instruction moves 1 KB of contiguous cache bytes
+//     (whole 128-byte lines): per-lane scattered copies run at about half the
+//     HBM rate.  The chunk loop issues no other vector-memory instruction
+//     (block table through scalar loads, no spills): vmcnt counts in order,
+//     so any such load would make its consumer wait for every chunk in
+//     flight.
 //     In LDS, position r keeps its 1152-byte row; its 16-byte pieces are
-//     permuted inside each aligned group of 8 by swz(r) =
-//     2*(r & 3) + ((r >> 2) & 1), which makes both read patterns below free
-//     of bank conflicts on the 128-byte-per-clock LDS (8 consecutive rows x
-//     one piece per clock for the 16-byte score reads; 4 rows x two adjacent
-//     pieces per clock for the 8-byte transposing reads).
+//     permuted inside each aligned group of 8 by the 3-bit mask
+//     swz(r) = 2*((r >> 1) & 3) XOR 7*((r >> 3) & 1).  The gfx950 LDS has
+//     64 four-byte banks (256 bytes per clock).  A 16-byte read serves 16
+//     lanes per clock: the lanes that agree in lane bit 5 and in the parity
+//     of lane bits 2..4.  An 8-byte transposing read serves 32 lanes per
+//     clock.  Rows start alternately at bank 0 and bank 32
+//     (1152 = 4.5 * 256).  Under that map both read patterns below are free
+//     of bank conflicts (checked by enumerating every lane's banks): 16 rows
+//     x one 16-byte piece per score read, 8 rows x two adjacent 8-byte
+//     halves per transposing read.
 //   * Scores are computed transposed, S^T = K Q^T, with the bf16 MFMA
 //     16x16x32: the cache tile is the A operand, the query the B operand
 //     held in registers for the whole launch.  Each lane ends up with the
 //     scores of ONE head for 4 positions per 16-position tile, exactly the
 //     B-operand layout of O^T = V^T P^T, so P never goes through LDS.  V^T
 //     comes from LDS through the transposing read (ds_read_b64_tr_b16).
-//   * The softmax of chunk j is scheduled under the score MFMAs of chunk j+1
-//     (software pipelining inside the wavefront), so the vector ALU work
-//     hides behind the matrix cores.
+//   * Per chunk a wavefront runs scores, softmax and P.V in that order
+//     (scheduling barriers keep the phases apart, so no phase's registers
+//     stay live across another).  The absorbed query (18 k-steps, 144 VGPRs)
+//     and the 32 x 512 fp32 output tile (256 accumulation registers) stay in
+//     registers for the whole item: one wavefront per SIMD.
 //   * Online softmax in log2 units (the query arrives pre-multiplied by
 //     softmax_scale * log2 e) with a fixed reference per row: the max of the
 //     item's first chunk, the only chunk that needs a cross-lane reduction.
@@ -78,7 +89,7 @@ struct Dma {
 };
 
 // Piece permutation inside each aligned group of 8 pieces of row r.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 3) << 1) ^ (((r >> 3) & 1) * 7); }
 
 // Per-lane source offsets of the wavefront's copies of one chunk.  Copy k
 // fills LDS pieces 64k .. 64k+63 (lane L -> piece Q = 64k + L, i.e. row Q / 72,
@@ -120,7 +131,7 @@ __device__ __forceinline__ void load_chunk(MLA_LDS char* buf, const char* src,
 // before the MFMAs of k-step ks.
 // Query k-steps kept in registers; k-steps kQReg..17 (the last 128 latent
 // features and the 64 rope features) are read from LDS.
-constexpr int kQReg = 12;
+constexpr int kQReg = 18;
 constexpr int kQTailBytes = (18 - kQReg) * 64;  // per query row
 
 template <int NH>
@@ -272,7 +283,7 @@ __device__ __forceinline__ void max_chunk(const f32x4 (&sacc)[NH][2], float (&m)
 template <int NW, int NH, int NBUF>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
                                                          const int32_t* __restrict__ block_table) {
-  static_assert(NBUF >= 2 && NBUF <= 3 &&
+  static_assert(NBUF >= 2 && NBUF <= 4 &&
                     NBUF * kBufBytes + NW * NH * 16 * kQTailBytes <= 160 * 1024,
                 "LDS ring of NBUF chunks plus the query tail");
   // ring of NBUF chunks, then the query k-steps kQReg..17 of the workgroup's rows
@@ -401,7 +412,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   // issued: at most the copies of the chunks issued after it may be pending
   auto wait_for = [&](int j, int issued) {
     const int later = issued - 1 - j;
-    if (later >= 2)
+    if (later >= 3)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kPer));
+    else if (later == 2)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
     else if (later == 1)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
@@ -533,7 +546,7 @@ DecodeConfig decode_config(int rows_per_seq) {
   if (groups % 8 == 0) {
     c.waves = 4;
     c.heads_per_wave = 2;
-    c.nbuf = 3;
+    c.nbuf = 4;
   } else if (groups % 4 == 0) {
     c.waves = 2;
     c.heads_per_wave = 2;
@@ -581,7 +594,7 @@ hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const u
   args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
-  if (cfg.waves == 4) return launch_t<4, 2, 3>(grid, args, block_table, stream);
+  if (cfg.waves == 4) return launch_t<4, 2, 4>(grid, args, block_table, stream);
   if (cfg.waves == 2) return launch_t<2, 2, 3>(grid, args, block_table, stream);
   if (cfg.heads_per_wave == 2) return launch_t<1, 2, 3>(grid, args, block_table, stream);
   return launch_t<1, 1, 3>(grid, args, block_table, stream);
