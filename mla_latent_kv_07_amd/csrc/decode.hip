@@ -114,32 +114,32 @@ constexpr int kRsrcWord3 = 0x00020000;
 
 // Copy one chunk (36 KB at `src`, a wavefront-uniform address) into the LDS
 // ring slot `buf` (wavefront-uniform): buffer loads straight to LDS, with the
-// chunk as the buffer (scalar descriptor) and a 32-bit per-lane offset.
+// chunk as the buffer (scalar descriptor) and a 32-bit per-lane offset.  With
+// `bytes` = 0 every lane is out of range: no memory is read (the slot gets
+// zeros), but the instruction count stays the same.
 template <int NW, int KP>
-__device__ __forceinline__ void load_chunk(MLA_LDS char* buf, const char* src,
+__device__ __forceinline__ void load_chunk(MLA_LDS char* buf, const char* src, int bytes,
                                            const uint32_t* off, int wave) {
   const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, kBufBytes, kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, bytes, kRsrcWord3);
 #pragma unroll
   for (int i = 0; i < KP; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, buf + (i * NW + wave) * 1024, 16, off[i], 0, 0,
                                              0);
 }
 
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008;
+constexpr int kSgDsRead = 0x100;
+
 // Scores of one chunk for the wavefront's NH row groups: sacc[h][t] holds
 // S^T for positions 16t..16t+15.  The LDS reads of k-step ks + KPD are issued
 // before the MFMAs of k-step ks.
-// Query k-steps kept in registers; k-steps kQReg..17 (the last 128 latent
-// features and the 64 rope features) are read from LDS.
-constexpr int kQReg = 18;
-constexpr int kQTailBytes = (18 - kQReg) * 64;  // per query row
-
 template <int NH>
 __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_even,
-                                            int sbase_odd, const bf16x8 (&qreg)[NH][kQReg],
-                                            const MLA_LDS char* const (&qt)[2],
+                                            int sbase_odd, const bf16x8 (&qreg)[NH][18],
                                             f32x4 (&sacc)[NH][2]) {
-  constexpr int KPD = 2;
+  constexpr int KPD = 3;
 #pragma unroll
   for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -151,11 +151,6 @@ __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_e
   auto kload = [&](int ks, int t) -> bf16x8 {
     return *reinterpret_cast<const MLA_LDS bf16x8*>((ks & 1 ? bo : be) + 64 * ks +
                                                     16 * kEntryBytes * t);
-  };
-  // query k-step kQReg + e of row group h: qt[e & 1] + 64e + h*16*kQTailBytes
-  auto qload = [&](int h, int e) -> bf16x8 {
-    return *reinterpret_cast<const MLA_LDS bf16x8*>(qt[e & 1] + 64 * e +
-                                                    h * 16 * kQTailBytes);
   };
   bf16x8 kb[KPD + 1][2];
 #pragma unroll
@@ -170,13 +165,22 @@ __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_e
     }
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-      const bf16x8 qb = ks < kQReg ? qreg[h][ks < kQReg ? ks : 0] : qload(h, ks - kQReg);
+      const bf16x8 qb = qreg[h][ks];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         sacc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks % (KPD + 1)][t], qb,
                                                              sacc[h][t], 0, 0, 0);
     }
   }
+  // schedule: KPD k-steps of reads ahead, then per k-step its MFMAs and the
+  // reads of k-step ks + KPD
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * KPD, 0);
+#pragma unroll
+  for (int ks = 0; ks < 18 - KPD; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 2 * NH, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgMfma, 2 * NH * KPD, 0);
 }
 
 // Softmax of one chunk's scores (already scaled to log2 units: the query was
@@ -227,10 +231,6 @@ __device__ __forceinline__ bool softmax_chunk(f32x4 (&sacc)[NH][2], bf16x8 (&pk)
   return restart;
 }
 
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgMfma = 0x008;
-constexpr int kSgValu = 0x002;
-constexpr int kSgDsRead = 0x100;
 
 template <int NH>
 __device__ __forceinline__ void pv_chunk(const MLA_LDS char* buf, const int (&vbase)[4],
@@ -280,24 +280,48 @@ __device__ __forceinline__ void max_chunk(const f32x4 (&sacc)[NH][2], float (&m)
   }
 }
 
-template <int NW, int NH, int NBUF>
+template <int S>
+using Slot = std::integral_constant<int, S>;
+
+// Encoding of "s_waitcnt lgkmcnt(0)" (vmcnt and expcnt left unconstrained).
+constexpr int kLgkm0 = 0xc07f;
+
+// Workgroup barrier of the chunk ring: this wavefront's LDS accesses have
+// completed, then s_barrier.  Written as asm with a memory clobber, so the
+// compiler moves no memory access across it; unlike __syncthreads it adds no
+// wait on the copies in flight (their completion is waited for explicitly).
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int NW, int NH>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
                                                          const int32_t* __restrict__ block_table) {
-  static_assert(NBUF >= 2 && NBUF <= 4 &&
-                    NBUF * kBufBytes + NW * NH * 16 * kQTailBytes <= 160 * 1024,
-                "LDS ring of NBUF chunks plus the query tail");
-  // ring of NBUF chunks, then the query k-steps kQReg..17 of the workgroup's rows
-  __shared__ __attribute__((aligned(1024))) char lds_raw[NBUF * kBufBytes +
-                                                         NW * NH * 16 * kQTailBytes];
-  MLA_LDS char* lds = (MLA_LDS char*)lds_raw;
+  // The ring: four chunk slots, each its own array.  Chunk j lives in slot
+  // j % 4, and the chunk loop is unrolled by four so that every access names
+  // its slot at compile time: the compiler then knows that the copies in
+  // flight (into the other slots) never alias the slot being read and adds
+  // no wait of its own on them.
+  __shared__ __attribute__((aligned(1024))) char ring0[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) char ring1[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) char ring2[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) char ring3[kBufBytes];
+  auto ring = [&](auto slot_c) -> MLA_LDS char* {
+    constexpr int S = decltype(slot_c)::value;
+    if constexpr (S == 0) return (MLA_LDS char*)ring0;
+    else if constexpr (S == 1) return (MLA_LDS char*)ring1;
+    else if constexpr (S == 2) return (MLA_LDS char*)ring2;
+    else return (MLA_LDS char*)ring3;
+  };
 
   // blockIdx -> (item, row group); the row groups of one item land on the
   // same XCD (block ids congruent mod 8) so their chunk reads share that L2.
   const int gid = blockIdx.x;
   const int xcd = gid & 7;
-  const int slot = gid >> 3;
-  const int item = (slot / a.row_groups) * 8 + xcd;
-  const int rg = slot - (slot / a.row_groups) * a.row_groups;
+  const int gslot = gid >> 3;
+  const int item = (gslot / a.row_groups) * 8 + xcd;
+  const int rg = gslot - (gslot / a.row_groups) * a.row_groups;
   if (item >= a.plan.header[0]) return;
 
   const int b = a.plan.item_b[item];
@@ -334,31 +358,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
       vbase[f4] = row * kEntryBytes + 16 * ((2 * f4) ^ y) + 8 * (qq & 1);
   }
 
-  // query rows: k-steps 0..kQReg-1 stay in registers (lane holds features
-  // 32ks + 8gq .. +8 of row n); k-steps kQReg..17 go to LDS, row r of the
-  // wavefront at qtail + r*kQTailBytes, piece p (16 B) at slot p ^ (r & 7)
-  bf16x8 qreg[NH][kQReg];
-  MLA_LDS char* qtail = lds + NBUF * kBufBytes + wave * NH * 16 * kQTailBytes;
+  // the absorbed query rows, in registers for the whole item: lane holds
+  // features 32ks + 8gq .. +8 of row n (the B operand of k-step ks)
+  bf16x8 qreg[NH][18];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(
         a.q_abs + ((int64_t)b * a.rows_per_seq + row0 + 16 * h + n) * kEntry + 8 * gq);
 #pragma unroll
-    for (int ks = 0; ks < kQReg; ++ks) qreg[h][ks] = qp[4 * ks];
-#pragma unroll
-    for (int e = 0; e < 18 - kQReg; ++e)
-      *reinterpret_cast<MLA_LDS bf16x8*>(qtail + (16 * h + n) * kQTailBytes +
-                                         16 * ((4 * e + gq) ^ (n & 7))) = qp[4 * (kQReg + e)];
-  }
-  // per-lane read bases: slot (4e + gq) ^ (n & 7) = 4(e ^ hb) + c with
-  // hb = (n >> 2) & 1, c = (gq ^ n) & 3, i.e. byte 64e + 16c + (e odd ? -64hb : 64hb)
-  const MLA_LDS char* qt[2];
-  {
-    const int hb = (n >> 2) & 1;
-    const int c = (gq ^ n) & 3;
-    const MLA_LDS char* rowq = qtail + n * kQTailBytes + 16 * c;
-    qt[0] = rowq + 64 * hb;
-    qt[1] = rowq - 64 * hb;
+    for (int ks = 0; ks < 18; ++ks) qreg[h][ks] = qp[4 * ks];
   }
   f32x4 oacc[NH][32];
   float m_ref[NH], l_run[NH];
@@ -381,122 +389,116 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   // `tail_rows` on hold other positions' slots (NaN sentinels, stale data)
   // and are zeroed in LDS once the chunk has landed, before any wave reads it
   const int tail_rows = tok_end - tok_begin - (nchunks - 1) * kChunk;
+  // chunks from jm on reach past the causal limit of some row (or the
+  // sequence end) and take the masked softmax
+  const int jm = (tmax_min - tok_begin + 1) / kChunk;
   const int32_t* bt = block_table + (int64_t)b * a.bt_stride;  // scalar loads (restrict)
   const char* cache = reinterpret_cast<const char*>(a.cache);
-  uint32_t doff[Dma<NW>::kPerWave];
+  constexpr int kPer = Dma<NW>::kPerWave;
+  uint32_t doff[kPer];
   dma_offsets<NW>(wave, lane, doff);
-  auto issue = [&](int j) {
-    const int t = tok_begin + j * kChunk;
+  // Every chunk step issues exactly one copy (an empty one past the item's
+  // end), so "chunk j has landed" is always "at most two copies pending":
+  // one wait count for every chunk, which the compiler can follow and so adds
+  // no conservative full drain of its own.
+  auto issue = [&](auto slot_c, int j) {
+    const bool real = j < nchunks;
+    const int t = tok_begin + (real ? j : 0) * kChunk;
     const int64_t blk = bt[t / kPage];
     const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kEntryBytes;
-    load_chunk<NW, Dma<NW>::kPerWave>(lds + (j % NBUF) * kBufBytes, src, doff, wave);
+    load_chunk<NW, kPer>(ring(slot_c), src, real ? kBufBytes : 0, doff, wave);
   };
-  auto buf_of = [&](int j) -> const MLA_LDS char* { return lds + (j % NBUF) * kBufBytes; };
   // after chunk j has landed in every wavefront's view (barrier passed)
-  auto fix_tail = [&](int j) {
+  auto fix_tail = [&](auto slot_c, int j) {
     if (j == nchunks - 1 && tail_rows < kChunk) {
-      MLA_LDS char* bp = lds + (j % NBUF) * kBufBytes;
+      MLA_LDS char* bp = ring(slot_c);
       for (int pc = tail_rows * kChunk16 + (int)threadIdx.x; pc < kChunk * kChunk16; pc += NW * 64)
         *reinterpret_cast<MLA_LDS u16x8*>(bp + 16 * pc) = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      __syncthreads();
+      ring_barrier();
     }
   };
-  constexpr int kPer = Dma<NW>::kPerWave;
   // visibility limit of chunk j for this lane, relative to its slot 16t + i
   auto chunk_limits = [&](int j, int (&lim)[NH]) {
     const int t0 = tok_begin + j * kChunk;
 #pragma unroll
     for (int h = 0; h < NH; ++h) lim[h] = tmax[h] - t0 - 4 * gq;
   };
-  // wait until chunk j has landed, given that chunks up to `issued - 1` were
-  // issued: at most the copies of the chunks issued after it may be pending
-  auto wait_for = [&](int j, int issued) {
-    const int later = issued - 1 - j;
-    if (later >= 3)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kPer));
-    else if (later == 2)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
-    else if (later == 1)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  };
+
   // ---- main pass: reference = the first chunk's max per row ----------------
-  // Ring: while chunk j is computed, chunks j+1 .. j+NBUF-1 are in flight;
-  // chunk j+NBUF-1 is issued into chunk j-1's slot.
+  // While chunk j is computed, chunks j+1 and j+2 are in flight and chunk j+3
+  // goes into chunk j-1's slot once every wavefront is past chunk j-1.
+  // After chunk 0 the chunks run in groups of four (slots 1, 2, 3, 0); a
+  // group may reach past the item's end, and such steps still wait, pass the
+  // barrier and issue their (empty) copy but skip the compute.  No vector
+  // memory instruction sits in a conditional, so on every path the compiler
+  // sees the same copies pending.
   // (a wavefront that needs a restart keeps going with a useless result;
-  // the flag is read once, after the pass)
-  bool restart = false;
-  {
-    int issued = 0;
-    for (; issued < NBUF - 1 && issued < nchunks; ++issued) issue(issued);
-    f32x4 sacc[NH][2];
-    bf16x8 pk[NH];
-    // chunk j: scores, softmax, P.V
-    auto step = [&](auto first_c, auto mask_c, int j) -> bool {
-      constexpr bool kFirst = decltype(first_c)::value;
-      constexpr bool kMask = decltype(mask_c)::value;
-      int lim[NH];
-      chunk_limits(j, lim);
-      // the phases stay in order: moving the next phase's LDS reads up would
-      // keep their registers live across this one
-      score_chunk<NH>(buf_of(j), sbase_even, sbase_odd, qreg, qt, sacc);
-      __builtin_amdgcn_sched_barrier(0);
-      const bool need = softmax_chunk<NH, kFirst, kMask>(sacc, pk, m_ref, l_run, lim);
-      __builtin_amdgcn_sched_barrier(0);
-      pv_chunk<NH>(buf_of(j), vbase, pk, oacc);
-      __builtin_amdgcn_sched_barrier(0);
-      return need;
-    };
-    using T = std::true_type;
-    using F = std::false_type;
-    // wait for chunk j; after the barrier chunk j-1's slot is free for the
-    // copy of chunk j + NBUF - 1
-    auto advance = [&](int j) {
-      wait_for(j, issued);
-      __syncthreads();
-      if (issued < nchunks) issue(issued++);
-      fix_tail(j);
-    };
-    auto flag_restart = [&](bool need) {
-      if (__builtin_amdgcn_ballot_w64(need) != 0 && lane == 0)
-        __atomic_store_n(flag, 1, __ATOMIC_RELAXED);
-    };
-    // chunk 0 sets the references (masked variant: it may be the last one);
-    // chunks from jm on reach past the causal limit of some row (or the
-    // sequence end) and take the masked variant; each range is its own loop
-    const int jm = max(1, min(nchunks, (tmax_min - tok_begin + 1) / kChunk));
-    if (nchunks > 0) {
-      advance(0);
-      flag_restart(step(T{}, T{}, 0));
-    }
-    for (int j = 1; j < jm; ++j) {
-      advance(j);
-      flag_restart(step(F{}, F{}, j));
-    }
-    for (int j = jm; j < nchunks; ++j) {
-      advance(j);
-      flag_restart(step(F{}, T{}, j));
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-    restart = restart || __atomic_load_n(flag, __ATOMIC_RELAXED);
+  // the verdict is taken once, after the pass)
+  using T = std::true_type;
+  using F = std::false_type;
+  f32x4 sacc[NH][2];
+  bf16x8 pk[NH];
+  bool need_restart = false;
+  auto chunk = [&](auto slot_c, auto first_c, int j) {
+    constexpr int S = decltype(slot_c)::value;
+    constexpr bool kFirst = decltype(first_c)::value;
+    // chunk j has landed once at most the copies of chunks j+1, j+2 are pending
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
+    ring_barrier();
+    issue(Slot<(S + 3) & 3>{}, j + 3);
+    if (j >= nchunks) return;
+    fix_tail(slot_c, j);
+    int lim[NH];
+    chunk_limits(j, lim);
+    // the phases stay in order: moving the next phase's LDS reads up would
+    // keep their registers live across this one
+    score_chunk<NH>(ring(slot_c), sbase_even, sbase_odd, qreg, sacc);
+    __builtin_amdgcn_sched_barrier(0);
+    bool need;
+    if (j >= jm)
+      need = softmax_chunk<NH, kFirst, true>(sacc, pk, m_ref, l_run, lim);
+    else
+      need = softmax_chunk<NH, kFirst, false>(sacc, pk, m_ref, l_run, lim);
+    __builtin_amdgcn_sched_barrier(0);
+    pv_chunk<NH>(ring(slot_c), vbase, pk, oacc);
+    __builtin_amdgcn_sched_barrier(0);
+    need_restart |= need;
+  };
+  // (an item always has at least one chunk)
+  issue(Slot<0>{}, 0);
+  issue(Slot<1>{}, 1);
+  issue(Slot<2>{}, 2);
+  chunk(Slot<0>{}, T{}, 0);
+  for (int j = 1; j < nchunks; j += 4) {
+    chunk(Slot<1>{}, F{}, j);
+    chunk(Slot<2>{}, F{}, j + 1);
+    chunk(Slot<3>{}, F{}, j + 2);
+    chunk(Slot<0>{}, F{}, j + 3);
   }
+  // every wavefront's verdict, then one decision for the workgroup
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  if (__builtin_amdgcn_ballot_w64(need_restart) != 0 && lane == 0)
+    __atomic_store_n(flag, 1, __ATOMIC_RELAXED);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  const bool restart = __atomic_load_n(flag, __ATOMIC_RELAXED) != 0;
 
   // ---- restart (rare): exact row max, then a pass with it as the reference --
+  // one chunk at a time through slot 0
   if (restart) {
     float m_exact[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) m_exact[h] = -INFINITY;
     for (int j = 0; j < nchunks; ++j) {
-      issue(j);
+      issue(Slot<0>{}, j);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
-      fix_tail(j);
-      f32x4 sacc[NH][2];
+      fix_tail(Slot<0>{}, j);
       int lim[NH];
       chunk_limits(j, lim);
-      score_chunk<NH>(buf_of(j), sbase_even, sbase_odd, qreg, qt, sacc);
+      f32x4 sacc[NH][2];
+      score_chunk<NH>(ring(Slot<0>{}), sbase_even, sbase_odd, qreg, sacc);
       max_chunk<NH>(sacc, m_exact, lim);
       __syncthreads();
     }
@@ -508,17 +510,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
       for (int f = 0; f < 32; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     for (int j = 0; j < nchunks; ++j) {
-      issue(j);
+      issue(Slot<0>{}, j);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
-      fix_tail(j);
-      f32x4 sacc[NH][2];
-      bf16x8 pk[NH];
+      fix_tail(Slot<0>{}, j);
       int lim[NH];
       chunk_limits(j, lim);
-      score_chunk<NH>(buf_of(j), sbase_even, sbase_odd, qreg, qt, sacc);
+      f32x4 sacc[NH][2];
+      bf16x8 pk[NH];
+      score_chunk<NH>(ring(Slot<0>{}), sbase_even, sbase_odd, qreg, sacc);
       softmax_chunk<NH, false, true>(sacc, pk, m_ref, l_run, lim);
-      pv_chunk<NH>(buf_of(j), vbase, pk, oacc);
+      pv_chunk<NH>(ring(Slot<0>{}), vbase, pk, oacc);
       __syncthreads();
     }
   }
@@ -543,33 +545,29 @@ DecodeConfig decode_config(int rows_per_seq) {
   const int groups = rows_per_seq / 16;
   DecodeConfig c;
   c.chunk = kChunk;
+  c.nbuf = 4;
   if (groups % 8 == 0) {
     c.waves = 4;
     c.heads_per_wave = 2;
-    c.nbuf = 4;
   } else if (groups % 4 == 0) {
     c.waves = 2;
     c.heads_per_wave = 2;
-    c.nbuf = 3;
   } else if (groups % 2 == 0) {
     c.waves = 1;
     c.heads_per_wave = 2;
-    c.nbuf = 3;
   } else {
     c.waves = 1;
     c.heads_per_wave = 1;
-    c.nbuf = 3;
   }
-  c.lds_bytes = c.nbuf * kBufBytes + c.waves * c.heads_per_wave * 16 * kQTailBytes;
-  // each wavefront uses more than half a SIMD's registers: one per SIMD
-  c.wgs_per_cu = min((160 * 1024) / c.lds_bytes, 4 / c.waves);
+  c.lds_bytes = c.nbuf * kBufBytes;
+  c.wgs_per_cu = 1;  // the ring fills the LDS
   return c;
 }
 
-template <int NW, int NH, int NBUF>
+template <int NW, int NH>
 static hipError_t launch_t(int grid, const DecodeArgs& args, const int32_t* block_table,
                           hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<NW, NH, NBUF>), dim3(grid), dim3(NW * 64), 0, stream, args,
+  hipLaunchKernelGGL((decode_kernel<NW, NH>), dim3(grid), dim3(NW * 64), 0, stream, args,
                      block_table);
   return hipGetLastError();
 }
@@ -594,10 +592,10 @@ hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const u
   args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
-  if (cfg.waves == 4) return launch_t<4, 2, 4>(grid, args, block_table, stream);
-  if (cfg.waves == 2) return launch_t<2, 2, 3>(grid, args, block_table, stream);
-  if (cfg.heads_per_wave == 2) return launch_t<1, 2, 3>(grid, args, block_table, stream);
-  return launch_t<1, 1, 3>(grid, args, block_table, stream);
+  if (cfg.waves == 4) return launch_t<4, 2>(grid, args, block_table, stream);
+  if (cfg.waves == 2) return launch_t<2, 2>(grid, args, block_table, stream);
+  if (cfg.heads_per_wave == 2) return launch_t<1, 2>(grid, args, block_table, stream);
+  return launch_t<1, 1>(grid, args, block_table, stream);
 }
 
 }  // namespace mla
