@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the run, one plain device-to-device copy of this many MiB "
+                         "(reference dispatch for scaling HBM byte counters)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "decode_kernel_traffic.json"),
                     help="HBM traffic of the decode kernel measured with rocprofv3 counters")
     return ap.parse_args()
@@ -161,6 +164,12 @@ def main():
                                         * (wl.ENTRY + wl.LATENT) / (dec_ms * 1e-3) / 1e12
                                         / MFMA_BF16_PEAK_TFS, 4)},
     }
+    if args.calib_copy_mib > 0:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
     print(json.dumps(result), flush=True)
