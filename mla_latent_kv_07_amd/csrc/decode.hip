@@ -83,9 +83,12 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 
 template <int NW>
 struct Dma {
-  static constexpr int kInsts = kBufBytes / 1024;   // 36 wavefront-wide copies per chunk
-  static constexpr int kPerWave = kInsts / NW;
-  static_assert(kInsts % NW == 0, "copies split evenly over the wavefronts");
+  static constexpr int kInsts = kBufBytes / 1024;  // 36 wavefront-wide copies per chunk
+  // every wavefront issues the same number of copies; when 36 does not split
+  // evenly the last ones are out of range (no memory access) and land in the
+  // slot's padding
+  static constexpr int kPerWave = (kInsts + NW - 1) / NW;
+  static constexpr int kSlotBytes = kPerWave * NW * 1024;
 };
 
 // Piece permutation inside each aligned group of 8 pieces of row r.
@@ -105,7 +108,8 @@ __device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&off)[
     const int q = 64 * k + lane;
     const int row = q / kChunk16;
     const int col = q - row * kChunk16;
-    off[i] = (uint32_t)(row * kEntryBytes + 16 * (col ^ swz(row)));
+    off[i] = k < Dma<NW>::kInsts ? (uint32_t)(row * kEntryBytes + 16 * (col ^ swz(row)))
+                                 : 0x80000000u;  // beyond any buffer range
   }
 }
 
@@ -303,10 +307,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   // its slot at compile time: the compiler then knows that the copies in
   // flight (into the other slots) never alias the slot being read and adds
   // no wait of its own on them.
-  __shared__ __attribute__((aligned(1024))) char ring0[kBufBytes];
-  __shared__ __attribute__((aligned(1024))) char ring1[kBufBytes];
-  __shared__ __attribute__((aligned(1024))) char ring2[kBufBytes];
-  __shared__ __attribute__((aligned(1024))) char ring3[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) char ring0[Dma<NW>::kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring1[Dma<NW>::kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring2[Dma<NW>::kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring3[Dma<NW>::kSlotBytes];
   auto ring = [&](auto slot_c) -> MLA_LDS char* {
     constexpr int S = decltype(slot_c)::value;
     if constexpr (S == 0) return (MLA_LDS char*)ring0;
@@ -425,56 +429,75 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   };
 
   // ---- main pass: reference = the first chunk's max per row ----------------
-  // While chunk j is computed, chunks j+1 and j+2 are in flight and chunk j+3
-  // goes into chunk j-1's slot once every wavefront is past chunk j-1.
-  // After chunk 0 the chunks run in groups of four (slots 1, 2, 3, 0); a
-  // group may reach past the item's end, and such steps still wait, pass the
-  // barrier and issue their (empty) copy but skip the compute.  No vector
-  // memory instruction sits in a conditional, so on every path the compiler
-  // sees the same copies pending.
+  // Interval j: wait for chunk j, barrier, copy chunk j+2 into the slot of
+  // chunk j-2.  While interval j computes, chunks j+1 and j+2 are in flight.
+  // With two wavefronts per SIMD (NW == 8) the wavefronts 4..7 lag: in
+  // interval j they run the P.V of chunk j-1 first, then the scores and
+  // softmax of chunk j, while their SIMD partners 0..3 run scores, softmax and
+  // P.V of chunk j.  One wavefront's matrix work then overlaps its partner's
+  // softmax and LDS waits instead of both running the same phase at once.
+  // After interval 0 the intervals run in groups of four (slots 1, 2, 3, 0),
+  // up to and including interval nchunks (the lagging P.V of the last chunk);
+  // intervals past the item's end still wait, pass the barrier and issue
+  // their (empty) copy.  No vector memory instruction sits in a conditional,
+  // so on every path the compiler sees the same copies pending.
   // (a wavefront that needs a restart keeps going with a useless result;
   // the verdict is taken once, after the pass)
-  using T = std::true_type;
-  using F = std::false_type;
-  f32x4 sacc[NH][2];
-  bf16x8 pk[NH];
   bool need_restart = false;
-  auto chunk = [&](auto slot_c, auto first_c, int j) {
-    constexpr int S = decltype(slot_c)::value;
-    constexpr bool kFirst = decltype(first_c)::value;
-    // chunk j has landed once at most the copies of chunks j+1, j+2 are pending
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
-    ring_barrier();
-    issue(Slot<(S + 3) & 3>{}, j + 3);
-    if (j >= nchunks) return;
-    fix_tail(slot_c, j);
-    int lim[NH];
-    chunk_limits(j, lim);
-    // the phases stay in order: moving the next phase's LDS reads up would
-    // keep their registers live across this one
-    score_chunk<NH>(ring(slot_c), sbase_even, sbase_odd, qreg, sacc);
-    __builtin_amdgcn_sched_barrier(0);
-    bool need;
-    if (j >= jm)
-      need = softmax_chunk<NH, kFirst, true>(sacc, pk, m_ref, l_run, lim);
-    else
-      need = softmax_chunk<NH, kFirst, false>(sacc, pk, m_ref, l_run, lim);
-    __builtin_amdgcn_sched_barrier(0);
-    pv_chunk<NH>(ring(slot_c), vbase, pk, oacc);
-    __builtin_amdgcn_sched_barrier(0);
-    need_restart |= need;
+  auto pass = [&](auto lag_c) {
+    constexpr bool kLag = decltype(lag_c)::value;
+    f32x4 sacc[NH][2];
+    bf16x8 pk[NH];
+    auto interval = [&](auto slot_c, auto first_c, int j) {
+      constexpr int S = decltype(slot_c)::value;
+      constexpr bool kFirst = decltype(first_c)::value;
+      // chunk j has landed once at most the copy of chunk j+1 is pending
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
+      ring_barrier();
+      issue(Slot<(S + 2) & 3>{}, j + 2);
+      if constexpr (kLag && !kFirst) {
+        if (j - 1 < nchunks) {
+          pv_chunk<NH>(ring(Slot<(S + 3) & 3>{}), vbase, pk, oacc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (j >= nchunks) return;
+      fix_tail(slot_c, j);
+      int lim[NH];
+      chunk_limits(j, lim);
+      // the phases stay in order: moving the next phase's LDS reads up would
+      // keep their registers live across this one
+      score_chunk<NH>(ring(slot_c), sbase_even, sbase_odd, qreg, sacc);
+      __builtin_amdgcn_sched_barrier(0);
+      bool need;
+      if (j >= jm)
+        need = softmax_chunk<NH, kFirst, true>(sacc, pk, m_ref, l_run, lim);
+      else
+        need = softmax_chunk<NH, kFirst, false>(sacc, pk, m_ref, l_run, lim);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!kLag) {
+        pv_chunk<NH>(ring(slot_c), vbase, pk, oacc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      need_restart |= need;
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    // (an item always has at least one chunk)
+    issue(Slot<0>{}, 0);
+    issue(Slot<1>{}, 1);
+    interval(Slot<0>{}, T{}, 0);
+    for (int j = 1; j <= nchunks; j += 4) {
+      interval(Slot<1>{}, F{}, j);
+      interval(Slot<2>{}, F{}, j + 1);
+      interval(Slot<3>{}, F{}, j + 2);
+      interval(Slot<0>{}, F{}, j + 3);
+    }
   };
-  // (an item always has at least one chunk)
-  issue(Slot<0>{}, 0);
-  issue(Slot<1>{}, 1);
-  issue(Slot<2>{}, 2);
-  chunk(Slot<0>{}, T{}, 0);
-  for (int j = 1; j < nchunks; j += 4) {
-    chunk(Slot<1>{}, F{}, j);
-    chunk(Slot<2>{}, F{}, j + 1);
-    chunk(Slot<3>{}, F{}, j + 2);
-    chunk(Slot<0>{}, F{}, j + 3);
-  }
+  if (NW == 8 && wave >= 4)
+    pass(std::true_type{});
+  else
+    pass(std::false_type{});
   // every wavefront's verdict, then one decision for the workgroup
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
@@ -547,8 +570,8 @@ DecodeConfig decode_config(int rows_per_seq) {
   c.chunk = kChunk;
   c.nbuf = 4;
   if (groups % 8 == 0) {
-    c.waves = 4;
-    c.heads_per_wave = 2;
+    c.waves = 8;
+    c.heads_per_wave = 1;
   } else if (groups % 4 == 0) {
     c.waves = 2;
     c.heads_per_wave = 2;
@@ -559,7 +582,7 @@ DecodeConfig decode_config(int rows_per_seq) {
     c.waves = 1;
     c.heads_per_wave = 1;
   }
-  c.lds_bytes = c.nbuf * kBufBytes;
+  c.lds_bytes = c.nbuf * (c.waves == 8 ? Dma<8>::kSlotBytes : kBufBytes);
   c.wgs_per_cu = 1;  // the ring fills the LDS
   return c;
 }
@@ -592,7 +615,7 @@ hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const u
   args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
-  if (cfg.waves == 4) return launch_t<4, 2>(grid, args, block_table, stream);
+  if (cfg.waves == 8) return launch_t<8, 1>(grid, args, block_table, stream);
   if (cfg.waves == 2) return launch_t<2, 2>(grid, args, block_table, stream);
   if (cfg.heads_per_wave == 2) return launch_t<1, 2>(grid, args, block_table, stream);
   return launch_t<1, 1>(grid, args, block_table, stream);
