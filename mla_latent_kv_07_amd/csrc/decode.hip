@@ -118,9 +118,10 @@ constexpr int kRsrcWord3 = 0x00020000;
 
 // Copy one chunk (36 KB at `src`, a wavefront-uniform address) into the LDS
 // ring slot `buf` (wavefront-uniform): buffer loads straight to LDS, with the
-// chunk as the buffer (scalar descriptor) and a 32-bit per-lane offset.  With
-// `bytes` = 0 every lane is out of range: no memory is read (the slot gets
-// zeros), but the instruction count stays the same.
+// chunk as the buffer (scalar descriptor) and a 32-bit per-lane offset.  The
+// buffer range is `bytes`: lanes beyond it read no memory and write zeros to
+// LDS (checked per dword).  A partial last chunk thus arrives zero-padded, and
+// `bytes` = 0 gives an empty copy with the same instruction count.
 template <int NW, int KP>
 __device__ __forceinline__ void load_chunk(MLA_LDS char* buf, const char* src, int bytes,
                                            const uint32_t* off, int wave) {
@@ -143,7 +144,7 @@ template <int NH>
 __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_even,
                                             int sbase_odd, const bf16x8 (&qreg)[NH][18],
                                             f32x4 (&sacc)[NH][2]) {
-  constexpr int KPD = 3;
+  constexpr int KPD = 4;
 #pragma unroll
   for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -236,34 +237,41 @@ __device__ __forceinline__ bool softmax_chunk(f32x4 (&sacc)[NH][2], bf16x8 (&pk)
 }
 
 
-template <int NH>
-__device__ __forceinline__ void pv_chunk(const MLA_LDS char* buf, const int (&vbase)[4],
-                                         const bf16x8 (&pk)[NH], f32x4 (&oacc)[NH][32]) {
-  // feature tile f: byte vbase[f & 3] + 128*(f >> 2); second half +16 rows
-  bf16x8 vb[32];
+// P.V for the wavefront's slice of the latent features: for the FT = 32/NW
+// feature tiles of the slice and all G = NW*NH row groups of the workgroup,
+// O^T[g][f] += V^T[f] P^T[g].  pb[g] is the B operand of row group g.  V^T
+// comes from the chunk through the transposing read; feature tile f of the
+// slice sits at vbase[f & 3] + 128*(f >> 2) + slice_off.
+template <int NW, int NH>
+__device__ __forceinline__ void pv_slice(const MLA_LDS char* buf, const int (&vbase)[4],
+                                         int slice_off, const bf16x8 (&pb)[NW * NH],
+                                         f32x4 (&oacc)[NW * NH][32 / NW]) {
+  constexpr int G = NW * NH;
+  constexpr int FT = 32 / NW;
+  bf16x8 vb[FT];
 #pragma unroll
-  for (int f = 0; f < 32; ++f) {
-    const MLA_LDS char* p = buf + vbase[f & 3] + 128 * (f >> 2);
+  for (int f = 0; f < FT; ++f) {
+    const MLA_LDS char* p = buf + vbase[f & 3] + 128 * (f >> 2) + slice_off;
     const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p);
     const bf16x4 a1 =
         __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p + 16 * kEntryBytes));
     vb[f] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 #pragma unroll
-  for (int f = 0; f < 32; ++f)
+  for (int f = 0; f < FT; ++f)
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
-      oacc[h][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[f], pk[h], oacc[h][f], 0, 0, 0);
+    for (int g = 0; g < G; ++g)
+      oacc[g][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[f], pb[g], oacc[g][f], 0, 0, 0);
   // schedule: VPD feature tiles of reads ahead, then one tile of reads per
   // tile of MFMAs (the reads of tile f + VPD overlap the MFMAs of tile f)
-  constexpr int VPD = 4;
+  constexpr int VPD = FT < 4 ? FT : 4;
   __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * VPD, 0);
 #pragma unroll
-  for (int f = 0; f < 32 - VPD; ++f) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, NH, 0);
+  for (int f = 0; f < FT - VPD; ++f) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, G, 0);
     __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(kSgMfma, NH * VPD, 0);
+  __builtin_amdgcn_sched_group_barrier(kSgMfma, G * VPD, 0);
 }
 
 // Row max only (the first pass of a restart).
@@ -302,6 +310,8 @@ __device__ __forceinline__ void ring_barrier() {
 template <int NW, int NH>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
                                                          const int32_t* __restrict__ block_table) {
+  constexpr int G = NW * NH;   // 16-row groups of the workgroup
+  constexpr int FT = 32 / NW;  // feature tiles of a wavefront's P.V slice
   // The ring: four chunk slots, each its own array.  Chunk j lives in slot
   // j % 4, and the chunk loop is unrolled by four so that every access names
   // its slot at compile time: the compiler then knows that the copies in
@@ -311,6 +321,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   __shared__ __attribute__((aligned(1024))) char ring1[Dma<NW>::kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char ring2[Dma<NW>::kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char ring3[Dma<NW>::kSlotBytes];
+  // probabilities of the chunk, one 1 KB B-operand tile per row group
+  __shared__ __attribute__((aligned(1024))) char pbuf[G * 1024];
+  // row sums at the end
+  __shared__ float lbuf[G * 16];
   auto ring = [&](auto slot_c) -> MLA_LDS char* {
     constexpr int S = decltype(slot_c)::value;
     if constexpr (S == 0) return (MLA_LDS char*)ring0;
@@ -318,6 +332,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     else if constexpr (S == 2) return (MLA_LDS char*)ring2;
     else return (MLA_LDS char*)ring3;
   };
+  MLA_LDS char* pb_lds = (MLA_LDS char*)pbuf;
 
   // blockIdx -> (item, row group); the row groups of one item land on the
   // same XCD (block ids congruent mod 8) so their chunk reads share that L2.
@@ -336,8 +351,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int gq = lane >> 4;
-  const int row0 = (rg * NW + wave) * 16 * NH;  // first row of this wave in the sequence
-  int tmax[NH];                                 // last visible position per row group
+  const int rows0 = rg * G * 16;          // first row of the workgroup in the sequence
+  const int row0 = rows0 + wave * 16 * NH;  // first scored row of this wavefront
+  int tmax[NH];                           // last visible position per scored row group
   int tmax_min = 0x7fffffff;
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
@@ -361,6 +377,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     for (int f4 = 0; f4 < 4; ++f4)
       vbase[f4] = row * kEntryBytes + 16 * ((2 * f4) ^ y) + 8 * (qq & 1);
   }
+  // this wavefront's feature slice: tiles wave*FT .. +FT (FT is a multiple of 4)
+  const int slice_off = 32 * wave * FT;
 
   // the absorbed query rows, in registers for the whole item: lane holds
   // features 32ks + 8gq .. +8 of row n (the B operand of k-step ks)
@@ -372,28 +390,27 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qreg[h][ks] = qp[4 * ks];
   }
-  f32x4 oacc[NH][32];
+  // O^T of the workgroup's rows, this wavefront's feature slice
+  f32x4 oacc[G][FT];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int f = 0; f < FT; ++f) oacc[g][f] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref[NH], l_run[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-#pragma unroll
-    for (int f = 0; f < 32; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_ref[h] = -INFINITY;
     l_run[h] = 0.f;
   }
-  // restart flag of this workgroup (LDS is full): written by any wavefront,
-  // read by all after a barrier, which orders it within the workgroup
+  // restart flag of this workgroup: written by any wavefront, read by all
+  // after a barrier, which orders it within the workgroup
   int* flag = a.restart_flag + blockIdx.x;
   if (threadIdx.x == 0) __atomic_store_n(flag, 0, __ATOMIC_RELAXED);
 
   const int tok_begin = p0 * kPage;
   const int tok_end = min(p1 * kPage, len);
   const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
-  // the last chunk of the sequence may end inside the chunk: its rows from
-  // `tail_rows` on hold other positions' slots (NaN sentinels, stale data)
-  // and are zeroed in LDS once the chunk has landed, before any wave reads it
-  const int tail_rows = tok_end - tok_begin - (nchunks - 1) * kChunk;
-  // chunks from jm on reach past the causal limit of some row (or the
+  // chunks from jm on reach past the causal limit of some scored row (or the
   // sequence end) and take the masked softmax
   const int jm = (tmax_min - tok_begin + 1) / kChunk;
   const int32_t* bt = block_table + (int64_t)b * a.bt_stride;  // scalar loads (restrict)
@@ -401,25 +418,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   constexpr int kPer = Dma<NW>::kPerWave;
   uint32_t doff[kPer];
   dma_offsets<NW>(wave, lane, doff);
-  // Every chunk step issues exactly one copy (an empty one past the item's
+  // Every interval issues exactly one copy (an empty one past the item's
   // end), so "chunk j has landed" is always "at most two copies pending":
   // one wait count for every chunk, which the compiler can follow and so adds
   // no conservative full drain of its own.
+  // The last chunk of the sequence may end inside the chunk: its copy reads
+  // only the valid rows, the others arrive as zeros (never the NaN sentinels
+  // or stale data of the slots beyond the sequence end).
   auto issue = [&](auto slot_c, int j) {
     const bool real = j < nchunks;
     const int t = tok_begin + (real ? j : 0) * kChunk;
     const int64_t blk = bt[t / kPage];
     const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kEntryBytes;
-    load_chunk<NW, kPer>(ring(slot_c), src, real ? kBufBytes : 0, doff, wave);
-  };
-  // after chunk j has landed in every wavefront's view (barrier passed)
-  auto fix_tail = [&](auto slot_c, int j) {
-    if (j == nchunks - 1 && tail_rows < kChunk) {
-      MLA_LDS char* bp = ring(slot_c);
-      for (int pc = tail_rows * kChunk16 + (int)threadIdx.x; pc < kChunk * kChunk16; pc += NW * 64)
-        *reinterpret_cast<MLA_LDS u16x8*>(bp + 16 * pc) = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      ring_barrier();
-    }
+    const int bytes = real ? min(tok_end - t, kChunk) * kEntryBytes : 0;
+    load_chunk<NW, kPer>(ring(slot_c), src, bytes, doff, wave);
   };
   // visibility limit of chunk j for this lane, relative to its slot 16t + i
   auto chunk_limits = [&](int j, int (&lim)[NH]) {
@@ -427,77 +439,71 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
 #pragma unroll
     for (int h = 0; h < NH; ++h) lim[h] = tmax[h] - t0 - 4 * gq;
   };
+  // One chunk: scores and softmax of this wavefront's rows, the probabilities
+  // to LDS, a barrier, then the P.V of all the workgroup's rows for this
+  // wavefront's feature slice.  Returns the restart verdict of its rows.
+  auto compute = [&](auto slot_c, auto first_c, int j) -> bool {
+    constexpr bool kFirst = decltype(first_c)::value;
+    int lim[NH];
+    chunk_limits(j, lim);
+    f32x4 sacc[NH][2];
+    // the phases stay in order: moving the next phase's LDS reads up would
+    // keep their registers live across this one
+    score_chunk<NH>(ring(slot_c), sbase_even, sbase_odd, qreg, sacc);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 pk[NH];
+    bool need;
+    if (j >= jm)
+      need = softmax_chunk<NH, kFirst, true>(sacc, pk, m_ref, l_run, lim);
+    else
+      need = softmax_chunk<NH, kFirst, false>(sacc, pk, m_ref, l_run, lim);
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+      *reinterpret_cast<MLA_LDS bf16x8*>(pb_lds + (wave * NH + h) * 1024 + lane * 16) = pk[h];
+    ring_barrier();
+    bf16x8 pb[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      pb[g] = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_lds + g * 1024 + lane * 16);
+    __builtin_amdgcn_sched_barrier(0);
+    pv_slice<NW, NH>(ring(slot_c), vbase, slice_off, pb, oacc);
+    __builtin_amdgcn_sched_barrier(0);
+    return need;
+  };
 
   // ---- main pass: reference = the first chunk's max per row ----------------
-  // Interval j: wait for chunk j, barrier, copy chunk j+2 into the slot of
-  // chunk j-2.  While interval j computes, chunks j+1 and j+2 are in flight.
-  // With two wavefronts per SIMD (NW == 8) the wavefronts 4..7 lag: in
-  // interval j they run the P.V of chunk j-1 first, then the scores and
-  // softmax of chunk j, while their SIMD partners 0..3 run scores, softmax and
-  // P.V of chunk j.  One wavefront's matrix work then overlaps its partner's
-  // softmax and LDS waits instead of both running the same phase at once.
-  // After interval 0 the intervals run in groups of four (slots 1, 2, 3, 0),
-  // up to and including interval nchunks (the lagging P.V of the last chunk);
-  // intervals past the item's end still wait, pass the barrier and issue
-  // their (empty) copy.  No vector memory instruction sits in a conditional,
-  // so on every path the compiler sees the same copies pending.
+  // While chunk j is computed, chunks j+1 and j+2 are in flight and chunk j+3
+  // goes into chunk j-1's slot once every wavefront is past chunk j-1.
+  // After chunk 0 the chunks run in groups of four (slots 1, 2, 3, 0); a
+  // group may reach past the item's end, and such steps still wait, pass the
+  // barrier and issue their (empty) copy but skip the compute.  No vector
+  // memory instruction sits in a conditional, so on every path the compiler
+  // sees the same copies pending.
   // (a wavefront that needs a restart keeps going with a useless result;
   // the verdict is taken once, after the pass)
+  using T = std::true_type;
+  using F = std::false_type;
   bool need_restart = false;
-  auto pass = [&](auto lag_c) {
-    constexpr bool kLag = decltype(lag_c)::value;
-    f32x4 sacc[NH][2];
-    bf16x8 pk[NH];
-    auto interval = [&](auto slot_c, auto first_c, int j) {
-      constexpr int S = decltype(slot_c)::value;
-      constexpr bool kFirst = decltype(first_c)::value;
-      // chunk j has landed once at most the copy of chunk j+1 is pending
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
-      ring_barrier();
-      issue(Slot<(S + 2) & 3>{}, j + 2);
-      if constexpr (kLag && !kFirst) {
-        if (j - 1 < nchunks) {
-          pv_chunk<NH>(ring(Slot<(S + 3) & 3>{}), vbase, pk, oacc);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      if (j >= nchunks) return;
-      fix_tail(slot_c, j);
-      int lim[NH];
-      chunk_limits(j, lim);
-      // the phases stay in order: moving the next phase's LDS reads up would
-      // keep their registers live across this one
-      score_chunk<NH>(ring(slot_c), sbase_even, sbase_odd, qreg, sacc);
-      __builtin_amdgcn_sched_barrier(0);
-      bool need;
-      if (j >= jm)
-        need = softmax_chunk<NH, kFirst, true>(sacc, pk, m_ref, l_run, lim);
-      else
-        need = softmax_chunk<NH, kFirst, false>(sacc, pk, m_ref, l_run, lim);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!kLag) {
-        pv_chunk<NH>(ring(slot_c), vbase, pk, oacc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      need_restart |= need;
-    };
-    using T = std::true_type;
-    using F = std::false_type;
-    // (an item always has at least one chunk)
-    issue(Slot<0>{}, 0);
-    issue(Slot<1>{}, 1);
-    interval(Slot<0>{}, T{}, 0);
-    for (int j = 1; j <= nchunks; j += 4) {
-      interval(Slot<1>{}, F{}, j);
-      interval(Slot<2>{}, F{}, j + 1);
-      interval(Slot<3>{}, F{}, j + 2);
-      interval(Slot<0>{}, F{}, j + 3);
-    }
+  auto interval = [&](auto slot_c, auto first_c, int j) {
+    constexpr int S = decltype(slot_c)::value;
+    // chunk j has landed once at most the copies of chunks j+1, j+2 are pending
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
+    ring_barrier();
+    // chunk j+3 goes into chunk j-1's slot: every wavefront is past it
+    issue(Slot<(S + 3) & 3>{}, j + 3);
+    if (j < nchunks) need_restart |= compute(slot_c, first_c, j);
   };
-  if (NW == 8 && wave >= 4)
-    pass(std::true_type{});
-  else
-    pass(std::false_type{});
+  // (an item always has at least one chunk)
+  issue(Slot<0>{}, 0);
+  issue(Slot<1>{}, 1);
+  issue(Slot<2>{}, 2);
+  interval(Slot<0>{}, T{}, 0);
+  for (int j = 1; j < nchunks; j += 4) {
+    interval(Slot<1>{}, F{}, j);
+    interval(Slot<2>{}, F{}, j + 1);
+    interval(Slot<3>{}, F{}, j + 2);
+    interval(Slot<0>{}, F{}, j + 3);
+  }
   // every wavefront's verdict, then one decision for the workgroup
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
@@ -517,7 +523,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
       issue(Slot<0>{}, j);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
-      fix_tail(Slot<0>{}, j);
       int lim[NH];
       chunk_limits(j, lim);
       f32x4 sacc[NH][2];
@@ -529,38 +534,42 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     for (int h = 0; h < NH; ++h) {
       m_ref[h] = m_exact[h];
       l_run[h] = 0.f;
-#pragma unroll
-      for (int f = 0; f < 32; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int f = 0; f < FT; ++f) oacc[g][f] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < nchunks; ++j) {
       issue(Slot<0>{}, j);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
-      fix_tail(Slot<0>{}, j);
-      int lim[NH];
-      chunk_limits(j, lim);
-      f32x4 sacc[NH][2];
-      bf16x8 pk[NH];
-      score_chunk<NH>(ring(Slot<0>{}), sbase_even, sbase_odd, qreg, sacc);
-      softmax_chunk<NH, false, true>(sacc, pk, m_ref, l_run, lim);
-      pv_chunk<NH>(ring(Slot<0>{}), vbase, pk, oacc);
+      compute(Slot<0>{}, F{}, j);
       __syncthreads();
     }
   }
 
   // ---- finalise: normalised rows and log2-sum-exp ---------------------------
+  // each wavefront's row sums to LDS; every wavefront normalises its slice
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     float l = l_run[h];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
     const float lse = l > 0.f ? m_ref[h] + __builtin_amdgcn_logf(l) : -INFINITY;
-    const int64_t orow = (int64_t)item * a.rows_per_seq + row0 + 16 * h + n;
-    float* op = a.o_part + orow * kLatent + 4 * gq;
+    if (gq == 0) {
+      lbuf[(wave * NH + h) * 16 + n] = l;
+      a.lse_part[(int64_t)item * a.rows_per_seq + row0 + 16 * h + n] = lse;
+    }
+  }
+  __syncthreads();
 #pragma unroll
-    for (int f = 0; f < 32; ++f) *reinterpret_cast<f32x4*>(op + 16 * f) = oacc[h][f] * inv;
-    if (gq == 0) a.lse_part[orow] = lse;
+  for (int g = 0; g < G; ++g) {
+    const float l = lbuf[g * 16 + n];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t orow = (int64_t)item * a.rows_per_seq + rows0 + 16 * g + n;
+    float* op = a.o_part + orow * kLatent + 16 * wave * FT + 4 * gq;
+#pragma unroll
+    for (int f = 0; f < FT; ++f) *reinterpret_cast<f32x4*>(op + 16 * f) = oacc[g][f] * inv;
   }
 }
 
@@ -570,8 +579,8 @@ DecodeConfig decode_config(int rows_per_seq) {
   c.chunk = kChunk;
   c.nbuf = 4;
   if (groups % 8 == 0) {
-    c.waves = 8;
-    c.heads_per_wave = 1;
+    c.waves = 4;
+    c.heads_per_wave = 2;
   } else if (groups % 4 == 0) {
     c.waves = 2;
     c.heads_per_wave = 2;
@@ -582,7 +591,7 @@ DecodeConfig decode_config(int rows_per_seq) {
     c.waves = 1;
     c.heads_per_wave = 1;
   }
-  c.lds_bytes = c.nbuf * (c.waves == 8 ? Dma<8>::kSlotBytes : kBufBytes);
+  c.lds_bytes = c.nbuf * kBufBytes + c.waves * c.heads_per_wave * (1024 + 64);
   c.wgs_per_cu = 1;  // the ring fills the LDS
   return c;
 }
@@ -615,7 +624,7 @@ hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const u
   args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
-  if (cfg.waves == 8) return launch_t<8, 1>(grid, args, block_table, stream);
+  if (cfg.waves == 4) return launch_t<4, 2>(grid, args, block_table, stream);
   if (cfg.waves == 2) return launch_t<2, 2>(grid, args, block_table, stream);
   if (cfg.heads_per_wave == 2) return launch_t<1, 2>(grid, args, block_table, stream);
   return launch_t<1, 1>(grid, args, block_table, stream);
