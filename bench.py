@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the step's kernels one call at a time instead of replaying a "
+                         "captured HIP graph of the step")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, one plain device-to-device copy of this many MiB "
                          "(reference dispatch for scaling HBM byte counters)")
@@ -110,10 +113,23 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if not args.eager:
+        # the step (insert + decode: four kernels) captured once as a HIP
+        # graph and replayed, as a serving loop would; the library allocates
+        # nothing and records no memset, so the graph is replay-safe
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
     # the timed steps: nothing else on the stream
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # the same steps again with HIP events recorded by the library around each
@@ -147,7 +163,8 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "batch": bsz, "q_len": q_len, "heads": heads,
                    "context": "8192 each" if args.workload == WORKLOAD else "see workloads.py",
-                   "page": 64, "kv_lora": 512, "rope": 64, "step": "cache_insert + decode"},
+                   "page": 64, "kv_lora": 512, "rope": 64, "step": "cache_insert + decode",
+                   "launch": "eager" if args.eager else "hip graph"},
         "tokens_per_s": round(bsz * q_len / (ms_step * 1e-3), 1),
         "alg_bytes_per_step": alg_bytes,
         "alg_flops_per_step": alg_flops,

@@ -9,10 +9,10 @@
 // 128 rows of head h's kv_b block; "DeepSeek-V2-Lite 模型结构详解" §五 gives
 // the identity that moves W_UV behind the weighted sum.
 //
-// One workgroup per (head, 32 query rows).  The merged latent rows are
-// rounded to bf16 into LDS, then D^T = W_UV o_lat^T runs on the bf16 MFMA
-// 16x16x32 with W_UV streamed from global memory (each head's 128 KB block is
-// read once per workgroup).
+// The split partials arrive as bf16 rows.  One workgroup per (head, 32 query
+// rows).  The merged latent rows are rounded to bf16 into LDS, then
+// D^T = W_UV o_lat^T runs on the bf16 MFMA 16x16x32 with W_UV streamed from
+// global memory (each head's 128 KB block is read once per workgroup).
 #include "mla_common.h"
 
 namespace mla {
@@ -20,7 +20,7 @@ namespace mla {
 constexpr int kCombRows = 32;                 // query rows per workgroup
 constexpr int kCombRowBytes = kLatent * 2 + 16;  // padded LDS row (bank spread)
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       PlanView plan,
                                                       const uint16_t* __restrict__ kv_b,
@@ -34,18 +34,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
 
-  // ---- merge: wave w handles rows w*8 .. w*8+7; lane covers 8 columns -------
-  // Two rows at a time: their split weights are computed lane-parallel
-  // (lane s <-> split s, 64 splits at a time), then all their partial rows
-  // are loaded with independent loads before any is used.
-  constexpr int kRowsPerWave = kCombRows / 4;
-  for (int rr = 0; rr < kRowsPerWave; rr += 2) {
-    int s0[2], ns[2];
-    int64_t srow[2];
-    bool live[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int bi = row_base + wave * kRowsPerWave + rr + u;
+  // ---- merge: wave w handles rows w*8 .. w*8+7 together; lane covers 8 columns
+  // All eight rows' split weights are computed lane-parallel (lane s <-> split
+  // s, 64 splits per pass), then their bf16 partial rows are loaded KB splits
+  // at a time with independent loads before any is used.
+  {
+    constexpr int R = kCombRows / 4;
+    constexpr int KB = 4;
+    int s0[R], ns[R];
+    int64_t srow[R];
+    bool live[R];
+  #pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int bi = row_base + wave * R + u;
       live[u] = bi < total_rows;
       const int b = live[u] ? bi / q_len : 0;
       const int i = live[u] ? bi - b * q_len : 0;
@@ -53,65 +54,66 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       s0[u] = plan.seq_start[b];
       ns[u] = live[u] ? plan.seq_count[b] : 0;
     }
-    float acc[2][8];
-    float wsum[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      wsum[u] = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[u][j] = 0.f;
+    int nmax = 0;
+  #pragma unroll
+    for (int u = 0; u < R; ++u) nmax = max(nmax, ns[u]);
+    // max log2-sum-exp over all splits of each row
+    float mx[R];
+  #pragma unroll
+    for (int u = 0; u < R; ++u) {
+      mx[u] = -INFINITY;
+      for (int s = lane; s < ns[u]; s += 64)
+        mx[u] = fmaxf(mx[u], lse_part[(int64_t)(s0[u] + s) * rows_per_seq + srow[u]]);
+  #pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) mx[u] = fmaxf(mx[u], __shfl_xor(mx[u], o, 64));
     }
-    const int nmax = max(ns[0], ns[1]);
+    float macc[R][8];
+    float wsum[R];
+  #pragma unroll
+    for (int u = 0; u < R; ++u) {
+      wsum[u] = 0.f;
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) macc[u][e] = 0.f;
+    }
     for (int sb = 0; sb < nmax; sb += 64) {
-      float w_l[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        // weights of splits sb .. sb+63 relative to the max over ALL splits
-        float mx = -INFINITY;
-        for (int s = lane; s < ns[u]; s += 64)
-          mx = fmaxf(mx, lse_part[(int64_t)(s0[u] + s) * rows_per_seq + srow[u]]);
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      float w_l[R];
+  #pragma unroll
+      for (int u = 0; u < R; ++u) {
         const int s_l = sb + lane;
         const float lse =
             s_l < ns[u] ? lse_part[(int64_t)(s0[u] + s_l) * rows_per_seq + srow[u]] : -INFINITY;
-        w_l[u] = lse == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lse - mx);
+        w_l[u] = lse == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lse - mx[u]);
       }
       const int cnt = min(64, nmax - sb);
-      for (int s = 0; s < cnt; s += 4) {
-        f32x4 v[2][4][2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const bool ok = s + k < cnt && sb + s + k < ns[u];
+      for (int s = 0; s < cnt; s += KB) {
+        u16x8 v[R][KB];
+  #pragma unroll
+        for (int u = 0; u < R; ++u)
+  #pragma unroll
+          for (int k = 0; k < KB; ++k) {
+            const bool ok = sb + s + k < ns[u];
             const int64_t r = (int64_t)(s0[u] + (ok ? sb + s + k : 0)) * rows_per_seq + srow[u];
-            const f32x4* src = reinterpret_cast<const f32x4*>(o_part + r * kLatent + lane * 8);
-            v[u][k][0] = ok ? src[0] : f32x4{0.f, 0.f, 0.f, 0.f};
-            v[u][k][1] = ok ? src[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+            v[u][k] = ok ? *reinterpret_cast<const u16x8*>(o_part + r * kLatent + lane * 8)
+                         : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
           }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
+  #pragma unroll
+        for (int u = 0; u < R; ++u)
+  #pragma unroll
+          for (int k = 0; k < KB; ++k) {
             const float w = (s + k < cnt) ? __shfl(w_l[u], s + k, 64) : 0.f;
             wsum[u] += w;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              acc[u][j] += w * v[u][k][0][j];
-              acc[u][4 + j] += w * v[u][k][1][j];
-            }
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) macc[u][e] += w * bf16_to_f32(v[u][k][e]);
           }
       }
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
+  #pragma unroll
+    for (int u = 0; u < R; ++u) {
       const float inv = wsum[u] > 0.f ? 1.f / wsum[u] : 0.f;
       u16x8 packed;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) packed[j] = live[u] ? f32_to_bf16(acc[u][j] * inv) : 0;
-      const int lr = wave * kRowsPerWave + rr + u;
-      *reinterpret_cast<u16x8*>(olat + lr * kCombRowBytes + lane * 16) = packed;
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) packed[e] = live[u] ? f32_to_bf16(macc[u][e] * inv) : 0;
+      *reinterpret_cast<u16x8*>(olat + (wave * R + u) * kCombRowBytes + lane * 16) = packed;
     }
   }
   __syncthreads();
@@ -126,7 +128,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint16_t* wuv = kv_b + ((int64_t)h * (kNope + kVdim) + kNope) * kLatent;
-#pragma unroll 4
+  // fully unrolled: every W_UV load of the wavefront can be in flight at once
+#pragma unroll
   for (int ks = 0; ks < kLatent / 32; ++ks) {
     bf16x8 av[2], bv[NT];
 #pragma unroll
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_combine(const float* o_part, const float* lse_part, PlanView plan,
+hipError_t launch_combine(const uint16_t* o_part, const float* lse_part, PlanView plan,
                           const uint16_t* kv_b, int heads, int q_len, int batch, uint16_t* out,
                           hipStream_t stream) {
   const int rows = batch * q_len;

@@ -51,8 +51,8 @@
 //     rescaled.  If the check fails (never for well-scaled attention, but
 //     possible), the workgroup restarts the item: one pass for the exact row
 //     max, one pass with that max as the reference.
-// Output per work item: normalised fp32 rows [rows, 512] and their log2-sum-
-// exp, merged across items by the combine kernel.
+// Output per work item: normalised rows [rows, 512] rounded to bf16 and their
+// log2-sum-exp, merged across items by the combine kernel.
 #include <type_traits>
 
 #include "mla_common.h"
@@ -63,7 +63,7 @@ struct DecodeArgs {
   const uint16_t* q_abs;     // [B * rows_per_seq, 576]
   const uint16_t* cache;     // [num_blocks, 64, 576]
   const int32_t* seq_lens;
-  float* o_part;             // [max_items, rows_per_seq, 512]
+  uint16_t* o_part;          // [max_items, rows_per_seq, 512] bf16
   float* lse_part;           // [max_items, rows_per_seq]
   int* restart_flag;         // one int per workgroup (workgroup-local communication)
   PlanView plan;
@@ -567,9 +567,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     const float l = lbuf[g * 16 + n];
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t orow = (int64_t)item * a.rows_per_seq + rows0 + 16 * g + n;
-    float* op = a.o_part + orow * kLatent + 16 * wave * FT + 4 * gq;
+    uint16_t* op = a.o_part + orow * kLatent + 16 * wave * FT + 4 * gq;
 #pragma unroll
-    for (int f = 0; f < FT; ++f) *reinterpret_cast<f32x4*>(op + 16 * f) = oacc[g][f] * inv;
+    for (int f = 0; f < FT; ++f) {
+      u16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(oacc[g][f][i] * inv);
+      *reinterpret_cast<u16x4*>(op + 16 * f) = v;
+    }
   }
 }
 
@@ -607,7 +612,7 @@ static hipError_t launch_t(int grid, const DecodeArgs& args, const int32_t* bloc
 hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const uint16_t* cache,
                          const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
                          int heads, int q_len, PlanView plan, int max_items,
-                         float* o_part, float* lse_part,
+                         uint16_t* o_part, float* lse_part,
                          int* restart_flags, hipStream_t stream) {
   DecodeArgs args;
   args.restart_flag = restart_flags;

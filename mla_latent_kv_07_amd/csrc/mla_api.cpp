@@ -8,7 +8,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/mla.h"
+#include "mla.h"
 #include "mla_common.h"
 
 namespace {
@@ -78,7 +78,7 @@ Layout make_layout(int heads, int batch, int q_len, int hint) {
   L.off_seq_count = take(4 * (size_t)batch);
   L.off_flags = take(4 * ((size_t)L.max_items + 8) * row_groups);
   L.off_qabs = take((size_t)batch * rows * kEntry * 2);
-  L.off_opart = take((size_t)L.max_items * rows * kLatent * 4);
+  L.off_opart = take((size_t)L.max_items * rows * kLatent * 2);
   L.off_lse = take((size_t)L.max_items * rows * 4);
   L.total = off;
   return L;
@@ -207,12 +207,14 @@ int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void
   plan.seq_start = reinterpret_cast<int32_t*>(ws + L.off_seq_start);
   plan.seq_count = reinterpret_cast<int32_t*>(ws + L.off_seq_count);
   uint16_t* q_abs = reinterpret_cast<uint16_t*>(ws + L.off_qabs);
-  float* o_part = reinterpret_cast<float*>(ws + L.off_opart);
+  uint16_t* o_part = reinterpret_cast<uint16_t*>(ws + L.off_opart);
   float* lse_part = reinterpret_cast<float*>(ws + L.off_lse);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int rows = heads * q_len;
-  // price of one item's partial rows (fp32 write + read) in cache pages
-  const float item_cost = (float)rows * kLatent * 4 * 2 / (float)kPageBytes;
+  // price of one item's fixed work in cache pages: its set-up (query rows,
+  // plan entries: about four pages' time) plus its partial rows (bf16 write
+  // + read)
+  const float item_cost = 4.0f + (float)rows * kLatent * 2 * 2 / (float)kPageBytes;
 
   const int pc = g_prof.used < g_prof.max_calls ? g_prof.used++ : -1;
   prof_mark(pc, 0, s);

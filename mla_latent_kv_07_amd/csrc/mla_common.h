@@ -82,10 +82,10 @@ DecodeConfig decode_config(int rows_per_seq);
 hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const uint16_t* cache,
                          const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
                          int heads, int q_len, PlanView plan, int max_items,
-                         float* o_part, float* lse_part,
+                         uint16_t* o_part, float* lse_part,
                          int* restart_flags, hipStream_t stream);
 
-hipError_t launch_combine(const float* o_part, const float* lse_part, PlanView plan,
+hipError_t launch_combine(const uint16_t* o_part, const float* lse_part, PlanView plan,
                           const uint16_t* kv_b, int heads, int q_len, int batch, uint16_t* out,
                           hipStream_t stream);
 

@@ -12,9 +12,12 @@
 //
 // Cost model for a candidate item size c (in pages):
 //   items(c) = sum_b ceil(pages_b / c)
-//   time(c)  = min(ceil(items/slots) * c, total/slots + c) + cost * items/slots
+//   big(c)   = max_b ceil(pages_b / ceil(pages_b / c))  (largest actual item)
+//   time(c)  = min(ceil(items/slots) * big(c), total/slots + big(c))
+//              + cost * items/slots
 // where `slots` is the number of workgroups that run at once and `cost` the
-// price, in pages, of writing and merging one item's partial rows.
+// price, in pages, of one item's fixed work: its set-up and the writing and
+// merging of its partial rows.
 //
 // Everything is wave-parallel (shuffle reductions and scans); no thread walks
 // a long dependent chain through LDS.
@@ -26,7 +29,7 @@ namespace mla {
 constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanShared = 8192;  // sequences whose page counts are kept in LDS
-constexpr int kCandidates = 64;
+constexpr int kCandidates = 24;
 constexpr int kPlanSmemBytes = 4 * (kPlanShared + kPlanWaves + kCandidates + 1);
 
 // Pages of a sequence, clamped to the host-side bound so that a length beyond
@@ -42,10 +45,12 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-// candidate k: 1..24, then a geometric ladder (x1.25), capped at max_pages
+// candidate k: 1..8 pages, then a ladder growing by about a third (the last
+// entry is replaced by max_pages)
 __device__ __forceinline__ int candidate(int k, int max_pages) {
-  int c = k < 24 ? k + 1 : (int)(24.0f * __builtin_exp2f(0.3219281f * (float)(k - 23)));
-  if (k == kCandidates - 1) c = max_pages;
+  constexpr int kLadder[kCandidates] = {1,  2,  3,  4,  5,  6,  7,   8,   10,  13,  18,  24,
+                                        32, 42, 56, 72, 96, 128, 168, 224, 296, 392, 512, 0};
+  int c = k == kCandidates - 1 ? max_pages : kLadder[k];
   return c > max_pages ? max_pages : (c < 1 ? 1 : c);
 }
 
@@ -92,15 +97,22 @@ __device__ void plan_block(const PlanArgs& pa, MLA_LDS char* smem) {
     // each wave scores kCandidates / kPlanWaves candidate sizes
     for (int k = wave; k < kCandidates; k += kPlanWaves) {
       const int c = candidate(k, max_pages);
-      int items = 0;
-      for (int b = lane; b < batch; b += 64) items += (pages(b) + c - 1) / c;
+      int items = 0, big = 0;
+      for (int b = lane; b < batch; b += 64) {
+        const int p = pages(b);
+        const int n = (p + c - 1) / c;
+        items += n;
+        big = max(big, (p + n - 1) / n);
+      }
       items = wave_sum(items);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) big = max(big, __shfl_xor(big, o, 64));
       if (lane == 0) {
         float cost = 3.0e38f;
         if (items <= max_items) {
           const float rounds = (float)((items + slots - 1) / slots);
-          const float t1 = rounds * (float)c;
-          const float t2 = (float)total / (float)slots + (float)c;
+          const float t1 = rounds * (float)big;
+          const float t2 = (float)total / (float)slots + (float)big;
           cost = fminf(t1, t2) + item_cost * (float)items / (float)slots;
         }
         sh_cost[k] = cost;
@@ -109,7 +121,7 @@ __device__ void plan_block(const PlanArgs& pa, MLA_LDS char* smem) {
     __syncthreads();
     if (wave == 0) {
       // arg-min over candidates, ties to the larger item size (lane = candidate)
-      float best = sh_cost[lane];
+      float best = lane < kCandidates ? sh_cost[lane] : 3.0e38f;
       int bk = lane;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {

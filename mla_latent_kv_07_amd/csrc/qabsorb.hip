@@ -7,8 +7,8 @@
 // block; "DeepSeek-V2-Lite 模型结构详解" §五 gives the identity
 // q . (W_k c) = (W_k^T q) . c that moves W_UK to the query side.
 //
-// The same launch also makes the split plan (plan.h) in one extra workgroup,
-// so the planner's latency hides under the absorption.
+// The same launch also makes the split plan (plan.h) in its first workgroup
+// (dispatched first), so the planner's latency hides under the absorption.
 //
 // One workgroup per (head, 128 latent columns); W_UK[h][:, cols] (32 KB) is
 // staged in LDS and read as the MFMA A operand with the gfx950 transposing
@@ -26,20 +26,20 @@ constexpr int kQaStride = kQaCols * 2 + 32;  // padded LDS row of W_UK (bytes)
 constexpr int kPrepSmem = kNope * kQaStride > kPlanSmemBytes ? kNope * kQaStride : kPlanSmemBytes;
 static_assert(kPlanThreads == 256, "the plan runs on one 256-thread workgroup");
 
-// Blocks 0 .. 4H-1: absorption of head b/4, latent columns (b%4)*128 .. +128.
-// Block 4H: the split plan (independent work, hidden under the absorption).
+// Block 0: the split plan (independent work, hidden under the absorption).
+// Blocks 1 .. 4H: absorption of head (b-1)/4, latent columns ((b-1)%4)*128 .. +128.
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ kv_b, int heads,
                                                    int rows, float q_scale,
                                                    uint16_t* __restrict__ q_abs, PlanArgs pa) {
   __shared__ __attribute__((aligned(16))) char smem[kPrepSmem];
-  if (blockIdx.x == (unsigned)heads * (kLatent / kQaCols)) {
+  if (blockIdx.x == 0) {
     plan_block(pa, (MLA_LDS char*)smem);
     return;
   }
   MLA_LDS char* w_lds = (MLA_LDS char*)smem;
-  const int h = blockIdx.x / (kLatent / kQaCols);
-  const int nc = blockIdx.x % (kLatent / kQaCols);  // column chunk
+  const int h = (blockIdx.x - 1) / (kLatent / kQaCols);
+  const int nc = (blockIdx.x - 1) % (kLatent / kQaCols);  // column chunk
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -90,29 +90,36 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
     }
   }
 
-  for (int rt = 0; rt * 16 < rows; ++rt) {
-    const int rr = rt * 16 + n;
-    const int64_t row = (int64_t)rr * heads + h;
-    bf16x8 bq[4];
+  // four 16-row tiles at a time: all their query loads before any MFMA
+  constexpr int RT = 4;
+  for (int rt0 = 0; rt0 * 16 < rows; rt0 += RT) {
+    bf16x8 bq[RT][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (rr < rows)
-        bq[ks] = *reinterpret_cast<const bf16x8*>(q + row * kQk + 32 * ks + 8 * g);
-      else
-        bq[ks] = bf16x8{};
-    }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < RT; ++u) {
+      const int rr = (rt0 + u) * 16 + n;
+      const int64_t row = (int64_t)rr * heads + h;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[mt][ks], bq[ks], acc, 0, 0, 0);
-      if (rr < rows) {
-        u16x4 v;
+        bq[u][ks] = rr < rows ? *reinterpret_cast<const bf16x8*>(q + row * kQk + 32 * ks + 8 * g)
+                              : bf16x8{};
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(acc[i] * q_scale);
-        *reinterpret_cast<u16x4*>(q_abs + row * kEntry + nc * kQaCols + wave * 32 + mt * 16 +
-                                  4 * g) = v;
+    for (int u = 0; u < RT; ++u) {
+      const int rr = (rt0 + u) * 16 + n;
+      const int64_t row = (int64_t)rr * heads + h;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[mt][ks], bq[u][ks], acc, 0, 0, 0);
+        if (rr < rows) {
+          u16x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(acc[i] * q_scale);
+          *reinterpret_cast<u16x4*>(q_abs + row * kEntry + nc * kQaCols + wave * 32 + mt * 16 +
+                                    4 * g) = v;
+        }
       }
     }
   }

@@ -83,7 +83,8 @@ def test_workspace_bytes(lib):
     d = _dims(heads=128)
     w0 = lib.mla_decode_workspace_bytes(ctypes.byref(d), 64, 1, 8192, 0)
     w1 = lib.mla_decode_workspace_bytes(ctypes.byref(d), 64, 1, 8192, 4)
-    assert w0 > 64 * 128 * 576 * 2 and w1 > 64 * 4 * 128 * 512 * 4
+    # absorbed query (bf16) and, with 4 splits, the bf16 split partials
+    assert w0 > 64 * 128 * 576 * 2 and w1 > 64 * 4 * 128 * 512 * 2
     assert lib.mla_decode_workspace_bytes(ctypes.byref(d), 64, 1, 0, 0) == 0
     assert lib.mla_decode_workspace_bytes(ctypes.byref(_dims(heads=8)), 64, 1, 8192, 0) == 0
 
