@@ -334,14 +334,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   };
   MLA_LDS char* pb_lds = (MLA_LDS char*)pbuf;
 
-  // blockIdx -> (item, row group); the row groups of one item land on the
-  // same XCD (block ids congruent mod 8) so their chunk reads share that L2.
+  // blockIdx -> (item, row group).  Workgroups are dispatched to the eight
+  // XCDs round-robin (block id mod 8); XCD x takes a contiguous range of the
+  // item list, which is in sequence order, so the items of one sequence (and
+  // the row groups of one item) share that XCD's L2: the sequence's absorbed
+  // query rows come from HBM once.
   const int gid = blockIdx.x;
   const int xcd = gid & 7;
   const int gslot = gid >> 3;
-  const int item = (gslot / a.row_groups) * 8 + xcd;
-  const int rg = gslot - (gslot / a.row_groups) * a.row_groups;
-  if (item >= a.plan.header[0]) return;
+  const int n_items = a.plan.header[0];
+  const int per_xcd = (n_items + 7) >> 3;
+  const int local = gslot / a.row_groups;
+  const int rg = gslot - local * a.row_groups;
+  const int item = xcd * per_xcd + local;
+  if (local >= per_xcd || item >= n_items) return;
 
   const int b = a.plan.item_b[item];
   const int p0 = a.plan.item_p0[item];
