@@ -115,22 +115,28 @@ __device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&off)[
 
 // Buffer descriptor word 3 for gfx9-family raw buffer loads.
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache-policy bits of the cache copies: non-temporal.  Every cache byte is
+// read once per launch; the hint keeps the stream from displacing what the
+// neighbouring kernels reuse from L2 and the last-level cache (the absorbed
+// query, the partial rows, kv_b).
+constexpr int kCopyPolicy = 2;
 
-// Copy one chunk (36 KB at `src`, a wavefront-uniform address) into the LDS
-// ring slot `buf` (wavefront-uniform): buffer loads straight to LDS, with the
-// chunk as the buffer (scalar descriptor) and a 32-bit per-lane offset.  The
-// buffer range is `bytes`: lanes beyond it read no memory and write zeros to
-// LDS (checked per dword).  A partial last chunk thus arrives zero-padded, and
-// `bytes` = 0 gives an empty copy with the same instruction count.
-template <int NW, int KP>
+// Copy instructions I0 .. I1-1 of the wavefront's share of one chunk (36 KB
+// at `src`, a wavefront-uniform address) into the LDS ring slot `buf`
+// (wavefront-uniform): buffer loads straight to LDS, with the chunk as the
+// buffer (scalar descriptor) and a 32-bit per-lane offset.  The buffer range
+// is `bytes`: lanes beyond it read no memory and write zeros to LDS (checked
+// per dword).  A partial last chunk thus arrives zero-padded, and `bytes` = 0
+// gives an empty copy with the same instruction count.
+template <int NW, int I0, int I1>
 __device__ __forceinline__ void load_chunk(MLA_LDS char* buf, const char* src, int bytes,
                                            const uint32_t* off, int wave) {
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, bytes, kRsrcWord3);
 #pragma unroll
-  for (int i = 0; i < KP; ++i)
+  for (int i = I0; i < I1; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, buf + (i * NW + wave) * 1024, 16, off[i], 0, 0,
-                                             0);
+                                             kCopyPolicy);
 }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
@@ -431,13 +437,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   // The last chunk of the sequence may end inside the chunk: its copy reads
   // only the valid rows, the others arrive as zeros (never the NaN sentinels
   // or stale data of the slots beyond the sequence end).
-  auto issue = [&](auto slot_c, int j) {
+  // copy instructions I0 .. I1-1 of chunk j into its slot
+  auto issue_part = [&](auto slot_c, int j, auto i0_c, auto i1_c) {
     const bool real = j < nchunks;
     const int t = tok_begin + (real ? j : 0) * kChunk;
     const int64_t blk = bt[t / kPage];
     const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kEntryBytes;
     const int bytes = real ? min(tok_end - t, kChunk) * kEntryBytes : 0;
-    load_chunk<NW, kPer>(ring(slot_c), src, bytes, doff, wave);
+    load_chunk<NW, decltype(i0_c)::value, decltype(i1_c)::value>(ring(slot_c), src, bytes, doff,
+                                                                   wave);
+  };
+  auto issue = [&](auto slot_c, int j) {
+    issue_part(slot_c, j, std::integral_constant<int, 0>{}, std::integral_constant<int, kPer>{});
   };
   // visibility limit of chunk j for this lane, relative to its slot 16t + i
   auto chunk_limits = [&](int j, int (&lim)[NH]) {
@@ -479,7 +490,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
 
   // ---- main pass: reference = the first chunk's max per row ----------------
   // While chunk j is computed, chunks j+1 and j+2 are in flight and chunk j+3
-  // goes into chunk j-1's slot once every wavefront is past chunk j-1.
+  // goes into chunk j-1's slot once every wavefront is past chunk j-1.  Its
+  // copies are issued in two halves, after the barrier and after the compute:
+  // the LDS-DMA path takes roughly 15 cycles per 1 KB copy, and a wavefront
+  // stalls when it issues copies faster than that, so the second half goes
+  // out while the other wavefronts finish the chunk.
   // After chunk 0 the chunks run in groups of four (slots 1, 2, 3, 0); a
   // group may reach past the item's end, and such steps still wait, pass the
   // barrier and issue their (empty) copy but skip the compute.  No vector
@@ -496,8 +511,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
     ring_barrier();
     // chunk j+3 goes into chunk j-1's slot: every wavefront is past it
-    issue(Slot<(S + 3) & 3>{}, j + 3);
+    constexpr int kHalf = (kPer + 1) / 2;
+    issue_part(Slot<(S + 3) & 3>{}, j + 3, std::integral_constant<int, 0>{},
+               std::integral_constant<int, kHalf>{});
     if (j < nchunks) need_restart |= compute(slot_c, first_c, j);
+    issue_part(Slot<(S + 3) & 3>{}, j + 3, std::integral_constant<int, kHalf>{},
+               std::integral_constant<int, kPer>{});
   };
   // (an item always has at least one chunk)
   issue(Slot<0>{}, 0);

@@ -94,29 +94,50 @@ __device__ void plan_block(const PlanArgs& pa, MLA_LDS char* smem) {
   for (int w = 0; w < kPlanWaves; ++w) total += sh_wave[w];
 
   if (splits_hint <= 0) {
-    // each wave scores kCandidates / kPlanWaves candidate sizes
-    for (int k = wave; k < kCandidates; k += kPlanWaves) {
-      const int c = candidate(k, max_pages);
-      int items = 0, big = 0;
-      for (int b = lane; b < batch; b += 64) {
-        const int p = pages(b);
-        const int n = (p + c - 1) / c;
-        items += n;
-        big = max(big, (p + n - 1) / n);
-      }
-      items = wave_sum(items);
+    // each wave scores kCandidates / kPlanWaves candidate sizes; their
+    // per-lane sums come first and the cross-lane reductions run side by side
+    // (one chain of shuffle latencies instead of one per candidate)
+    constexpr int kPerWave = kCandidates / kPlanWaves;
+    static_assert(kCandidates % kPlanWaves == 0, "candidates split evenly over the waves");
+    int items[kPerWave], big[kPerWave];
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) big = max(big, __shfl_xor(big, o, 64));
-      if (lane == 0) {
-        float cost = 3.0e38f;
-        if (items <= max_items) {
-          const float rounds = (float)((items + slots - 1) / slots);
-          const float t1 = rounds * (float)big;
-          const float t2 = (float)total / (float)slots + (float)big;
-          cost = fminf(t1, t2) + item_cost * (float)items / (float)slots;
-        }
-        sh_cost[k] = cost;
+    for (int i = 0; i < kPerWave; ++i) {
+      items[i] = 0;
+      big[i] = 0;
+    }
+    for (int b = lane; b < batch; b += 64) {
+      const int p = pages(b);
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int c = candidate(wave + i * kPlanWaves, max_pages);
+        const int n = (p + c - 1) / c;
+        items[i] += n;
+        big[i] = max(big[i], (p + n - 1) / n);
       }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        items[i] += __shfl_xor(items[i], o, 64);
+        big[i] = max(big[i], __shfl_xor(big[i], o, 64));
+      }
+    if (lane < kPerWave) {
+      // lane i publishes candidate wave + i*kPlanWaves
+      int it = items[0], bg = big[0];
+#pragma unroll
+      for (int i = 1; i < kPerWave; ++i) {
+        it = lane == i ? items[i] : it;
+        bg = lane == i ? big[i] : bg;
+      }
+      float cost = 3.0e38f;
+      if (it <= max_items) {
+        const float rounds = (float)((it + slots - 1) / slots);
+        const float t1 = rounds * (float)bg;
+        const float t2 = (float)total / (float)slots + (float)bg;
+        cost = fminf(t1, t2) + item_cost * (float)it / (float)slots;
+      }
+      sh_cost[wave + lane * kPlanWaves] = cost;
     }
     __syncthreads();
     if (wave == 0) {

@@ -43,16 +43,38 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  // Every global load that does not depend on another goes out first: the
+  // query rows of the first RT row tiles (B operands), then W_UK.
+  constexpr int RT = 4;  // 16-row tiles per round: all their query loads before any MFMA
+  auto load_q = [&](int rt0, bf16x8 (&bq)[RT][4]) {
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+      const int rr = min((rt0 + u) * 16 + n, rows - 1);  // rows past the end: never stored
+      const int64_t row = (int64_t)rr * heads + h;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        bq[u][ks] = *reinterpret_cast<const bf16x8*>(q + row * kQk + 32 * ks + 8 * g);
+    }
+  };
+  bf16x8 bq[RT][4];
+  load_q(0, bq);
 
   // stage W_UK[h][d][nc*128 .. +128] for d < 128
   const uint16_t* wuk = kv_b + (int64_t)h * (kNope + kVdim) * kLatent + nc * kQaCols;
+  constexpr int kStage = (kNope * kQaCols / 8) / 256;
+  u16x8 wst[kStage];
 #pragma unroll
-  for (int k = 0; k < (kNope * kQaCols / 8) / 256; ++k) {
+  for (int k = 0; k < kStage; ++k) {
     const int p = k * 256 + tid;
-    const int d = p >> 4;
-    const int c16 = p & 15;
-    *reinterpret_cast<MLA_LDS u16x8*>(w_lds + d * kQaStride + c16 * 16) =
-        *reinterpret_cast<const u16x8*>(wuk + (int64_t)d * kLatent + c16 * 8);
+    wst[k] = *reinterpret_cast<const u16x8*>(wuk + (int64_t)(p >> 4) * kLatent + (p & 15) * 8);
+  }
+#pragma unroll
+  for (int k = 0; k < kStage; ++k) {
+    const int p = k * 256 + tid;
+    *reinterpret_cast<MLA_LDS u16x8*>(w_lds + (p >> 4) * kQaStride + (p & 15) * 16) = wst[k];
   }
   // q_pe times the scale (done once per head, by column chunk 0)
   if (nc == 0) {
@@ -70,8 +92,6 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   __syncthreads();
 
   // A operands: W_UK^T tiles for this wave's 32 columns, all 4 k-steps of 32 d
-  const int n = lane & 15;
-  const int g = lane >> 4;
   const int s16 = lane & 15;
   const int r = s16 >> 2;
   const int qq = s16 & 3;
@@ -90,19 +110,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
     }
   }
 
-  // four 16-row tiles at a time: all their query loads before any MFMA
-  constexpr int RT = 4;
   for (int rt0 = 0; rt0 * 16 < rows; rt0 += RT) {
-    bf16x8 bq[RT][4];
-#pragma unroll
-    for (int u = 0; u < RT; ++u) {
-      const int rr = (rt0 + u) * 16 + n;
-      const int64_t row = (int64_t)rr * heads + h;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        bq[u][ks] = rr < rows ? *reinterpret_cast<const bf16x8*>(q + row * kQk + 32 * ks + 8 * g)
-                              : bf16x8{};
-    }
+    if (rt0 > 0) load_q(rt0, bq);
 #pragma unroll
     for (int u = 0; u < RT; ++u) {
       const int rr = (rt0 + u) * 16 + n;
