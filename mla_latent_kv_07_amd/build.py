@@ -36,9 +36,17 @@ def common_flags() -> list[str]:
             "-Wno-unused-command-line-argument"]
 
 
+# Per-source flags.  decode.hip: uniform branches stay as written (no flow
+# blocks): the decode chunk loop issues the same copies on both arms of its
+# "chunk past the item's end" branch, and the compiler's wait-count analysis
+# follows them exactly only if the branch is not restructured.
+EXTRA_FLAGS = {"decode.hip": ["-mllvm", "-structurizecfg-skip-uniform-regions"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -141,15 +141,56 @@ __device__ __forceinline__ void load_chunk(MLA_LDS char* buf, const char* src, i
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgMfma = 0x008;
+constexpr int kSgVmemRead = 0x020;
 constexpr int kSgDsRead = 0x100;
+
+// One chunk's copy as a buffer (scalar descriptor) and its ring slot.
+struct ChunkCopy {
+  __amdgpu_buffer_rsrc_t rsrc;
+  MLA_LDS char* dst;
+};
+
+// Copy instruction i of the wavefront's share of a chunk (see load_chunk).
+template <int NW>
+__device__ __forceinline__ void copy_piece(const ChunkCopy& c, const uint32_t* off, int i,
+                                           int wave) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, c.dst + (i * NW + wave) * 1024, 16, off[i], 0,
+                                           0, kCopyPolicy);
+}
+
+// Score k-step at which copy c of NC goes out: spread evenly over the first
+// KS k-steps.
+constexpr int copy_step(int c, int nc, int ks) { return c * ks / nc; }
+
+// Schedule of k-steps KS .. KEND-1 of score_chunk: the step's copies, its
+// MFMAs, then the LDS reads of a later step.
+template <int NH, int NC, int KS, int KEND>
+__device__ __forceinline__ void score_schedule() {
+  if constexpr (KS < KEND) {
+    constexpr int kNc = [] {
+      int k = 0;
+      for (int c = 0; c < NC; ++c) k += copy_step(c, NC, KEND) == KS;
+      return k;
+    }();
+    if constexpr (kNc > 0) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, kNc, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 2 * NH, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+    score_schedule<NH, NC, KS + 1, KEND>();
+  }
+}
 
 // Scores of one chunk for the wavefront's NH row groups: sacc[h][t] holds
 // S^T for positions 16t..16t+15.  The LDS reads of k-step ks + KPD are issued
-// before the MFMAs of k-step ks.
-template <int NH>
+// before the MFMAs of k-step ks.  NC > 0: the NC copy instructions of a later
+// chunk (`cc`, into another slot) are spread over the k-steps: the LDS-DMA
+// path takes roughly 15 cycles per 1 KB copy, and a wavefront that issues
+// copies faster than that stalls, so they go out one at a time between
+// MFMAs instead of all at once.
+template <int NH, int NW, int NC>
 __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_even,
                                             int sbase_odd, const bf16x8 (&qreg)[NH][18],
-                                            f32x4 (&sacc)[NH][2]) {
+                                            f32x4 (&sacc)[NH][2], const ChunkCopy& cc,
+                                            const uint32_t* off, int wave) {
   constexpr int KPD = 4;
 #pragma unroll
   for (int h = 0; h < NH; ++h)
@@ -175,6 +216,9 @@ __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_e
       for (int t = 0; t < 2; ++t) kb[(ks + KPD) % (KPD + 1)][t] = kload(ks + KPD, t);
     }
 #pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (copy_step(c, NC, 18 - KPD) == ks) copy_piece<NW>(cc, off, c, wave);
+#pragma unroll
     for (int h = 0; h < NH; ++h) {
       const bf16x8 qb = qreg[h][ks];
 #pragma unroll
@@ -186,11 +230,7 @@ __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_e
   // schedule: KPD k-steps of reads ahead, then per k-step its MFMAs and the
   // reads of k-step ks + KPD
   __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * KPD, 0);
-#pragma unroll
-  for (int ks = 0; ks < 18 - KPD; ++ks) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 2 * NH, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-  }
+  score_schedule<NH, NC, 0, 18 - KPD>();
   __builtin_amdgcn_sched_group_barrier(kSgMfma, 2 * NH * KPD, 0);
 }
 
@@ -437,6 +477,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   // The last chunk of the sequence may end inside the chunk: its copy reads
   // only the valid rows, the others arrive as zeros (never the NaN sentinels
   // or stale data of the slots beyond the sequence end).
+  auto chunk_copy = [&](auto slot_c, int j) -> ChunkCopy {
+    const bool real = j < nchunks;
+    const int t = tok_begin + (real ? j : 0) * kChunk;
+    const int64_t blk = bt[t / kPage];
+    const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kEntryBytes;
+    const int bytes = real ? min(tok_end - t, kChunk) * kEntryBytes : 0;
+    return ChunkCopy{
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, bytes, kRsrcWord3),
+        ring(slot_c)};
+  };
   // copy instructions I0 .. I1-1 of chunk j into its slot
   auto issue_part = [&](auto slot_c, int j, auto i0_c, auto i1_c) {
     const bool real = j < nchunks;
@@ -459,14 +509,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   // One chunk: scores and softmax of this wavefront's rows, the probabilities
   // to LDS, a barrier, then the P.V of all the workgroup's rows for this
   // wavefront's feature slice.  Returns the restart verdict of its rows.
-  auto compute = [&](auto slot_c, auto first_c, int j) -> bool {
+  // (NC > 0: the copies of `cc` go out during the score phase)
+  auto compute = [&](auto slot_c, auto first_c, auto nc_c, int j, const ChunkCopy& cc) -> bool {
     constexpr bool kFirst = decltype(first_c)::value;
     int lim[NH];
     chunk_limits(j, lim);
     f32x4 sacc[NH][2];
     // the phases stay in order: moving the next phase's LDS reads up would
     // keep their registers live across this one
-    score_chunk<NH>(ring(slot_c), sbase_even, sbase_odd, qreg, sacc);
+    score_chunk<NH, NW, decltype(nc_c)::value>(ring(slot_c), sbase_even, sbase_odd, qreg, sacc,
+                                               cc, doff, wave);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 pk[NH];
     bool need;
@@ -490,11 +542,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
 
   // ---- main pass: reference = the first chunk's max per row ----------------
   // While chunk j is computed, chunks j+1 and j+2 are in flight and chunk j+3
-  // goes into chunk j-1's slot once every wavefront is past chunk j-1.  Its
-  // copies are issued in two halves, after the barrier and after the compute:
-  // the LDS-DMA path takes roughly 15 cycles per 1 KB copy, and a wavefront
-  // stalls when it issues copies faster than that, so the second half goes
-  // out while the other wavefronts finish the chunk.
+  // goes into chunk j-1's slot once every wavefront is past chunk j-1; its
+  // copies run inside the score phase of chunk j (or on their own for a step
+  // past the item's end).
   // After chunk 0 the chunks run in groups of four (slots 1, 2, 3, 0); a
   // group may reach past the item's end, and such steps still wait, pass the
   // barrier and issue their (empty) copy but skip the compute.  No vector
@@ -511,12 +561,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
     ring_barrier();
     // chunk j+3 goes into chunk j-1's slot: every wavefront is past it
-    constexpr int kHalf = (kPer + 1) / 2;
-    issue_part(Slot<(S + 3) & 3>{}, j + 3, std::integral_constant<int, 0>{},
-               std::integral_constant<int, kHalf>{});
-    if (j < nchunks) need_restart |= compute(slot_c, first_c, j);
-    issue_part(Slot<(S + 3) & 3>{}, j + 3, std::integral_constant<int, kHalf>{},
-               std::integral_constant<int, kPer>{});
+    const ChunkCopy cc = chunk_copy(Slot<(S + 3) & 3>{}, j + 3);
+    if (j < nchunks) {
+      need_restart |= compute(slot_c, first_c, std::integral_constant<int, kPer>{}, j, cc);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) copy_piece<NW>(cc, doff, i, wave);
+    }
   };
   // (an item always has at least one chunk)
   issue(Slot<0>{}, 0);
@@ -551,7 +602,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
       int lim[NH];
       chunk_limits(j, lim);
       f32x4 sacc[NH][2];
-      score_chunk<NH>(ring(Slot<0>{}), sbase_even, sbase_odd, qreg, sacc);
+      score_chunk<NH, NW, 0>(ring(Slot<0>{}), sbase_even, sbase_odd, qreg, sacc, ChunkCopy{},
+                             doff, wave);
       max_chunk<NH>(sacc, m_exact, lim);
       __syncthreads();
     }
@@ -568,7 +620,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
       issue(Slot<0>{}, j);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
-      compute(Slot<0>{}, F{}, j);
+      compute(Slot<0>{}, F{}, std::integral_constant<int, 0>{}, j, ChunkCopy{});
       __syncthreads();
     }
   }
