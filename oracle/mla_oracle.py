@@ -173,11 +173,15 @@ def cache_insert(cache_bits: np.ndarray, kv_a_bits: np.ndarray, w_bits: np.ndarr
 
 
 def _gather_sequence(cache: np.ndarray, block_table: np.ndarray, b: int, length: int):
-    """Rows 0..length-1 of sequence b, through its block table (float64)."""
+    """Rows 0..length-1 of sequence b, through its block table (float64).
+
+    ``cache`` holds bf16 bit patterns (uint16), or values already widened to
+    float64 (the dequantised FP8 cache), which pass through unchanged."""
     page = cache.shape[1]
     t = np.arange(length)
     blocks = block_table[b, t // page].astype(np.int64)
-    return bf16_bits_to_f64(cache[blocks, t % page, :])
+    rows = cache[blocks, t % page, :]
+    return rows if rows.dtype == np.float64 else bf16_bits_to_f64(rows)
 
 
 def _visible(length: int, q_len: int) -> np.ndarray:
@@ -200,7 +204,7 @@ def decode_expanded(q_bits: np.ndarray, kv_b_bits: np.ndarray, cache_bits: np.nd
 
     q_bits     : uint16 [B, q_len, H, nope + rope], q_pe already rotated
     kv_b_bits  : uint16 [H * (nope + v_dim), latent] (kv_b_proj weight)
-    cache_bits : uint16 [num_blocks, page, latent + rope]
+    cache_bits : uint16 [num_blocks, page, latent + rope] (or float64 values)
     Returns float64 [len(batches), q_len, len(heads), v_dim].
 
     [V3-src] "(a) Naive实现": kv_b_proj applied to the normalised latent gives
