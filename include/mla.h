@@ -134,8 +134,45 @@ int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void
                int32_t num_splits_hint, void* stream);
 
 /*
+ * FP8 latent cache ("DeepSeek-V3.2-Exp unboxing", 初步研读: the deployed KV
+ * cache is FP8, and the indexer beside it keeps one scale per cached token;
+ * the vLLM DeepSeek-V4 notes, section 一: KV quantisation fused into the
+ * cache insert, UE8M0 power-of-two scales).  The pages fix no format; this
+ * library's row is MLA_FP8_ROW_BYTES bytes per token:
+ *   bytes [0, 512)    the 512 latent values as FP8 E4M3 ("FN": bias 7, no
+ *                     infinities, 0x7F/0xFF NaN, largest finite 448) codes
+ *   bytes [512, 640)  the 64 rope values, bf16, little endian
+ *   byte  640         scale byte s: the latent value of code c is
+ *                     e4m3(c) * 2^(s - 127)
+ *   bytes [641, 656)  zero
+ * A page is 64 such rows; cache = uint8 [num_blocks, 64, 656].
+ *
+ * mla_cache_insert_fp8 — as mla_cache_insert (same arguments, same
+ * normalised latent and rotated k_pe), then per token the scale 2^e is the
+ * smallest power of two with max|latent| * 2^-e <= 448 (e in [-126, 127];
+ * e = 0 for an all-zero latent) and each latent value is stored as the E4M3
+ * code of value * 2^-e, rounded to nearest even.  Writes whole 656-byte rows.
+ *
+ * mla_decode_fp8 — as mla_decode (same arguments and workspace size, same
+ * output) over an FP8 cache: every cached latent value is taken as
+ * e4m3(code) * 2^(s - 127), which is exact in bf16, so the arithmetic is that
+ * of mla_decode on the dequantised cache.
+ */
+#define MLA_FP8_ROW_BYTES 656
+int mla_cache_insert_fp8(const mla_dims* dims, const void* kv_a, const void* rms_w,
+                         float eps, float rope_base, const int32_t* block_table,
+                         int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
+                         int32_t q_len, void* cache, int32_t num_blocks, void* stream);
+int mla_decode_fp8(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+                   int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                   const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t max_seq_len,
+                   float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                   int32_t num_splits_hint, void* stream);
+
+/*
  * mla_profile_enable / mla_profile_collect — stage timing for benchmarks.
- * While enabled (max_calls > 0), each mla_decode call records four HIP events
+ * While enabled (max_calls > 0), each mla_decode / mla_decode_fp8 call records
+ * four HIP events
  * on its stream: before the prep kernel (query absorption + split plan),
  * before the split-KV decode kernel, before the merge + projection kernel, and
  * after it.  Events come from a pool of max_calls sets created here

@@ -5,6 +5,7 @@ declared in ``include/mla.h``).  This package is a thin ctypes binding with the
 same entry-point names; torch is used only for device memory and streams.
 """
 from ._lib import (  # noqa: F401
+    FP8_ROW_BYTES,
     MLAError,
     abi_version,
     cache_insert,

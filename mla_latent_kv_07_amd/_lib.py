@@ -14,6 +14,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libmla.so"
 LATENT, ROPE, NOPE, VDIM, PAGE = 512, 64, 128, 128, 64
+FP8_ROW_BYTES = 656  # FP8 cache row (see include/mla.h)
 
 _lib = None
 
@@ -51,6 +52,10 @@ def load() -> ctypes.CDLL:
     lib.mla_decode_workspace_bytes.restype = SZ
     lib.mla_decode.argtypes = [DP, P, P, P, I32, P, I32, P, I32, I32, I32, F, P, P, SZ, I32, P]
     lib.mla_decode.restype = ctypes.c_int
+    lib.mla_cache_insert_fp8.argtypes = lib.mla_cache_insert.argtypes
+    lib.mla_cache_insert_fp8.restype = ctypes.c_int
+    lib.mla_decode_fp8.argtypes = lib.mla_decode.argtypes
+    lib.mla_decode_fp8.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_profile_enable.argtypes = [I32]
@@ -101,11 +106,21 @@ def _check(t, name, dtype, shape=None, device=None):
     return t
 
 
+def _check_cache(cache, fp8: bool, dev):
+    import torch
+    if fp8:
+        return _check(cache, "cache", torch.uint8, (cache.shape[0], PAGE, FP8_ROW_BYTES), dev)
+    return _check(cache, "cache", torch.bfloat16, (cache.shape[0], PAGE, LATENT + ROPE), dev)
+
+
 def cache_insert(kv_a, rms_w, block_table, seq_lens, cache, *, eps: float = 1e-6,
-                 rope_base: float = 10000.0, heads: int = 16, stream=None) -> None:
-    """mla_cache_insert: kv_a bf16 [B, q_len, 576], rms_w bf16 [512],
-    block_table int32 [B, max_blocks], seq_lens int32 [B] (post-insert lengths),
-    cache bf16 [num_blocks, 64, 576] updated in place."""
+                 rope_base: float = 10000.0, heads: int = 16, stream=None,
+                 fp8: bool = False) -> None:
+    """mla_cache_insert (fp8=False: cache bf16 [num_blocks, 64, 576]) or
+    mla_cache_insert_fp8 (fp8=True: cache uint8 [num_blocks, 64, 656]):
+    kv_a bf16 [B, q_len, 576], rms_w bf16 [512], block_table int32
+    [B, max_blocks], seq_lens int32 [B] (post-insert lengths); the cache is
+    updated in place."""
     import torch
     bsz, q_len = kv_a.shape[0], kv_a.shape[1]
     dev = cache.device
@@ -113,13 +128,14 @@ def cache_insert(kv_a, rms_w, block_table, seq_lens, cache, *, eps: float = 1e-6
     _check(rms_w, "rms_w", torch.bfloat16, (LATENT,), dev)
     _check(block_table, "block_table", torch.int32, None, dev)
     _check(seq_lens, "seq_lens", torch.int32, (bsz,), dev)
-    _check(cache, "cache", torch.bfloat16, (cache.shape[0], PAGE, LATENT + ROPE), dev)
+    _check_cache(cache, fp8, dev)
     d = dims(heads)
-    st = load().mla_cache_insert(ctypes.byref(d), _ptr(kv_a), _ptr(rms_w), eps, rope_base,
-                                 _ptr(block_table), block_table.shape[1], _ptr(seq_lens), bsz,
-                                 q_len, _ptr(cache), cache.shape[0], _stream(stream))
+    fn = load().mla_cache_insert_fp8 if fp8 else load().mla_cache_insert
+    st = fn(ctypes.byref(d), _ptr(kv_a), _ptr(rms_w), eps, rope_base, _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), bsz, q_len, _ptr(cache), cache.shape[0],
+            _stream(stream))
     if st != 0:
-        raise MLAError(st, "mla_cache_insert")
+        raise MLAError(st, "mla_cache_insert_fp8" if fp8 else "mla_cache_insert")
 
 
 def decode_workspace_bytes(heads: int, batch: int, q_len: int, max_seq_len: int,
@@ -131,15 +147,17 @@ def decode_workspace_bytes(heads: int, batch: int, q_len: int, max_seq_len: int,
 
 def decode(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, *,
            softmax_scale: float | None = None, out=None, workspace=None,
-           num_splits_hint: int = 0, stream=None):
-    """mla_decode: q bf16 [B, q_len, H, 192], kv_b bf16 [H*256, 512],
-    cache bf16 [num_blocks, 64, 576]; returns out bf16 [B, q_len, H, 128]."""
+           num_splits_hint: int = 0, stream=None, fp8: bool = False):
+    """mla_decode (fp8=False: cache bf16 [num_blocks, 64, 576]) or
+    mla_decode_fp8 (fp8=True: cache uint8 [num_blocks, 64, 656]):
+    q bf16 [B, q_len, H, 192], kv_b bf16 [H*256, 512]; returns out bf16
+    [B, q_len, H, 128]."""
     import torch
     bsz, q_len, heads = q.shape[0], q.shape[1], q.shape[2]
     dev = cache.device
     _check(q, "q", torch.bfloat16, (bsz, q_len, heads, NOPE + ROPE), dev)
     _check(kv_b, "kv_b", torch.bfloat16, (heads * (NOPE + VDIM), LATENT), dev)
-    _check(cache, "cache", torch.bfloat16, (cache.shape[0], PAGE, LATENT + ROPE), dev)
+    _check_cache(cache, fp8, dev)
     _check(block_table, "block_table", torch.int32, None, dev)
     _check(seq_lens, "seq_lens", torch.int32, (bsz,), dev)
     if softmax_scale is None:
@@ -152,12 +170,12 @@ def decode(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, *,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check(workspace, "workspace", torch.uint8, None, dev)
     d = dims(heads)
-    st = load().mla_decode(ctypes.byref(d), _ptr(q), _ptr(kv_b), _ptr(cache), cache.shape[0],
-                           _ptr(block_table), block_table.shape[1], _ptr(seq_lens), bsz, q_len,
-                           max_seq_len, softmax_scale, _ptr(out), _ptr(workspace),
-                           workspace.numel(), num_splits_hint, _stream(stream))
+    fn = load().mla_decode_fp8 if fp8 else load().mla_decode
+    st = fn(ctypes.byref(d), _ptr(q), _ptr(kv_b), _ptr(cache), cache.shape[0], _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), bsz, q_len, max_seq_len, softmax_scale,
+            _ptr(out), _ptr(workspace), workspace.numel(), num_splits_hint, _stream(stream))
     if st != 0:
-        raise MLAError(st, "mla_decode")
+        raise MLAError(st, "mla_decode_fp8" if fp8 else "mla_decode")
     return out
 
 

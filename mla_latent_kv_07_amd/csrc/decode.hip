@@ -61,7 +61,7 @@ namespace mla {
 
 struct DecodeArgs {
   const uint16_t* q_abs;     // [B * rows_per_seq, 576]
-  const uint16_t* cache;     // [num_blocks, 64, 576]
+  const void* cache;         // bf16 [num_blocks, 64, 576] or FP8 rows [num_blocks, 64, 656]
   const int32_t* seq_lens;
   uint16_t* o_part;          // [max_items, rows_per_seq, 512] bf16
   float* lse_part;           // [max_items, rows_per_seq]
@@ -81,15 +81,19 @@ constexpr float kSlackPow = 65536.0f;          // 2^16: headroom above the refer
 // Encoding of "s_waitcnt vmcnt(n)" (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int NW>
+// Copies of one chunk of CB bytes: 1 KB per wavefront-wide instruction.
+template <int NW, int CB = kBufBytes>
 struct Dma {
-  static constexpr int kInsts = kBufBytes / 1024;  // 36 wavefront-wide copies per chunk
-  // every wavefront issues the same number of copies; when 36 does not split
-  // evenly the last ones are out of range (no memory access) and land in the
-  // slot's padding
+  static constexpr int kInsts = (CB + 1023) / 1024;  // 36 for a bf16 chunk, 21 for FP8
+  // every wavefront issues the same number of copies; when the count does not
+  // split evenly the last ones are out of range (no memory access) and land
+  // in the slot's padding
   static constexpr int kPerWave = (kInsts + NW - 1) / NW;
   static constexpr int kSlotBytes = kPerWave * NW * 1024;
 };
+// bytes of one chunk in the cache format: 32 rows
+template <bool FP8>
+constexpr int chunk_bytes() { return kChunk * (FP8 ? kFp8EntryBytes : kEntryBytes); }
 
 // Piece permutation inside each aligned group of 8 pieces of row r.
 __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 3) << 1) ^ (((r >> 3) & 1) * 7); }
@@ -100,7 +104,9 @@ __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 3) << 1) ^ (((r 
 // the same contiguous 1 KB of the chunk, permuted within 128-byte lines.  The
 // offsets are the same for every chunk (a chunk is 36 KB of contiguous cache:
 // half a page), so they are computed once.
-template <int NW, int KP>
+// FP8 chunks are copied as they are (lane L of copy k reads bytes
+// 1024k + 16L ..), then expanded into the bf16 layout (dequant_chunk).
+template <int NW, int KP, bool FP8 = false>
 __device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&off)[KP]) {
 #pragma unroll
   for (int i = 0; i < KP; ++i) {
@@ -108,8 +114,53 @@ __device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&off)[
     const int q = 64 * k + lane;
     const int row = q / kChunk16;
     const int col = q - row * kChunk16;
-    off[i] = k < Dma<NW>::kInsts ? (uint32_t)(row * kEntryBytes + 16 * (col ^ swz(row)))
-                                 : 0x80000000u;  // beyond any buffer range
+    const uint32_t o = FP8 ? (uint32_t)(16 * q)
+                           : (uint32_t)(row * kEntryBytes + 16 * (col ^ swz(row)));
+    off[i] = k < Dma<NW, chunk_bytes<FP8>()>::kInsts ? o : 0x80000000u;  // beyond any range
+  }
+}
+
+// Expand an FP8 chunk (32 rows of kFp8EntryBytes at `src`) into the bf16
+// chunk layout the compute reads (1152-byte rows, 16-byte pieces permuted by
+// swz): each group of 8 latent codes becomes 8 bf16 values times the row's
+// power-of-two scale (exact: 4 significant bits), the rope part is copied.
+// Rows past the sequence end arrive as zeros and expand to zeros.
+template <int NW>
+__device__ __forceinline__ void dequant_chunk(const MLA_LDS char* src, MLA_LDS char* dst,
+                                              int tid) {
+  constexpr int T = NW * 64;
+  // the per-thread offsets below are the same for every chunk: recompute them
+  // here rather than let them stay live across the whole chunk loop
+  asm volatile("" : "+v"(tid));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int k = 0; k < (kChunk * 64) / T; ++k) {  // latent: (row, 8-code group)
+    const int task = k * T + tid;
+    const int r = task >> 6;
+    const int c = task & 63;
+    const MLA_LDS char* row = src + r * kFp8EntryBytes;
+    const u32x2 codes = *reinterpret_cast<const MLA_LDS u32x2*>(row + 8 * c);
+    const uint32_t sb = *reinterpret_cast<const MLA_LDS unsigned char*>(row + kFp8ScaleOff);
+    const float scale = __uint_as_float(sb << 23);  // 2^(sb - 127); only its exponent is used
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], scale, false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], scale, true);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], scale, false);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], scale, true);
+    const bf16x8 v = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    *reinterpret_cast<MLA_LDS bf16x8*>(dst + r * kEntryBytes + 16 * (c ^ swz(r))) = v;
+  }
+#pragma unroll
+  for (int k = 0; k < (kChunk * 8 + T - 1) / T; ++k) {  // rope: (row, 16-byte piece)
+    const int task = k * T + tid;
+    if (task < kChunk * 8) {
+      const int r = task >> 3;
+      const int c = task & 7;
+      const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(src + r * kFp8EntryBytes +
+                                                               kFp8RopeOff + 16 * c);
+      *reinterpret_cast<MLA_LDS u32x4*>(dst + r * kEntryBytes + 16 * ((64 + c) ^ swz(r))) = v;
+    }
   }
 }
 
@@ -353,20 +404,26 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int NW, int NH>
+// FP8: the cache holds FP8 rows; each chunk lands in the ring in that form
+// and is expanded into the staging chunk (bf16 layout) before the compute.
+template <int NW, int NH, bool FP8>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
                                                          const int32_t* __restrict__ block_table) {
   constexpr int G = NW * NH;   // 16-row groups of the workgroup
   constexpr int FT = 32 / NW;  // feature tiles of a wavefront's P.V slice
+  constexpr int kRowBytes = FP8 ? kFp8EntryBytes : kEntryBytes;  // cache bytes per position
+  using D = Dma<NW, chunk_bytes<FP8>()>;
   // The ring: four chunk slots, each its own array.  Chunk j lives in slot
   // j % 4, and the chunk loop is unrolled by four so that every access names
   // its slot at compile time: the compiler then knows that the copies in
   // flight (into the other slots) never alias the slot being read and adds
   // no wait of its own on them.
-  __shared__ __attribute__((aligned(1024))) char ring0[Dma<NW>::kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) char ring1[Dma<NW>::kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) char ring2[Dma<NW>::kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) char ring3[Dma<NW>::kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring0[D::kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring1[D::kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring2[D::kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring3[D::kSlotBytes];
+  // FP8: the chunk being computed, expanded to bf16
+  __shared__ __attribute__((aligned(1024))) char stage[FP8 ? kBufBytes : 16];
   // probabilities of the chunk, one 1 KB B-operand tile per row group
   __shared__ __attribute__((aligned(1024))) char pbuf[G * 1024];
   // row sums at the end
@@ -377,6 +434,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     else if constexpr (S == 1) return (MLA_LDS char*)ring1;
     else if constexpr (S == 2) return (MLA_LDS char*)ring2;
     else return (MLA_LDS char*)ring3;
+  };
+  // the bf16 chunk the compute reads for slot S
+  auto cbuf = [&](auto slot_c) -> MLA_LDS char* {
+    if constexpr (FP8) return (MLA_LDS char*)stage;
+    else return ring(slot_c);
   };
   MLA_LDS char* pb_lds = (MLA_LDS char*)pbuf;
 
@@ -467,9 +529,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   const int jm = (tmax_min - tok_begin + 1) / kChunk;
   const int32_t* bt = block_table + (int64_t)b * a.bt_stride;  // scalar loads (restrict)
   const char* cache = reinterpret_cast<const char*>(a.cache);
-  constexpr int kPer = Dma<NW>::kPerWave;
+  constexpr int kPer = D::kPerWave;
   uint32_t doff[kPer];
-  dma_offsets<NW>(wave, lane, doff);
+  dma_offsets<NW, kPer, FP8>(wave, lane, doff);
   // Every interval issues exactly one copy (an empty one past the item's
   // end), so "chunk j has landed" is always "at most two copies pending":
   // one wait count for every chunk, which the compiler can follow and so adds
@@ -481,8 +543,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     const bool real = j < nchunks;
     const int t = tok_begin + (real ? j : 0) * kChunk;
     const int64_t blk = bt[t / kPage];
-    const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kEntryBytes;
-    const int bytes = real ? min(tok_end - t, kChunk) * kEntryBytes : 0;
+    const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kRowBytes;
+    const int bytes = real ? min(tok_end - t, kChunk) * kRowBytes : 0;
     return ChunkCopy{
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, bytes, kRsrcWord3),
         ring(slot_c)};
@@ -492,8 +554,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     const bool real = j < nchunks;
     const int t = tok_begin + (real ? j : 0) * kChunk;
     const int64_t blk = bt[t / kPage];
-    const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kEntryBytes;
-    const int bytes = real ? min(tok_end - t, kChunk) * kEntryBytes : 0;
+    const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kRowBytes;
+    const int bytes = real ? min(tok_end - t, kChunk) * kRowBytes : 0;
     load_chunk<NW, decltype(i0_c)::value, decltype(i1_c)::value>(ring(slot_c), src, bytes, doff,
                                                                    wave);
   };
@@ -517,7 +579,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     f32x4 sacc[NH][2];
     // the phases stay in order: moving the next phase's LDS reads up would
     // keep their registers live across this one
-    score_chunk<NH, NW, decltype(nc_c)::value>(ring(slot_c), sbase_even, sbase_odd, qreg, sacc,
+    score_chunk<NH, NW, decltype(nc_c)::value>(cbuf(slot_c), sbase_even, sbase_odd, qreg, sacc,
                                                cc, doff, wave);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 pk[NH];
@@ -535,7 +597,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     for (int g = 0; g < G; ++g)
       pb[g] = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_lds + g * 1024 + lane * 16);
     __builtin_amdgcn_sched_barrier(0);
-    pv_slice<NW, NH>(ring(slot_c), vbase, slice_off, pb, oacc);
+    pv_slice<NW, NH>(cbuf(slot_c), vbase, slice_off, pb, oacc);
     __builtin_amdgcn_sched_barrier(0);
     return need;
   };
@@ -560,6 +622,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     // chunk j has landed once at most the copies of chunks j+1, j+2 are pending
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
     ring_barrier();
+    if constexpr (FP8) {
+      // every wavefront is past chunk j-1, so the staging chunk is free
+      dequant_chunk<NW>(ring(slot_c), (MLA_LDS char*)stage, threadIdx.x);
+      ring_barrier();
+    }
     // chunk j+3 goes into chunk j-1's slot: every wavefront is past it
     const ChunkCopy cc = chunk_copy(Slot<(S + 3) & 3>{}, j + 3);
     if (j < nchunks) {
@@ -599,10 +666,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
       issue(Slot<0>{}, j);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
+      if constexpr (FP8) {
+        dequant_chunk<NW>(ring(Slot<0>{}), (MLA_LDS char*)stage, threadIdx.x);
+        __syncthreads();
+      }
       int lim[NH];
       chunk_limits(j, lim);
       f32x4 sacc[NH][2];
-      score_chunk<NH, NW, 0>(ring(Slot<0>{}), sbase_even, sbase_odd, qreg, sacc, ChunkCopy{},
+      score_chunk<NH, NW, 0>(cbuf(Slot<0>{}), sbase_even, sbase_odd, qreg, sacc, ChunkCopy{},
                              doff, wave);
       max_chunk<NH>(sacc, m_exact, lim);
       __syncthreads();
@@ -620,6 +691,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
       issue(Slot<0>{}, j);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();
+      if constexpr (FP8) {
+        dequant_chunk<NW>(ring(Slot<0>{}), (MLA_LDS char*)stage, threadIdx.x);
+        __syncthreads();
+      }
       compute(Slot<0>{}, F{}, std::integral_constant<int, 0>{}, j, ChunkCopy{});
       __syncthreads();
     }
@@ -679,14 +754,18 @@ DecodeConfig decode_config(int rows_per_seq) {
 }
 
 template <int NW, int NH>
-static hipError_t launch_t(int grid, const DecodeArgs& args, const int32_t* block_table,
-                          hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<NW, NH>), dim3(grid), dim3(NW * 64), 0, stream, args,
-                     block_table);
+static hipError_t launch_t(int grid, bool fp8, const DecodeArgs& args,
+                          const int32_t* block_table, hipStream_t stream) {
+  if (fp8)
+    hipLaunchKernelGGL((decode_kernel<NW, NH, true>), dim3(grid), dim3(NW * 64), 0, stream, args,
+                       block_table);
+  else
+    hipLaunchKernelGGL((decode_kernel<NW, NH, false>), dim3(grid), dim3(NW * 64), 0, stream,
+                       args, block_table);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const uint16_t* cache,
+hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_abs, const void* cache,
                          const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
                          int heads, int q_len, PlanView plan, int max_items,
                          uint16_t* o_part, float* lse_part,
@@ -706,10 +785,10 @@ hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const u
   args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
-  if (cfg.waves == 4) return launch_t<4, 2>(grid, args, block_table, stream);
-  if (cfg.waves == 2) return launch_t<2, 2>(grid, args, block_table, stream);
-  if (cfg.heads_per_wave == 2) return launch_t<1, 2>(grid, args, block_table, stream);
-  return launch_t<1, 1>(grid, args, block_table, stream);
+  if (cfg.waves == 4) return launch_t<4, 2>(grid, fp8, args, block_table, stream);
+  if (cfg.waves == 2) return launch_t<2, 2>(grid, fp8, args, block_table, stream);
+  if (cfg.heads_per_wave == 2) return launch_t<1, 2>(grid, fp8, args, block_table, stream);
+  return launch_t<1, 1>(grid, fp8, args, block_table, stream);
 }
 
 }  // namespace mla

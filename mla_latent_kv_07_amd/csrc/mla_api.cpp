@@ -148,8 +148,11 @@ const char* mla_status_string(int status) {
   }
 }
 
-int mla_cache_insert(const mla_dims* dims, const void* kv_a, const void* rms_w, float eps,
-                     float rope_base, const int32_t* block_table, int32_t bt_stride,
+namespace {
+
+// The two cache formats share the argument checks of each entry point.
+int cache_insert_any(bool fp8, const mla_dims* dims, const void* kv_a, const void* rms_w,
+                     float eps, float rope_base, const int32_t* block_table, int32_t bt_stride,
                      const int32_t* seq_lens, int32_t batch, int32_t q_len, void* cache,
                      int32_t num_blocks, void* stream) {
   int st = check_dims(dims);
@@ -161,11 +164,34 @@ int mla_cache_insert(const mla_dims* dims, const void* kv_a, const void* rms_w, 
     return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
   if (!kv_a || !rms_w || !block_table || !seq_lens || !cache) return MLA_ERR_NULL;
-  hipError_t e = launch_insert(static_cast<const uint16_t*>(kv_a),
-                               static_cast<const uint16_t*>(rms_w), eps, rope_base, block_table,
-                               bt_stride, seq_lens, batch, q_len, static_cast<uint16_t*>(cache),
-                               static_cast<hipStream_t>(stream));
+  hipError_t e =
+      fp8 ? launch_insert_fp8(static_cast<const uint16_t*>(kv_a),
+                              static_cast<const uint16_t*>(rms_w), eps, rope_base, block_table,
+                              bt_stride, seq_lens, batch, q_len, static_cast<uint8_t*>(cache),
+                              static_cast<hipStream_t>(stream))
+          : launch_insert(static_cast<const uint16_t*>(kv_a),
+                          static_cast<const uint16_t*>(rms_w), eps, rope_base, block_table,
+                          bt_stride, seq_lens, batch, q_len, static_cast<uint16_t*>(cache),
+                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+int mla_cache_insert(const mla_dims* dims, const void* kv_a, const void* rms_w, float eps,
+                     float rope_base, const int32_t* block_table, int32_t bt_stride,
+                     const int32_t* seq_lens, int32_t batch, int32_t q_len, void* cache,
+                     int32_t num_blocks, void* stream) {
+  return cache_insert_any(false, dims, kv_a, rms_w, eps, rope_base, block_table, bt_stride,
+                          seq_lens, batch, q_len, cache, num_blocks, stream);
+}
+
+int mla_cache_insert_fp8(const mla_dims* dims, const void* kv_a, const void* rms_w, float eps,
+                         float rope_base, const int32_t* block_table, int32_t bt_stride,
+                         const int32_t* seq_lens, int32_t batch, int32_t q_len, void* cache,
+                         int32_t num_blocks, void* stream) {
+  return cache_insert_any(true, dims, kv_a, rms_w, eps, rope_base, block_table, bt_stride,
+                          seq_lens, batch, q_len, cache, num_blocks, stream);
 }
 
 size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t q_len,
@@ -177,11 +203,13 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t q
   return make_layout(dims->heads, batch, q_len, num_splits_hint).total;
 }
 
-int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
-               int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
-               const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t max_seq_len,
-               float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
-               int32_t num_splits_hint, void* stream) {
+namespace {
+
+int decode_any(bool fp8, const mla_dims* dims, const void* q, const void* kv_b,
+               const void* cache, int32_t num_blocks, const int32_t* block_table,
+               int32_t bt_stride, const int32_t* seq_lens, int32_t batch, int32_t q_len,
+               int32_t max_seq_len, float softmax_scale, void* out, void* workspace,
+               size_t workspace_bytes, int32_t num_splits_hint, void* stream) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (batch < 0 || batch > kMaxBatch || q_len < 1 || q_len > kMaxQLen || max_seq_len < q_len ||
@@ -226,7 +254,7 @@ int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void
                              item_cost, plan, s);
   prof_mark(pc, 1, s);
   if (e == hipSuccess)
-    e = launch_decode(L.cfg, q_abs, static_cast<const uint16_t*>(cache), block_table, bt_stride,
+    e = launch_decode(L.cfg, fp8, q_abs, cache, block_table, bt_stride,
                       seq_lens, heads, q_len, plan,
                       L.max_items, o_part, lse_part,
                       reinterpret_cast<int*>(ws + L.off_flags), s);
@@ -236,6 +264,28 @@ int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void
                        batch, static_cast<uint16_t*>(out), s);
   prof_mark(pc, 3, s);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+               int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+               const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t max_seq_len,
+               float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+               int32_t num_splits_hint, void* stream) {
+  return decode_any(false, dims, q, kv_b, cache, num_blocks, block_table, bt_stride, seq_lens,
+                    batch, q_len, max_seq_len, softmax_scale, out, workspace, workspace_bytes,
+                    num_splits_hint, stream);
+}
+
+int mla_decode_fp8(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+                   int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                   const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t max_seq_len,
+                   float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                   int32_t num_splits_hint, void* stream) {
+  return decode_any(true, dims, q, kv_b, cache, num_blocks, block_table, bt_stride, seq_lens,
+                    batch, q_len, max_seq_len, softmax_scale, out, workspace, workspace_bytes,
+                    num_splits_hint, stream);
 }
 
 }  // extern "C"

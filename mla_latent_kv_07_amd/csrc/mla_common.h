@@ -18,6 +18,11 @@ constexpr int kQk = kNope + kRope;             // 192
 constexpr int kPage = 64;
 constexpr int kPageBytes = kPage * kEntryBytes;  // 73728
 constexpr int kChunk16 = kEntryBytes / 16;     // 72 16-byte pieces per entry
+// FP8 cache row: 512 E4M3 latent codes, the 64 rope values in bf16, one
+// power-of-two scale byte (value 2^(byte - 127)), zero padding to 656 bytes.
+constexpr int kFp8EntryBytes = 656;
+constexpr int kFp8RopeOff = 512;
+constexpr int kFp8ScaleOff = 640;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -61,6 +66,10 @@ struct PlanView {
 hipError_t launch_insert(const uint16_t* kv_a, const uint16_t* rms_w, float eps, float rope_base,
                          const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
                          int batch, int q_len, uint16_t* cache, hipStream_t stream);
+hipError_t launch_insert_fp8(const uint16_t* kv_a, const uint16_t* rms_w, float eps,
+                             float rope_base, const int32_t* block_table, int bt_stride,
+                             const int32_t* seq_lens, int batch, int q_len, uint8_t* cache,
+                             hipStream_t stream);
 
 // query absorption and the split plan, in one launch
 hipError_t launch_prep(const uint16_t* q, const uint16_t* kv_b, int heads, int rows,
@@ -79,7 +88,8 @@ struct DecodeConfig {
 };
 DecodeConfig decode_config(int rows_per_seq);
 
-hipError_t launch_decode(const DecodeConfig& cfg, const uint16_t* q_abs, const uint16_t* cache,
+// cache: bf16 rows [.., 64, 576], or FP8 rows [.., 64, 656] when fp8
+hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_abs, const void* cache,
                          const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
                          int heads, int q_len, PlanView plan, int max_items,
                          uint16_t* o_part, float* lse_part,

@@ -38,8 +38,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .mla_oracle import (bf16_bits_to_f64, cache_insert, decode_expanded, rmsnorm_bf16,
-                         rope_bf16)
+from .mla_oracle import (bf16_bits_to_f64, cache_insert, decode_expanded, f64_to_bf16_bits,
+                         rmsnorm_bf16, rope_bf16)
 
 FP8_ROW_BYTES = 656           # bytes per cached token
 FP8_MAX = 448.0               # largest finite E4M3 value
@@ -201,12 +201,27 @@ def cache_insert_fp8(cache_u8: np.ndarray, kv_a_bits: np.ndarray, w_bits: np.nda
     return out
 
 
-def decode_expanded_fp8(q_bits, kv_b_bits, cache_u8, block_table, seq_lens, q_len, **kw):
+def decode_expanded_fp8(q_bits, kv_b_bits, cache_u8, block_table, seq_lens, q_len, *,
+                        batches=None, **kw):
     """MLA decode over the FP8 cache: the expanded-form oracle
     (``decode_expanded``) on the dequantised entries (codes times the token's
-    scale, exact in float64; rope bf16 widened exactly)."""
-    return decode_expanded(q_bits, kv_b_bits, dequantize_cache(cache_u8), block_table,
-                           seq_lens, q_len, **kw)
+    scale, exact in float64; rope bf16 widened exactly).
+
+    Only the pages of the requested sequences are dequantised (the same
+    entries, gathered into a smaller cache through a renumbered block table),
+    so sampled checks at full size stay cheap."""
+    bsz = q_bits.shape[0]
+    batches = list(range(bsz)) if batches is None else list(batches)
+    page = cache_u8.shape[1]
+    need = [np.asarray(block_table[b, :(int(seq_lens[b]) + page - 1) // page], dtype=np.int64)
+            for b in batches]
+    used = np.unique(np.concatenate(need)) if need else np.zeros(0, dtype=np.int64)
+    compact = dequantize_cache(cache_u8[used])
+    bt = np.zeros((bsz, max(1, block_table.shape[1])), dtype=np.int64)
+    for b, blocks in zip(batches, need):
+        bt[b, :len(blocks)] = np.searchsorted(used, blocks)
+    return decode_expanded(q_bits, kv_b_bits, compact, bt, seq_lens, q_len, batches=batches,
+                           **kw)
 
 
 __all__ = ["FP8_ROW_BYTES", "FP8_MAX", "e4m3_decode", "e4m3_encode", "scale_exponent",
