@@ -12,6 +12,12 @@ Prints ONE JSON line.  ``value`` is KV-cache bytes streamed per second
 HBM; ``roofline`` reports the split-KV decode kernel alone, timed with HIP
 events recorded by the library on the launch stream; ``cpu_baseline`` times the
 float64 oracle on a bounded sample of the same workload.
+
+``--cache fp8`` runs the same step over the FP8 latent cache
+(mla_cache_insert_fp8 + mla_decode_fp8; 656-byte rows, see include/mla.h):
+``value`` and the roofline then count 656 bytes per cached position, and the
+CPU baseline times the FP8 oracle.  The FP8 cache is filled from the same
+synthetic latent rows (times 2^6, cast to E4M3 by torch; scale byte 2^-6).
 """
 from __future__ import annotations
 
@@ -36,6 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--cache", choices=("bf16", "fp8"), default="bf16",
+                    help="cache format of the step (bf16: the headline; fp8: the FP8 latent cache)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
@@ -50,35 +58,48 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(d, budget_s: float) -> dict:
+def cpu_baseline(d, budget_s: float, fp8_cache=None) -> dict:
     """Time the float64 oracle (insert + expanded-form decode) sequence by
-    sequence until the budget is spent; scale to KV GB/s like the GPU figure."""
+    sequence until the budget is spent; scale to KV GB/s like the GPU figure.
+    fp8_cache: the FP8 cache (numpy uint8) to run the FP8 oracle on instead."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import cache_insert, decode_expanded
+    from oracle import fp8 as ofp8
     import workloads as wl
 
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     eps = float(np.float32(wl.EPS))
     t0 = time.perf_counter()
-    ref_cache = cache_insert(d["cache"], d["kv_a"], d["rms_w"], d["block_table"], d["seq_lens"],
-                             d["q_len"], eps, wl.ROPE_BASE, wl.LATENT)
+    if fp8_cache is None:
+        ref_cache = cache_insert(d["cache"], d["kv_a"], d["rms_w"], d["block_table"],
+                                 d["seq_lens"], d["q_len"], eps, wl.ROPE_BASE, wl.LATENT)
+        row_bytes = wl.BYTES_PER_TOKEN
+    else:
+        ref_cache = ofp8.cache_insert_fp8(fp8_cache, d["kv_a"], d["rms_w"], d["block_table"],
+                                          d["seq_lens"], d["q_len"], eps, wl.ROPE_BASE)
+        row_bytes = ofp8.FP8_ROW_BYTES
     t_insert = time.perf_counter() - t0
     done, tokens, t_dec = 0, 0, 0.0
     while done < d["batch"] and t_dec < budget_s:
         t1 = time.perf_counter()
-        decode_expanded(d["q"], d["kv_b"], ref_cache, d["block_table"], d["seq_lens"], d["q_len"],
-                        batches=[done])
+        if fp8_cache is None:
+            decode_expanded(d["q"], d["kv_b"], ref_cache, d["block_table"], d["seq_lens"],
+                            d["q_len"], batches=[done])
+        else:
+            ofp8.decode_expanded_fp8(d["q"], d["kv_b"], ref_cache, d["block_table"],
+                                     d["seq_lens"], d["q_len"], batches=[done])
         t_dec += time.perf_counter() - t1
         tokens += int(d["seq_lens"][done])
         done += 1
     # insert cost is for the whole batch; charge the sampled share of it
     t = t_dec + t_insert * done / d["batch"]
-    return {"value": round(tokens * wl.BYTES_PER_TOKEN / t / 1e9, 4), "unit": "GB/s",
+    return {"value": round(tokens * row_bytes / t / 1e9, 4), "unit": "GB/s",
             "tokens_per_s": round(done * d["q_len"] / t, 3), "cores": threads, "kind": "oracle",
             "sample": f"{done} of {d['batch']} sequences ({tokens} cached positions, all "
                       f"{d['heads']} heads) of {d['name']}: float64 expanded-form decode plus "
-                      f"its share of the insert, {t:.1f} s"}
+                      f"its share of the insert{' (FP8 cache)' if fp8_cache is not None else ''}"
+                      f", {t:.1f} s"}
 
 
 def main():
@@ -106,9 +127,25 @@ def main():
                      device="cuda")
     eps = float(np.float32(wl.EPS))
 
+    fp8 = args.cache == "fp8"
+    row_bytes = mla.FP8_ROW_BYTES if fp8 else wl.BYTES_PER_TOKEN
+    if fp8:
+        # FP8 rows from the same synthetic latent rows: x * 2^6 cast to E4M3 by
+        # torch, scale byte 127 - 6, rope bf16 bytes, zero padding
+        lat = torch.nan_to_num(cache[..., :wl.LATENT].float(), nan=0.0, posinf=0.0, neginf=0.0)
+        codes = (lat * 64.0).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+        rope = torch.nan_to_num(cache[..., wl.LATENT:].float(), nan=0.0).to(torch.bfloat16)
+        rope = rope.contiguous().view(torch.uint8)
+        tail = torch.zeros((*codes.shape[:2], mla.FP8_ROW_BYTES - 640), dtype=torch.uint8,
+                           device="cuda")
+        tail[..., 0] = 127 - 6
+        cache = torch.cat([codes, rope, tail], dim=-1).contiguous()
+        del lat, codes, rope, tail
+        torch.cuda.synchronize()
+
     def step():
-        mla.cache_insert(kv_a, rms_w, bt, sl, cache, eps=eps, heads=heads)
-        mla.decode(q, kv_b, cache, bt, sl, max_len, out=out, workspace=ws)
+        mla.cache_insert(kv_a, rms_w, bt, sl, cache, eps=eps, heads=heads, fp8=fp8)
+        mla.decode(q, kv_b, cache, bt, sl, max_len, out=out, workspace=ws, fp8=fp8)
 
     for _ in range(args.warmup):
         step()
@@ -143,7 +180,7 @@ def main():
     mla.profile_enable(0)
     assert calls == args.steps
     ms_step = wall * 1e3 / args.steps
-    kv_bytes = int(seq_lens.sum()) * wl.BYTES_PER_TOKEN
+    kv_bytes = int(seq_lens.sum()) * row_bytes
     alg_bytes = wl.decode_bytes(seq_lens, bsz, q_len, heads, bt.numel())
     alg_flops = wl.decode_flops(seq_lens, bsz, q_len, heads)
     dec_ms = stage_ms["decode"] / calls
@@ -151,7 +188,8 @@ def main():
     traffic = None
     if os.path.exists(args.traffic):
         tr = json.load(open(args.traffic))
-        if tr.get("workload") == args.workload and tr.get("kernel_source_sha") == kernel_sha():
+        if (tr.get("workload") == args.workload and tr.get("kernel_source_sha") == kernel_sha()
+                and tr.get("cache", "bf16") == args.cache):
             traffic = tr.get("bytes_per_launch")
     result = {
         "metric": "MLA decode KV-cache GB/s & tokens/s at V3 shape; % of HBM roofline",
@@ -164,7 +202,7 @@ def main():
         "config": {"workload": args.workload, "batch": bsz, "q_len": q_len, "heads": heads,
                    "context": "8192 each" if args.workload == WORKLOAD else "see workloads.py",
                    "page": 64, "kv_lora": 512, "rope": 64, "step": "cache_insert + decode",
-                   "launch": "eager" if args.eager else "hip graph"},
+                   "cache": args.cache, "launch": "eager" if args.eager else "hip graph"},
         "tokens_per_s": round(bsz * q_len / (ms_step * 1e-3), 1),
         "alg_bytes_per_step": alg_bytes,
         "alg_flops_per_step": alg_flops,
@@ -173,7 +211,8 @@ def main():
         "roofline": {"kernel": "mla::decode_kernel (split-KV decode)", "bound": "hbm",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "per_unit": "1152 B per cached position (576 bf16)",
+                     "per_unit": ("656 B per cached position (FP8 row)" if fp8 else
+                                  "1152 B per cached position (576 bf16)"),
                      "units_per_launch": int(seq_lens.sum()),
                      "mfma_tflops": round(2 * heads * wl.visible_pairs(seq_lens, q_len)
                                           * (wl.ENTRY + wl.LATENT) / (dec_ms * 1e-3) / 1e12, 1),
@@ -188,7 +227,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+        fp8_host = cache.cpu().numpy() if fp8 else None
+        result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds, fp8_host)
     print(json.dumps(result), flush=True)
 
 
