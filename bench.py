@@ -53,9 +53,15 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the run, one plain device-to-device copy of this many MiB "
                          "(reference dispatch for scaling HBM byte counters)")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "decode_kernel_traffic.json"),
-                    help="HBM traffic of the decode kernel measured with rocprofv3 counters")
-    return ap.parse_args()
+    ap.add_argument("--traffic", default=None,
+                    help="HBM traffic of the decode kernel measured with rocprofv3 counters "
+                         "(default: profiles/decode_kernel_traffic.json, or "
+                         "profiles/decode_fp8_kernel_traffic.json with --cache fp8)")
+    args = ap.parse_args()
+    if args.traffic is None:
+        name = "decode_fp8_kernel_traffic.json" if args.cache == "fp8" else "decode_kernel_traffic.json"
+        args.traffic = os.path.join(ROOT, "profiles", name)
+    return args
 
 
 def cpu_baseline(d, budget_s: float, fp8_cache=None) -> dict:
