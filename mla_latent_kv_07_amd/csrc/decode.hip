@@ -81,67 +81,79 @@ constexpr float kSlackPow = 65536.0f;          // 2^16: headroom above the refer
 // Encoding of "s_waitcnt vmcnt(n)" (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// Copies of one chunk of CB bytes: 1 KB per wavefront-wide instruction.
-template <int NW, int CB = kBufBytes>
+// Copies of one chunk: 1 KB per wavefront-wide instruction.
+//   bf16: the chunk's 36 KB is dealt to the wavefronts round robin (copy i of
+//         wavefront w fills LDS bytes 1024 (i NW + w) ..); the chunk is read
+//         by every wavefront, after a barrier.
+//   FP8:  wavefront w copies rows w RW .. w RW + RW - 1 of the chunk (RW =
+//         32 / NW) into a region of its own, the only rows it later expands,
+//         so its own wait on the copies is all the expansion needs.
+template <int NW, bool FP8>
 struct Dma {
-  static constexpr int kInsts = (CB + 1023) / 1024;  // 36 for a bf16 chunk, 21 for FP8
-  // every wavefront issues the same number of copies; when the count does not
-  // split evenly the last ones are out of range (no memory access) and land
-  // in the slot's padding
-  static constexpr int kPerWave = (kInsts + NW - 1) / NW;
+  static constexpr int kWaveBytes = (kChunk / NW) * kFp8EntryBytes;  // FP8 rows of a wavefront
+  // copies per wavefront; when the count does not split evenly the last ones
+  // are out of range (no memory access) and land in the slot's padding
+  static constexpr int kPerWave = FP8 ? (kWaveBytes + 1023) / 1024 : (kBufBytes / 1024 + NW - 1) / NW;
   static constexpr int kSlotBytes = kPerWave * NW * 1024;
+  static constexpr int kStride = FP8 ? 1024 : NW * 1024;      // LDS distance of a wavefront's copies
+  static constexpr int kWaveBase = FP8 ? kPerWave * 1024 : 1024;  // LDS offset of wavefront w: w * this
 };
-// bytes of one chunk in the cache format: 32 rows
-template <bool FP8>
-constexpr int chunk_bytes() { return kChunk * (FP8 ? kFp8EntryBytes : kEntryBytes); }
 
 // Piece permutation inside each aligned group of 8 pieces of row r.
 __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 3) << 1) ^ (((r >> 3) & 1) * 7); }
 
-// Per-lane source offsets of the wavefront's copies of one chunk.  Copy k
-// fills LDS pieces 64k .. 64k+63 (lane L -> piece Q = 64k + L, i.e. row Q / 72,
-// slot Q % 72) from piece (Q % 72) ^ swz(row) of that row: the 64 lanes read
-// the same contiguous 1 KB of the chunk, permuted within 128-byte lines.  The
-// offsets are the same for every chunk (a chunk is 36 KB of contiguous cache:
-// half a page), so they are computed once.
-// FP8 chunks are copied as they are (lane L of copy k reads bytes
-// 1024k + 16L ..), then expanded into the bf16 layout (dequant_chunk).
-template <int NW, int KP, bool FP8 = false>
+// Per-lane source offsets of the wavefront's copies of one chunk.
+// bf16: copy k = i NW + wave fills LDS pieces 64k .. 64k+63 (lane L -> piece
+// Q = 64k + L, i.e. row Q / 72, slot Q % 72) from piece (Q % 72) ^ swz(row) of
+// that row: the 64 lanes read the same contiguous 1 KB of the chunk, permuted
+// within 128-byte lines.  The offsets are the same for every chunk (a chunk
+// is 36 KB of contiguous cache: half a page), so they are computed once.
+// FP8: copy i reads bytes 1024 i + 16 L of the wavefront's rows as they are
+// (expanded into the bf16 layout later, by dequant_rows).
+template <int NW, int KP, bool FP8>
 __device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&off)[KP]) {
+  using D = Dma<NW, FP8>;
 #pragma unroll
   for (int i = 0; i < KP; ++i) {
-    const int k = i * NW + wave;
-    const int q = 64 * k + lane;
-    const int row = q / kChunk16;
-    const int col = q - row * kChunk16;
-    const uint32_t o = FP8 ? (uint32_t)(16 * q)
-                           : (uint32_t)(row * kEntryBytes + 16 * (col ^ swz(row)));
-    off[i] = k < Dma<NW, chunk_bytes<FP8>()>::kInsts ? o : 0x80000000u;  // beyond any range
+    if constexpr (FP8) {
+      const int o = 1024 * i + 16 * lane;
+      off[i] = o < D::kWaveBytes ? (uint32_t)(wave * D::kWaveBytes + o) : 0x80000000u;
+    } else {
+      const int k = i * NW + wave;
+      const int q = 64 * k + lane;
+      const int row = q / kChunk16;
+      const int col = q - row * kChunk16;
+      off[i] = k < kBufBytes / 1024 ? (uint32_t)(row * kEntryBytes + 16 * (col ^ swz(row)))
+                                    : 0x80000000u;  // beyond any range
+    }
   }
 }
 
-// Expand an FP8 chunk (32 rows of kFp8EntryBytes at `src`) into the bf16
-// chunk layout the compute reads (1152-byte rows, 16-byte pieces permuted by
-// swz): each group of 8 latent codes becomes 8 bf16 values times the row's
-// power-of-two scale (exact: 4 significant bits), the rope part is copied.
-// Rows past the sequence end arrive as zeros and expand to zeros.
+// Expand the wavefront's FP8 rows of a chunk (RW = 32 / NW rows of
+// kFp8EntryBytes in its region of the ring slot `src`, see Dma) into the
+// bf16 chunk layout the compute reads (1152-byte rows, 16-byte pieces
+// permuted by swz): each group of 8 latent codes becomes 8 bf16 values times
+// the row's power-of-two scale (exact: 4 significant bits), the rope part is
+// copied.  Rows past the sequence end arrive as zeros and expand to zeros.
+// Lane L expands code group L of every row (a contiguous 512-byte read per
+// row across the wavefront).
 template <int NW>
-__device__ __forceinline__ void dequant_chunk(const MLA_LDS char* src, MLA_LDS char* dst,
-                                              int tid) {
-  constexpr int T = NW * 64;
-  // the per-thread offsets below are the same for every chunk: recompute them
+__device__ __forceinline__ void dequant_rows(const MLA_LDS char* src, MLA_LDS char* dst, int wave,
+                                             int lane) {
+  using D = Dma<NW, true>;
+  constexpr int RW = kChunk / NW;
+  // the per-lane offsets below are the same for every chunk: recompute them
   // here rather than let them stay live across the whole chunk loop
-  asm volatile("" : "+v"(tid));
+  asm volatile("" : "+v"(lane));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const MLA_LDS char* rows = src + wave * D::kWaveBase;
 #pragma unroll
-  for (int k = 0; k < (kChunk * 64) / T; ++k) {  // latent: (row, 8-code group)
-    const int task = k * T + tid;
-    const int r = task >> 6;
-    const int c = task & 63;
-    const MLA_LDS char* row = src + r * kFp8EntryBytes;
-    const u32x2 codes = *reinterpret_cast<const MLA_LDS u32x2*>(row + 8 * c);
+  for (int k = 0; k < RW; ++k) {
+    const int r = wave * RW + k;  // row in the chunk
+    const MLA_LDS char* row = rows + k * kFp8EntryBytes;
+    const u32x2 codes = *reinterpret_cast<const MLA_LDS u32x2*>(row + 8 * lane);
     const uint32_t sb = *reinterpret_cast<const MLA_LDS unsigned char*>(row + kFp8ScaleOff);
     const float scale = __uint_as_float(sb << 23);  // 2^(sb - 127); only its exponent is used
     const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], scale, false);
@@ -149,16 +161,17 @@ __device__ __forceinline__ void dequant_chunk(const MLA_LDS char* src, MLA_LDS c
     const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], scale, false);
     const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], scale, true);
     const bf16x8 v = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-    *reinterpret_cast<MLA_LDS bf16x8*>(dst + r * kEntryBytes + 16 * (c ^ swz(r))) = v;
+    *reinterpret_cast<MLA_LDS bf16x8*>(dst + r * kEntryBytes + 16 * (lane ^ swz(r))) = v;
   }
 #pragma unroll
-  for (int k = 0; k < (kChunk * 8 + T - 1) / T; ++k) {  // rope: (row, 16-byte piece)
-    const int task = k * T + tid;
-    if (task < kChunk * 8) {
-      const int r = task >> 3;
+  for (int t = 0; t < (RW * 8 + 63) / 64; ++t) {  // rope: (row, 16-byte piece)
+    const int task = t * 64 + lane;
+    if (RW * 8 % 64 == 0 || task < RW * 8) {
+      const int k = task >> 3;
       const int c = task & 7;
-      const u32x4 v = *reinterpret_cast<const MLA_LDS u32x4*>(src + r * kFp8EntryBytes +
-                                                               kFp8RopeOff + 16 * c);
+      const int r = wave * RW + k;
+      const u32x4 v =
+          *reinterpret_cast<const MLA_LDS u32x4*>(rows + k * kFp8EntryBytes + kFp8RopeOff + 16 * c);
       *reinterpret_cast<MLA_LDS u32x4*>(dst + r * kEntryBytes + 16 * ((64 + c) ^ swz(r))) = v;
     }
   }
@@ -172,21 +185,23 @@ constexpr int kRsrcWord3 = 0x00020000;
 // query, the partial rows, kv_b).
 constexpr int kCopyPolicy = 2;
 
-// Copy instructions I0 .. I1-1 of the wavefront's share of one chunk (36 KB
-// at `src`, a wavefront-uniform address) into the LDS ring slot `buf`
-// (wavefront-uniform): buffer loads straight to LDS, with the chunk as the
-// buffer (scalar descriptor) and a 32-bit per-lane offset.  The buffer range
-// is `bytes`: lanes beyond it read no memory and write zeros to LDS (checked
-// per dword).  A partial last chunk thus arrives zero-padded, and `bytes` = 0
-// gives an empty copy with the same instruction count.
-template <int NW, int I0, int I1>
+// Copy instructions I0 .. I1-1 of the wavefront's share of one chunk (at
+// `src`, a wavefront-uniform address) into the LDS ring slot `buf`
+// (wavefront-uniform; layout of the copies in D): buffer loads straight to
+// LDS, with the chunk as the buffer (scalar descriptor) and a 32-bit per-lane
+// offset.  The buffer range is `bytes`: lanes beyond it read no memory and
+// write zeros to LDS (checked per dword).  A partial last chunk thus arrives
+// zero-padded, and `bytes` = 0 gives an empty copy with the same instruction
+// count.
+// (WB, ST: Dma::kWaveBase, Dma::kStride)
+template <int WB, int ST, int I0, int I1>
 __device__ __forceinline__ void load_chunk(MLA_LDS char* buf, const char* src, int bytes,
                                            const uint32_t* off, int wave) {
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, bytes, kRsrcWord3);
 #pragma unroll
   for (int i = I0; i < I1; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, buf + (i * NW + wave) * 1024, 16, off[i], 0, 0,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, buf + wave * WB + i * ST, 16, off[i], 0, 0,
                                              kCopyPolicy);
 }
 
@@ -202,11 +217,12 @@ struct ChunkCopy {
 };
 
 // Copy instruction i of the wavefront's share of a chunk (see load_chunk).
-template <int NW>
+// (WB, ST: Dma::kWaveBase, Dma::kStride)
+template <int WB, int ST>
 __device__ __forceinline__ void copy_piece(const ChunkCopy& c, const uint32_t* off, int i,
                                            int wave) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, c.dst + (i * NW + wave) * 1024, 16, off[i], 0,
-                                           0, kCopyPolicy);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, c.dst + wave * WB + i * ST, 16, off[i], 0, 0,
+                                           kCopyPolicy);
 }
 
 // Score k-step at which copy c of NC goes out: spread evenly over the first
@@ -237,7 +253,7 @@ __device__ __forceinline__ void score_schedule() {
 // path takes roughly 15 cycles per 1 KB copy, and a wavefront that issues
 // copies faster than that stalls, so they go out one at a time between
 // MFMAs instead of all at once.
-template <int NH, int NW, int NC>
+template <int NH, class D, int NC>
 __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_even,
                                             int sbase_odd, const bf16x8 (&qreg)[NH][18],
                                             f32x4 (&sacc)[NH][2], const ChunkCopy& cc,
@@ -268,7 +284,7 @@ __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_e
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      if (copy_step(c, NC, 18 - KPD) == ks) copy_piece<NW>(cc, off, c, wave);
+      if (copy_step(c, NC, 18 - KPD) == ks) copy_piece<D::kWaveBase, D::kStride>(cc, off, c, wave);
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const bf16x8 qb = qreg[h][ks];
@@ -338,20 +354,24 @@ __device__ __forceinline__ bool softmax_chunk(f32x4 (&sacc)[NH][2], bf16x8 (&pk)
 // feature tiles of the slice and all G = NW*NH row groups of the workgroup,
 // O^T[g][f] += V^T[f] P^T[g].  pb[g] is the B operand of row group g.  V^T
 // comes from the chunk through the transposing read; feature tile f of the
-// slice sits at vbase[f & 3] + 128*(f >> 2) + slice_off.
+// slice sits at vbase[f & 3] + 128*(f >> 2) (vbase includes the slice).
 template <int NW, int NH>
 __device__ __forceinline__ void pv_slice(const MLA_LDS char* buf, const int (&vbase)[4],
-                                         int slice_off, const bf16x8 (&pb)[NW * NH],
+                                         const bf16x8 (&pb)[NW * NH],
                                          f32x4 (&oacc)[NW * NH][32 / NW]) {
   constexpr int G = NW * NH;
   constexpr int FT = 32 / NW;
   bf16x8 vb[FT];
 #pragma unroll
   for (int f = 0; f < FT; ++f) {
-    const MLA_LDS char* p = buf + vbase[f & 3] + 128 * (f >> 2) + slice_off;
-    const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p);
+    // one variable offset per read plus constants: the address stays a
+    // short chain of offsets from the LDS array, short enough for the
+    // compiler to keep track of which array it reads (and so of which copies
+    // in flight it must wait for)
+    const int o = vbase[f & 3] + 128 * (f >> 2);
+    const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(buf + o));
     const bf16x4 a1 =
-        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(p + 16 * kEntryBytes));
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(buf + (o + 16 * kEntryBytes)));
     vb[f] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 #pragma unroll
@@ -405,25 +425,28 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 // FP8: the cache holds FP8 rows; each chunk lands in the ring in that form
-// and is expanded into the staging chunk (bf16 layout) before the compute.
+// and every wavefront expands its own rows of it into a bf16 staging chunk
+// while the chunk before it is multiplied (double-buffered staging).
 template <int NW, int NH, bool FP8>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
                                                          const int32_t* __restrict__ block_table) {
   constexpr int G = NW * NH;   // 16-row groups of the workgroup
   constexpr int FT = 32 / NW;  // feature tiles of a wavefront's P.V slice
   constexpr int kRowBytes = FP8 ? kFp8EntryBytes : kEntryBytes;  // cache bytes per position
-  using D = Dma<NW, chunk_bytes<FP8>()>;
-  // The ring: four chunk slots, each its own array.  Chunk j lives in slot
-  // j % 4, and the chunk loop is unrolled by four so that every access names
-  // its slot at compile time: the compiler then knows that the copies in
-  // flight (into the other slots) never alias the slot being read and adds
-  // no wait of its own on them.
+  using D = Dma<NW, FP8>;
+  // The ring: NS chunk slots (bf16: 4; FP8: 3 next to the two staging
+  // chunks), each its own array.  Chunk j lives in slot j % NS, and the chunk
+  // loop is unrolled by NS so that every access names its slot at compile
+  // time: the compiler then knows that the copies in flight (into the other
+  // slots) never alias the slot being read and adds no wait of its own on
+  // them.
+  constexpr int NS = FP8 ? 3 : 4;
   __shared__ __attribute__((aligned(1024))) char ring0[D::kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char ring1[D::kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char ring2[D::kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) char ring3[D::kSlotBytes];
-  // FP8: the chunk being computed, expanded to bf16
-  __shared__ __attribute__((aligned(1024))) char stage[FP8 ? kBufBytes : 16];
+  __shared__ __attribute__((aligned(1024))) char ring3[FP8 ? 16 : D::kSlotBytes];
+  // FP8: chunks j (read by the compute) and j + 1 (being expanded), bf16 layout
+  __shared__ __attribute__((aligned(1024))) char stage[FP8 ? 2 * kBufBytes : 16];
   // probabilities of the chunk, one 1 KB B-operand tile per row group
   __shared__ __attribute__((aligned(1024))) char pbuf[G * 1024];
   // row sums at the end
@@ -435,10 +458,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     else if constexpr (S == 2) return (MLA_LDS char*)ring2;
     else return (MLA_LDS char*)ring3;
   };
-  // the bf16 chunk the compute reads for slot S
-  auto cbuf = [&](auto slot_c) -> MLA_LDS char* {
-    if constexpr (FP8) return (MLA_LDS char*)stage;
-    else return ring(slot_c);
+  // FP8: the staging chunk of chunk j.  The offset is made opaque so that
+  // every access stays a plain offset from `stage` (not a select or phi of
+  // two pointers): the compiler then still tells it apart from the ring
+  // slots the copies in flight write, and adds no wait on them.
+  auto stage_of = [&](int j) -> MLA_LDS char* {
+    int off = (j & 1) * kBufBytes;
+    asm volatile("" : "+s"(off));
+    return (MLA_LDS char*)stage + off;
   };
   MLA_LDS char* pb_lds = (MLA_LDS char*)pbuf;
 
@@ -487,12 +514,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     const int qq = lane & 3;
     const int row = 4 * gq + r4;
     const int y = (qq >> 1) ^ swz(row);
+    // this wavefront's feature slice: tiles wave*FT .. +FT (FT is a multiple
+    // of 4), folded into the bases (kept as one value each: see pv_slice)
+    const int slice_off = 32 * wave * FT;
 #pragma unroll
-    for (int f4 = 0; f4 < 4; ++f4)
-      vbase[f4] = row * kEntryBytes + 16 * ((2 * f4) ^ y) + 8 * (qq & 1);
+    for (int f4 = 0; f4 < 4; ++f4) {
+      vbase[f4] = row * kEntryBytes + 16 * ((2 * f4) ^ y) + 8 * (qq & 1) + slice_off;
+      asm volatile("" : "+v"(vbase[f4]));
+    }
   }
-  // this wavefront's feature slice: tiles wave*FT .. +FT (FT is a multiple of 4)
-  const int slice_off = 32 * wave * FT;
 
   // the absorbed query rows, in registers for the whole item: lane holds
   // features 32ks + 8gq .. +8 of row n (the B operand of k-step ks)
@@ -532,35 +562,32 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   constexpr int kPer = D::kPerWave;
   uint32_t doff[kPer];
   dma_offsets<NW, kPer, FP8>(wave, lane, doff);
-  // Every interval issues exactly one copy (an empty one past the item's
-  // end), so "chunk j has landed" is always "at most two copies pending":
-  // one wait count for every chunk, which the compiler can follow and so adds
-  // no conservative full drain of its own.
+  // Every interval issues exactly one chunk's copies (empty ones past the
+  // item's end), so "chunk j has landed" is always the same count of copies
+  // pending: one wait count for every chunk, which the compiler can follow
+  // and so adds no conservative full drain of its own.
   // The last chunk of the sequence may end inside the chunk: its copy reads
   // only the valid rows, the others arrive as zeros (never the NaN sentinels
   // or stale data of the slots beyond the sequence end).
-  auto chunk_copy = [&](auto slot_c, int j) -> ChunkCopy {
+  auto chunk_src = [&](int j, int& bytes) -> const char* {
     const bool real = j < nchunks;
     const int t = tok_begin + (real ? j : 0) * kChunk;
     const int64_t blk = bt[t / kPage];
-    const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kRowBytes;
-    const int bytes = real ? min(tok_end - t, kChunk) * kRowBytes : 0;
+    bytes = real ? min(tok_end - t, kChunk) * kRowBytes : 0;
+    return cache + (blk * kPage + (t % kPage)) * (int64_t)kRowBytes;
+  };
+  auto chunk_copy = [&](auto slot_c, int j) -> ChunkCopy {
+    int bytes;
+    const char* src = chunk_src(j, bytes);
     return ChunkCopy{
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, bytes, kRsrcWord3),
         ring(slot_c)};
   };
-  // copy instructions I0 .. I1-1 of chunk j into its slot
-  auto issue_part = [&](auto slot_c, int j, auto i0_c, auto i1_c) {
-    const bool real = j < nchunks;
-    const int t = tok_begin + (real ? j : 0) * kChunk;
-    const int64_t blk = bt[t / kPage];
-    const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kRowBytes;
-    const int bytes = real ? min(tok_end - t, kChunk) * kRowBytes : 0;
-    load_chunk<NW, decltype(i0_c)::value, decltype(i1_c)::value>(ring(slot_c), src, bytes, doff,
-                                                                   wave);
-  };
+  // all copy instructions of chunk j into its slot
   auto issue = [&](auto slot_c, int j) {
-    issue_part(slot_c, j, std::integral_constant<int, 0>{}, std::integral_constant<int, kPer>{});
+    int bytes;
+    const char* src = chunk_src(j, bytes);
+    load_chunk<D::kWaveBase, D::kStride, 0, kPer>(ring(slot_c), src, bytes, doff, wave);
   };
   // visibility limit of chunk j for this lane, relative to its slot 16t + i
   auto chunk_limits = [&](int j, int (&lim)[NH]) {
@@ -568,19 +595,23 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
 #pragma unroll
     for (int h = 0; h < NH; ++h) lim[h] = tmax[h] - t0 - 4 * gq;
   };
-  // One chunk: scores and softmax of this wavefront's rows, the probabilities
-  // to LDS, a barrier, then the P.V of all the workgroup's rows for this
-  // wavefront's feature slice.  Returns the restart verdict of its rows.
-  // (NC > 0: the copies of `cc` go out during the score phase)
-  auto compute = [&](auto slot_c, auto first_c, auto nc_c, int j, const ChunkCopy& cc) -> bool {
+  // One chunk (bf16 layout at `buf`): scores and softmax of this wavefront's
+  // rows, the probabilities to LDS, a barrier, then the P.V of all the
+  // workgroup's rows for this wavefront's feature slice.  Returns the restart
+  // verdict of its rows.  (NC > 0: the copies of `cc` go out during the score
+  // phase; DQ: the wavefront's FP8 rows at `dq_src` are expanded into `dq_dst`
+  // during the P.V phase.)
+  auto compute = [&](const MLA_LDS char* buf, auto first_c, auto nc_c, auto dq_c, int j,
+                     const ChunkCopy& cc, const MLA_LDS char* dq_src,
+                     MLA_LDS char* dq_dst) __attribute__((always_inline)) -> bool {
     constexpr bool kFirst = decltype(first_c)::value;
     int lim[NH];
     chunk_limits(j, lim);
     f32x4 sacc[NH][2];
     // the phases stay in order: moving the next phase's LDS reads up would
     // keep their registers live across this one
-    score_chunk<NH, NW, decltype(nc_c)::value>(cbuf(slot_c), sbase_even, sbase_odd, qreg, sacc,
-                                               cc, doff, wave);
+    score_chunk<NH, D, decltype(nc_c)::value>(buf, sbase_even, sbase_odd, qreg, sacc, cc, doff,
+                                              wave);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 pk[NH];
     bool need;
@@ -597,55 +628,83 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     for (int g = 0; g < G; ++g)
       pb[g] = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_lds + g * 1024 + lane * 16);
     __builtin_amdgcn_sched_barrier(0);
-    pv_slice<NW, NH>(cbuf(slot_c), vbase, slice_off, pb, oacc);
+    pv_slice<NW, NH>(buf, vbase, pb, oacc);
+    if constexpr (decltype(dq_c)::value) {
+      // the rows to expand have landed once at most the copies of the two
+      // chunks after them are pending
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
+      dequant_rows<NW>(dq_src, dq_dst, wave, lane);
+    }
     __builtin_amdgcn_sched_barrier(0);
     return need;
   };
 
   // ---- main pass: reference = the first chunk's max per row ----------------
-  // While chunk j is computed, chunks j+1 and j+2 are in flight and chunk j+3
-  // goes into chunk j-1's slot once every wavefront is past chunk j-1; its
-  // copies run inside the score phase of chunk j (or on their own for a step
-  // past the item's end).
-  // After chunk 0 the chunks run in groups of four (slots 1, 2, 3, 0); a
-  // group may reach past the item's end, and such steps still wait, pass the
-  // barrier and issue their (empty) copy but skip the compute.  No vector
-  // memory instruction sits in a conditional, so on every path the compiler
-  // sees the same copies pending.
+  // bf16: while chunk j is computed, chunks j+1 and j+2 are in flight and
+  // chunk j+3 goes into chunk j-1's slot once every wavefront is past chunk
+  // j-1; its copies run inside the score phase of chunk j.
+  // FP8: chunk j was expanded into its staging chunk during the P.V of chunk
+  // j-1; chunk j+3 goes into chunk j's ring slot (this wavefront expanded its
+  // rows of it already), and chunk j+1 is expanded during the P.V of chunk j.
+  // The chunks run in groups of NS; a group may reach past the item's end,
+  // and such steps still pass the barrier and issue their (empty) copies but
+  // skip the compute.  No vector memory instruction sits in a conditional,
+  // so on every path the compiler sees the same copies pending.
   // (a wavefront that needs a restart keeps going with a useless result;
   // the verdict is taken once, after the pass)
   using T = std::true_type;
   using F = std::false_type;
+  using NoCopy = std::integral_constant<int, 0>;
+  using AllCopies = std::integral_constant<int, kPer>;
   bool need_restart = false;
-  auto interval = [&](auto slot_c, auto first_c, int j) {
+  auto interval = [&](auto slot_c, auto first_c, int j) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_c)::value;
-    // chunk j has landed once at most the copies of chunks j+1, j+2 are pending
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
-    ring_barrier();
     if constexpr (FP8) {
-      // every wavefront is past chunk j-1, so the staging chunk is free
-      dequant_chunk<NW>(ring(slot_c), (MLA_LDS char*)stage, threadIdx.x);
+      // every wavefront's rows of chunk j are in its staging chunk, and every
+      // wavefront is past chunk j-1 (whose staging chunk takes chunk j+1)
       ring_barrier();
-    }
-    // chunk j+3 goes into chunk j-1's slot: every wavefront is past it
-    const ChunkCopy cc = chunk_copy(Slot<(S + 3) & 3>{}, j + 3);
-    if (j < nchunks) {
-      need_restart |= compute(slot_c, first_c, std::integral_constant<int, kPer>{}, j, cc);
-    } else {
+      const ChunkCopy cc = chunk_copy(slot_c, j + 3);
+      if (j < nchunks) {
+        need_restart |= compute(stage_of(j), first_c, AllCopies{}, T{}, j, cc,
+                                ring(Slot<(S + 1) % NS>{}), stage_of(j + 1));
+      } else {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) copy_piece<NW>(cc, doff, i, wave);
+        for (int i = 0; i < kPer; ++i) copy_piece<D::kWaveBase, D::kStride>(cc, doff, i, wave);
+      }
+    } else {
+      // chunk j has landed once at most the copies of chunks j+1, j+2 are pending
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
+      ring_barrier();
+      // chunk j+3 goes into chunk j-1's slot: every wavefront is past it
+      const ChunkCopy cc = chunk_copy(Slot<(S + 3) & 3>{}, j + 3);
+      if (j < nchunks) {
+        need_restart |= compute(ring(slot_c), first_c, AllCopies{}, F{}, j, cc, nullptr, nullptr);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) copy_piece<D::kWaveBase, D::kStride>(cc, doff, i, wave);
+      }
     }
   };
   // (an item always has at least one chunk)
   issue(Slot<0>{}, 0);
   issue(Slot<1>{}, 1);
   issue(Slot<2>{}, 2);
-  interval(Slot<0>{}, T{}, 0);
-  for (int j = 1; j < nchunks; j += 4) {
-    interval(Slot<1>{}, F{}, j);
-    interval(Slot<2>{}, F{}, j + 1);
-    interval(Slot<3>{}, F{}, j + 2);
-    interval(Slot<0>{}, F{}, j + 3);
+  if constexpr (FP8) {
+    dequant_rows<NW>(ring(Slot<0>{}), stage_of(0), wave, lane);
+    interval(Slot<0>{}, T{}, 0);
+    for (int j = 1; j < nchunks; j += 3) {
+      interval(Slot<1>{}, F{}, j);
+      interval(Slot<2>{}, F{}, j + 1);
+      interval(Slot<0>{}, F{}, j + 2);
+    }
+  } else {
+    interval(Slot<0>{}, T{}, 0);
+    for (int j = 1; j < nchunks; j += 4) {
+      interval(Slot<1>{}, F{}, j);
+      interval(Slot<2>{}, F{}, j + 1);
+      interval(Slot<3>{}, F{}, j + 2);
+      interval(Slot<0>{}, F{}, j + 3);
+    }
   }
   // every wavefront's verdict, then one decision for the workgroup
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -657,24 +716,29 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   const bool restart = __atomic_load_n(flag, __ATOMIC_RELAXED) != 0;
 
   // ---- restart (rare): exact row max, then a pass with it as the reference --
-  // one chunk at a time through slot 0
+  // one chunk at a time through slot 0 (FP8: expanded into staging chunk 0)
   if (restart) {
+    auto fetch = [&](int j) -> const MLA_LDS char* {
+      issue(Slot<0>{}, j);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      if constexpr (FP8) {
+        dequant_rows<NW>(ring(Slot<0>{}), stage_of(0), wave, lane);
+        __syncthreads();
+        return stage_of(0);
+      } else {
+        __syncthreads();
+        return ring(Slot<0>{});
+      }
+    };
     float m_exact[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) m_exact[h] = -INFINITY;
     for (int j = 0; j < nchunks; ++j) {
-      issue(Slot<0>{}, j);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      __syncthreads();
-      if constexpr (FP8) {
-        dequant_chunk<NW>(ring(Slot<0>{}), (MLA_LDS char*)stage, threadIdx.x);
-        __syncthreads();
-      }
+      const MLA_LDS char* buf = fetch(j);
       int lim[NH];
       chunk_limits(j, lim);
       f32x4 sacc[NH][2];
-      score_chunk<NH, NW, 0>(cbuf(Slot<0>{}), sbase_even, sbase_odd, qreg, sacc, ChunkCopy{},
-                             doff, wave);
+      score_chunk<NH, D, 0>(buf, sbase_even, sbase_odd, qreg, sacc, ChunkCopy{}, doff, wave);
       max_chunk<NH>(sacc, m_exact, lim);
       __syncthreads();
     }
@@ -688,14 +752,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
 #pragma unroll
       for (int f = 0; f < FT; ++f) oacc[g][f] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < nchunks; ++j) {
-      issue(Slot<0>{}, j);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      __syncthreads();
-      if constexpr (FP8) {
-        dequant_chunk<NW>(ring(Slot<0>{}), (MLA_LDS char*)stage, threadIdx.x);
-        __syncthreads();
-      }
-      compute(Slot<0>{}, F{}, std::integral_constant<int, 0>{}, j, ChunkCopy{});
+      const MLA_LDS char* buf = fetch(j);
+      compute(buf, F{}, NoCopy{}, F{}, j, ChunkCopy{}, nullptr, nullptr);
       __syncthreads();
     }
   }
