@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark: MLA decode KV-cache GB/s and tokens/s at the DeepSeek-V3 shape.
 
-One step = the whole hot path over one batch: mla_cache_insert of the new
-token(s) (kv_a RMSNorm + RoPE + paged write) followed by mla_decode (query
-absorption, split-KV decode, merge + per-head projection).  Workload: batch
+One step = the whole hot path over one batch: the insert of the new token(s)
+(kv_a RMSNorm + RoPE + paged write), RoPE on q_pe and the query absorption
+(one launch), split-KV decode, merge + per-head projection: mla_decode_step.
+``--path separate`` times mla_cache_insert + mla_decode instead (q_pe arrives
+rotated; four launches).  Workload: batch
 64, q_len 1, 128 heads, every context 8192 positions, 64-position pages in a
 random block order, seeded synthetic bf16 data (see workloads.py).
 
@@ -44,6 +46,9 @@ def parse():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--cache", choices=("bf16", "fp8"), default="bf16",
                     help="cache format of the step (bf16: the headline; fp8: the FP8 latent cache)")
+    ap.add_argument("--path", choices=("step", "separate"), default="step",
+                    help="step: mla_decode_step (insert and query preparation fused); "
+                         "separate: mla_cache_insert then mla_decode")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
@@ -64,13 +69,14 @@ def parse():
     return args
 
 
-def cpu_baseline(d, budget_s: float, fp8_cache=None) -> dict:
-    """Time the float64 oracle (insert + expanded-form decode) sequence by
-    sequence until the budget is spent; scale to KV GB/s like the GPU figure.
-    fp8_cache: the FP8 cache (numpy uint8) to run the FP8 oracle on instead."""
+def cpu_baseline(d, budget_s: float, fp8_cache=None, rotate: bool = True) -> dict:
+    """Time the float64 oracle (insert, RoPE of q_pe when ``rotate``, and the
+    expanded-form decode) sequence by sequence until the budget is spent;
+    scale to KV GB/s like the GPU figure.  fp8_cache: the FP8 cache (numpy
+    uint8) to run the FP8 oracle on instead."""
     import numpy as np
     from threadpoolctl import threadpool_info
-    from oracle import cache_insert, decode_expanded
+    from oracle import cache_insert, decode_expanded, rotate_q
     from oracle import fp8 as ofp8
     import workloads as wl
 
@@ -85,15 +91,16 @@ def cpu_baseline(d, budget_s: float, fp8_cache=None) -> dict:
         ref_cache = ofp8.cache_insert_fp8(fp8_cache, d["kv_a"], d["rms_w"], d["block_table"],
                                           d["seq_lens"], d["q_len"], eps, wl.ROPE_BASE)
         row_bytes = ofp8.FP8_ROW_BYTES
+    q = rotate_q(d["q"], d["seq_lens"], d["q_len"], wl.ROPE_BASE, wl.NOPE) if rotate else d["q"]
     t_insert = time.perf_counter() - t0
     done, tokens, t_dec = 0, 0, 0.0
     while done < d["batch"] and t_dec < budget_s:
         t1 = time.perf_counter()
         if fp8_cache is None:
-            decode_expanded(d["q"], d["kv_b"], ref_cache, d["block_table"], d["seq_lens"],
+            decode_expanded(q, d["kv_b"], ref_cache, d["block_table"], d["seq_lens"],
                             d["q_len"], batches=[done])
         else:
-            ofp8.decode_expanded_fp8(d["q"], d["kv_b"], ref_cache, d["block_table"],
+            ofp8.decode_expanded_fp8(q, d["kv_b"], ref_cache, d["block_table"],
                                      d["seq_lens"], d["q_len"], batches=[done])
         t_dec += time.perf_counter() - t1
         tokens += int(d["seq_lens"][done])
@@ -104,7 +111,8 @@ def cpu_baseline(d, budget_s: float, fp8_cache=None) -> dict:
             "tokens_per_s": round(done * d["q_len"] / t, 3), "cores": threads, "kind": "oracle",
             "sample": f"{done} of {d['batch']} sequences ({tokens} cached positions, all "
                       f"{d['heads']} heads) of {d['name']}: float64 expanded-form decode plus "
-                      f"its share of the insert{' (FP8 cache)' if fp8_cache is not None else ''}"
+                      f"its share of the insert{' and q RoPE' if rotate else ''}"
+                      f"{' (FP8 cache)' if fp8_cache is not None else ''}"
                       f", {t:.1f} s"}
 
 
@@ -150,15 +158,19 @@ def main():
         torch.cuda.synchronize()
 
     def step():
-        mla.cache_insert(kv_a, rms_w, bt, sl, cache, eps=eps, heads=heads, fp8=fp8)
-        mla.decode(q, kv_b, cache, bt, sl, max_len, out=out, workspace=ws, fp8=fp8)
+        if args.path == "step":
+            mla.decode_step(q, kv_a, rms_w, kv_b, cache, bt, sl, max_len, eps=eps, out=out,
+                            workspace=ws, fp8=fp8)
+        else:
+            mla.cache_insert(kv_a, rms_w, bt, sl, cache, eps=eps, heads=heads, fp8=fp8)
+            mla.decode(q, kv_b, cache, bt, sl, max_len, out=out, workspace=ws, fp8=fp8)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     run = step
     if not args.eager:
-        # the step (insert + decode: four kernels) captured once as a HIP
+        # the step (three kernels; four with --path separate) captured once as a HIP
         # graph and replayed, as a serving loop would; the library allocates
         # nothing and records no memset, so the graph is replay-safe
         graph = torch.cuda.CUDAGraph()
@@ -207,7 +219,9 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "batch": bsz, "q_len": q_len, "heads": heads,
                    "context": "8192 each" if args.workload == WORKLOAD else "see workloads.py",
-                   "page": 64, "kv_lora": 512, "rope": 64, "step": "cache_insert + decode",
+                   "page": 64, "kv_lora": 512, "rope": 64, "step": ("mla_decode_step: insert + q_pe RoPE + absorption in one launch, "
+                            "decode, combine" if args.path == "step" else
+                            "mla_cache_insert + mla_decode"),
                    "cache": args.cache, "launch": "eager" if args.eager else "hip graph"},
         "tokens_per_s": round(bsz * q_len / (ms_step * 1e-3), 1),
         "alg_bytes_per_step": alg_bytes,
@@ -234,7 +248,8 @@ def main():
         del src, dst
     if not args.no_cpu:
         fp8_host = cache.cpu().numpy() if fp8 else None
-        result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds, fp8_host)
+        result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds, fp8_host,
+                                              rotate=args.path == "step")
     print(json.dumps(result), flush=True)
 
 

@@ -170,12 +170,51 @@ int mla_decode_fp8(const mla_dims* dims, const void* q, const void* kv_b, const 
                    int32_t num_splits_hint, void* stream);
 
 /*
+ * mla_decode_step / mla_decode_step_fp8 — one decoding step with the
+ * query-side work fused into the insert (the vLLM DeepSeek-V4 notes, section
+ * 一: RoPE of the query, KV quantisation and cache insert in one kernel;
+ * "深度解读DeepSeek：源码解读 DeepSeek-V3", section MLA: the new tokens'
+ * entries are cached before attention and q_pe is rotated at the same
+ * positions as k_pe).  Equivalent to
+ *   mla_cache_insert[_fp8](dims, kv_a, rms_w, eps, rope_base, block_table,
+ *                          bt_stride, seq_lens, batch, q_len, cache, ...)
+ *   q' = q with each head's q_pe rotated at position seq_lens[b] - q_len + i
+ *        (the rotation of the insert: interleaved pairs, angle
+ *        position * rope_base^(-2j/64), computed in double, rounded once to
+ *        bf16)
+ *   mla_decode[_fp8](dims, q', kv_b, cache, ...)
+ * with bit-identical cache contents and output, in three launches on
+ * `stream` instead of four (the insert, the RoPE of q_pe, the query
+ * absorption and the split plan share one launch).
+ *   q      bf16 [B, q_len, H, 192], q_pe part NOT rotated; read only
+ *   kv_a, rms_w, eps, rope_base: as mla_cache_insert
+ *   cache  read and written (the q_len new rows of every sequence)
+ *   every other argument, the workspace size and the errors: as mla_decode
+ *   (the insert's arguments are checked as mla_cache_insert checks them).
+ */
+int mla_decode_step(const mla_dims* dims, const void* q, const void* kv_a, const void* rms_w,
+                    float eps, float rope_base, const void* kv_b, void* cache,
+                    int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                    const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t max_seq_len,
+                    float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                    int32_t num_splits_hint, void* stream);
+int mla_decode_step_fp8(const mla_dims* dims, const void* q, const void* kv_a,
+                        const void* rms_w, float eps, float rope_base, const void* kv_b,
+                        void* cache, int32_t num_blocks, const int32_t* block_table,
+                        int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
+                        int32_t q_len, int32_t max_seq_len, float softmax_scale, void* out,
+                        void* workspace, size_t workspace_bytes, int32_t num_splits_hint,
+                        void* stream);
+
+/*
  * mla_profile_enable / mla_profile_collect — stage timing for benchmarks.
- * While enabled (max_calls > 0), each mla_decode / mla_decode_fp8 call records
+ * While enabled (max_calls > 0), each mla_decode / mla_decode_fp8 /
+ * mla_decode_step / mla_decode_step_fp8 call records
  * four HIP events
  * on its stream: before the prep kernel (query absorption + split plan),
  * before the split-KV decode kernel, before the merge + projection kernel, and
- * after it.  Events come from a pool of max_calls sets created here
+ * after it (for the step entry points the first stage also holds the
+insert).  Events come from a pool of max_calls sets created here
  * (hipEventCreate; no device memory); calls beyond the pool are not timed.
  * mla_profile_enable(0) releases the pool.  mla_profile_collect waits for the
  * recorded events and writes, per stage, the summed milliseconds over the

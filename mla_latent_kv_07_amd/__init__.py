@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     abi_version,
     cache_insert,
     decode,
+    decode_step,
     decode_workspace_bytes,
     lib_path,
     load,

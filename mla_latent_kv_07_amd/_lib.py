@@ -56,6 +56,11 @@ def load() -> ctypes.CDLL:
     lib.mla_cache_insert_fp8.restype = ctypes.c_int
     lib.mla_decode_fp8.argtypes = lib.mla_decode.argtypes
     lib.mla_decode_fp8.restype = ctypes.c_int
+    lib.mla_decode_step.argtypes = [DP, P, P, P, F, F, P, P, I32, P, I32, P, I32, I32, I32, F, P,
+                                    P, SZ, I32, P]
+    lib.mla_decode_step.restype = ctypes.c_int
+    lib.mla_decode_step_fp8.argtypes = lib.mla_decode_step.argtypes
+    lib.mla_decode_step_fp8.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_profile_enable.argtypes = [I32]
@@ -176,6 +181,45 @@ def decode(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, *,
             _ptr(out), _ptr(workspace), workspace.numel(), num_splits_hint, _stream(stream))
     if st != 0:
         raise MLAError(st, "mla_decode_fp8" if fp8 else "mla_decode")
+    return out
+
+
+def decode_step(q, kv_a, rms_w, kv_b, cache, block_table, seq_lens, max_seq_len: int, *,
+                eps: float = 1e-6, rope_base: float = 10000.0,
+                softmax_scale: float | None = None, out=None, workspace=None,
+                num_splits_hint: int = 0, stream=None, fp8: bool = False):
+    """mla_decode_step (fp8=False) or mla_decode_step_fp8 (fp8=True): the
+    insert of kv_a bf16 [B, q_len, 576] into the cache, RoPE on q's q_pe (q
+    bf16 [B, q_len, H, 192], q_pe NOT rotated) and the decode, in three
+    launches; returns out bf16 [B, q_len, H, 128].  The cache is updated in
+    place."""
+    import torch
+    bsz, q_len, heads = q.shape[0], q.shape[1], q.shape[2]
+    dev = cache.device
+    _check(q, "q", torch.bfloat16, (bsz, q_len, heads, NOPE + ROPE), dev)
+    _check(kv_a, "kv_a", torch.bfloat16, (bsz, q_len, LATENT + ROPE), dev)
+    _check(rms_w, "rms_w", torch.bfloat16, (LATENT,), dev)
+    _check(kv_b, "kv_b", torch.bfloat16, (heads * (NOPE + VDIM), LATENT), dev)
+    _check_cache(cache, fp8, dev)
+    _check(block_table, "block_table", torch.int32, None, dev)
+    _check(seq_lens, "seq_lens", torch.int32, (bsz,), dev)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(NOPE + ROPE)
+    if out is None:
+        out = torch.empty((bsz, q_len, heads, VDIM), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (bsz, q_len, heads, VDIM), dev)
+    need = decode_workspace_bytes(heads, bsz, q_len, max_seq_len, num_splits_hint)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    d = dims(heads)
+    fn = load().mla_decode_step_fp8 if fp8 else load().mla_decode_step
+    st = fn(ctypes.byref(d), _ptr(q), _ptr(kv_a), _ptr(rms_w), eps, rope_base, _ptr(kv_b),
+            _ptr(cache), cache.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+            bsz, q_len, max_seq_len, softmax_scale, _ptr(out), _ptr(workspace), workspace.numel(),
+            num_splits_hint, _stream(stream))
+    if st != 0:
+        raise MLAError(st, "mla_decode_step_fp8" if fp8 else "mla_decode_step")
     return out
 
 

@@ -8,6 +8,7 @@
 #include <mutex>
 #include <vector>
 
+#include "insert_dev.h"
 #include "mla.h"
 #include "mla_common.h"
 
@@ -205,11 +206,13 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t q
 
 namespace {
 
-int decode_any(bool fp8, const mla_dims* dims, const void* q, const void* kv_b,
-               const void* cache, int32_t num_blocks, const int32_t* block_table,
-               int32_t bt_stride, const int32_t* seq_lens, int32_t batch, int32_t q_len,
-               int32_t max_seq_len, float softmax_scale, void* out, void* workspace,
-               size_t workspace_bytes, int32_t num_splits_hint, void* stream) {
+// ins != nullptr: the fused step (insert of the new tokens and RoPE on q_pe
+// in the query-preparation launch); ins->cache is `cache`.
+int decode_any(bool fp8, const InsertArgs* ins, const mla_dims* dims, const void* q,
+               const void* kv_b, const void* cache, int32_t num_blocks,
+               const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+               int32_t batch, int32_t q_len, int32_t max_seq_len, float softmax_scale, void* out,
+               void* workspace, size_t workspace_bytes, int32_t num_splits_hint, void* stream) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (batch < 0 || batch > kMaxBatch || q_len < 1 || q_len > kMaxQLen || max_seq_len < q_len ||
@@ -248,10 +251,15 @@ int decode_any(bool fp8, const mla_dims* dims, const void* q, const void* kv_b,
   prof_mark(pc, 0, s);
   // the absorbed query carries softmax_scale * log2(e): scores come out of the
   // matrix cores in log2 units
-  hipError_t e = launch_prep(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_b),
-                             heads, batch * q_len, softmax_scale * 1.4426950408889634f, q_abs,
-                             seq_lens, batch, max_pages, L.slots, L.max_items, num_splits_hint,
-                             item_cost, plan, s);
+  const float q_scale = softmax_scale * 1.4426950408889634f;
+  hipError_t e =
+      ins ? launch_prep_step(fp8, *ins, static_cast<const uint16_t*>(q),
+                             static_cast<const uint16_t*>(kv_b), heads, batch * q_len, q_scale,
+                             q_abs, seq_lens, batch, max_pages, L.slots, L.max_items,
+                             num_splits_hint, item_cost, plan, s)
+          : launch_prep(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_b),
+                        heads, batch * q_len, q_scale, q_abs, seq_lens, batch, max_pages,
+                        L.slots, L.max_items, num_splits_hint, item_cost, plan, s);
   prof_mark(pc, 1, s);
   if (e == hipSuccess)
     e = launch_decode(L.cfg, fp8, q_abs, cache, block_table, bt_stride,
@@ -273,9 +281,9 @@ int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void
                const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t max_seq_len,
                float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
                int32_t num_splits_hint, void* stream) {
-  return decode_any(false, dims, q, kv_b, cache, num_blocks, block_table, bt_stride, seq_lens,
-                    batch, q_len, max_seq_len, softmax_scale, out, workspace, workspace_bytes,
-                    num_splits_hint, stream);
+  return decode_any(false, nullptr, dims, q, kv_b, cache, num_blocks, block_table, bt_stride,
+                    seq_lens, batch, q_len, max_seq_len, softmax_scale, out, workspace,
+                    workspace_bytes, num_splits_hint, stream);
 }
 
 int mla_decode_fp8(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
@@ -283,9 +291,51 @@ int mla_decode_fp8(const mla_dims* dims, const void* q, const void* kv_b, const 
                    const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t max_seq_len,
                    float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
                    int32_t num_splits_hint, void* stream) {
-  return decode_any(true, dims, q, kv_b, cache, num_blocks, block_table, bt_stride, seq_lens,
-                    batch, q_len, max_seq_len, softmax_scale, out, workspace, workspace_bytes,
-                    num_splits_hint, stream);
+  return decode_any(true, nullptr, dims, q, kv_b, cache, num_blocks, block_table, bt_stride,
+                    seq_lens, batch, q_len, max_seq_len, softmax_scale, out, workspace,
+                    workspace_bytes, num_splits_hint, stream);
+}
+
+namespace {
+
+int step_any(bool fp8, const mla_dims* dims, const void* q, const void* kv_a, const void* rms_w,
+             float eps, float rope_base, const void* kv_b, void* cache, int32_t num_blocks,
+             const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+             int32_t batch, int32_t q_len, int32_t max_seq_len, float softmax_scale, void* out,
+             void* workspace, size_t workspace_bytes, int32_t num_splits_hint, void* stream) {
+  if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(rope_base) || rope_base <= 0.f)
+    return MLA_ERR_SHAPE;
+  if (batch > 0 && (!kv_a || !rms_w)) return MLA_ERR_NULL;
+  const InsertArgs ins{static_cast<const uint16_t*>(kv_a), static_cast<const uint16_t*>(rms_w),
+                       (double)eps, (double)rope_base, block_table, bt_stride, seq_lens, q_len,
+                       cache};
+  return decode_any(fp8, &ins, dims, q, kv_b, cache, num_blocks, block_table, bt_stride,
+                    seq_lens, batch, q_len, max_seq_len, softmax_scale, out, workspace,
+                    workspace_bytes, num_splits_hint, stream);
+}
+
+}  // namespace
+
+int mla_decode_step(const mla_dims* dims, const void* q, const void* kv_a, const void* rms_w,
+                    float eps, float rope_base, const void* kv_b, void* cache, int32_t num_blocks,
+                    const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                    int32_t batch, int32_t q_len, int32_t max_seq_len, float softmax_scale,
+                    void* out, void* workspace, size_t workspace_bytes, int32_t num_splits_hint,
+                    void* stream) {
+  return step_any(false, dims, q, kv_a, rms_w, eps, rope_base, kv_b, cache, num_blocks,
+                  block_table, bt_stride, seq_lens, batch, q_len, max_seq_len, softmax_scale, out,
+                  workspace, workspace_bytes, num_splits_hint, stream);
+}
+
+int mla_decode_step_fp8(const mla_dims* dims, const void* q, const void* kv_a, const void* rms_w,
+                        float eps, float rope_base, const void* kv_b, void* cache,
+                        int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                        const int32_t* seq_lens, int32_t batch, int32_t q_len,
+                        int32_t max_seq_len, float softmax_scale, void* out, void* workspace,
+                        size_t workspace_bytes, int32_t num_splits_hint, void* stream) {
+  return step_any(true, dims, q, kv_a, rms_w, eps, rope_base, kv_b, cache, num_blocks,
+                  block_table, bt_stride, seq_lens, batch, q_len, max_seq_len, softmax_scale, out,
+                  workspace, workspace_bytes, num_splits_hint, stream);
 }
 
 }  // extern "C"

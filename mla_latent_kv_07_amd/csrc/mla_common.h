@@ -78,6 +78,15 @@ hipError_t launch_prep(const uint16_t* q, const uint16_t* kv_b, int heads, int r
                        int slots, int max_items, int splits_hint, float item_cost_pages,
                        PlanView plan, hipStream_t stream);
 
+// the fused step: the same, plus the insert of the new tokens (bf16 or FP8
+// cache) and RoPE on q_pe (which arrives unrotated); qabsorb.hip
+struct InsertArgs;
+hipError_t launch_prep_step(bool fp8, const InsertArgs& ia, const uint16_t* q,
+                            const uint16_t* kv_b, int heads, int rows, float q_scale,
+                            uint16_t* q_abs, const int32_t* seq_lens, int batch, int max_pages,
+                            int slots, int max_items, int splits_hint, float item_cost_pages,
+                            PlanView plan, hipStream_t stream);
+
 struct DecodeConfig {
   int waves;    // wavefronts per workgroup
   int heads_per_wave;  // 16-row groups per wavefront

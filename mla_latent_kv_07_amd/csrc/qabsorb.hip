@@ -9,12 +9,19 @@
 //
 // The same launch also makes the split plan (plan.h) in its first workgroup
 // (dispatched first), so the planner's latency hides under the absorption.
+// In the fused step (the insert and the query preparation in one launch, as
+// the vLLM DeepSeek-V4 notes, section 一, fuse the query-side RoPE with the
+// cache insert) the launch also writes the new tokens' cache entries
+// (insert_dev.h, one wavefront per token), and the same wavefront rotates
+// the token's q_pe of every head: the angles are those of the token's own
+// k_pe, computed once per token.
 //
 // One workgroup per (head, 128 latent columns); W_UK[h][:, cols] (32 KB) is
 // staged in LDS and read as the MFMA A operand with the gfx950 transposing
 // LDS read (the contraction index d is W_UK's row index).  The query rows are
 // the B operand, straight from global memory.  Result rows are written with
 // 8-byte stores (4 consecutive latent columns per lane).
+#include "insert_dev.h"
 #include "mla_common.h"
 #include "plan.h"
 
@@ -26,20 +33,88 @@ constexpr int kQaStride = kQaCols * 2 + 32;  // padded LDS row of W_UK (bytes)
 constexpr int kPrepSmem = kNope * kQaStride > kPlanSmemBytes ? kNope * kQaStride : kPlanSmemBytes;
 static_assert(kPlanThreads == 256, "the plan runs on one 256-thread workgroup");
 
+// MODE 0: q_pe arrives rotated.  MODE 1 / 2: the fused step with the bf16 /
+// FP8 cache: q_pe arrives unrotated, and the new tokens are inserted.
 // Block 0: the split plan (independent work, hidden under the absorption).
-// Blocks 1 .. 4H: absorption of head (b-1)/4, latent columns ((b-1)%4)*128 .. +128.
+// Blocks 1 .. n_ins (MODE > 0): one per new token, its insert and q_pe.
+// Then 4H blocks: absorption of head k/4, latent columns (k%4)*128 .. +128.
+// q_abs's rope part of heads h0 .. h0 + 2 kQpeBatch - 1 (those below `heads`)
+// of query row `token`: q_pe rotated at the token's position (each head's 32
+// pairs by the 32 angles of that position, as rope_pair), times q_scale,
+// rounded to bf16.  Lane L handles pair L % 32 of heads h0 + L / 32 + 2u.
+// The pairs are loaded first (load_query_pe), so their latency is paid once.
+constexpr int kQpeBatch = 16;
+static_assert(4 * 2 * kQpeBatch >= 128, "four wavefronts cover every head (heads <= 128)");
+struct QueryPe {
+  uint32_t pair[kQpeBatch];
+};
+
+__device__ __forceinline__ void load_query_pe(const uint16_t* __restrict__ q, int heads,
+                                              int token, int lane, int h0, QueryPe& qp) {
+  const int j = lane & 31;
+#pragma unroll
+  for (int u = 0; u < kQpeBatch; ++u) {
+    const int h = h0 + (lane >> 5) + 2 * u;
+    const int64_t row = (int64_t)token * heads + min(h, heads - 1);
+    qp.pair[u] = *reinterpret_cast<const uint32_t*>(q + row * kQk + kNope + 2 * j);
+  }
+}
+
+__device__ __forceinline__ void rotate_query_pe(const QueryPe& qp, int heads, float q_scale,
+                                                uint16_t* __restrict__ q_abs,
+                                                const InsertArgs& ia, int token, int lane,
+                                                int h0) {
+  const int b = token / ia.q_len;
+  const int pos = ia.seq_lens[b] - ia.q_len + (token - b * ia.q_len);
+  const int j = lane & 31;
+  double c, s;
+  rope_angle(pos, j, ia.rope_base, c, s);
+#pragma unroll
+  for (int u = 0; u < kQpeBatch; ++u) {
+    const int h = h0 + (lane >> 5) + 2 * u;
+    if (h < heads) {
+      const int64_t row = (int64_t)token * heads + h;
+      const uint32_t rot = rotate_pair(qp.pair[u], c, s);
+      const uint32_t lo = f32_to_bf16(bf16_to_f32((uint16_t)(rot & 0xffffu)) * q_scale);
+      const uint32_t hi = f32_to_bf16(bf16_to_f32((uint16_t)(rot >> 16)) * q_scale);
+      *reinterpret_cast<uint32_t*>(q_abs + row * kEntry + kLatent + 2 * j) = lo | (hi << 16);
+    }
+  }
+}
+
+template <int MODE>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ kv_b, int heads,
                                                    int rows, float q_scale,
-                                                   uint16_t* __restrict__ q_abs, PlanArgs pa) {
+                                                   uint16_t* __restrict__ q_abs, PlanArgs pa,
+                                                   InsertArgs ia, int n_ins) {
   __shared__ __attribute__((aligned(16))) char smem[kPrepSmem];
   if (blockIdx.x == 0) {
     plan_block(pa, (MLA_LDS char*)smem);
     return;
   }
+  if (MODE > 0 && (int)blockIdx.x <= n_ins) {
+    // one workgroup per new token: wavefront w rotates q_pe of heads
+    // w * 2 kQpeBatch .. (heads <= 128), wavefront 0 also inserts the token
+    const int token = blockIdx.x - 1;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int h0 = wave * 2 * kQpeBatch;
+    QueryPe qp;
+    if (h0 < heads) load_query_pe(q, heads, token, lane, h0, qp);
+    if (wave == 0) {
+      if (MODE == 1)
+        insert_token_bf16(ia, token, lane);
+      else
+        insert_token_fp8(ia, token, lane);
+    }
+    if (h0 < heads) rotate_query_pe(qp, heads, q_scale, q_abs, ia, token, lane, h0);
+    return;
+  }
   MLA_LDS char* w_lds = (MLA_LDS char*)smem;
-  const int h = (blockIdx.x - 1) / (kLatent / kQaCols);
-  const int nc = (blockIdx.x - 1) % (kLatent / kQaCols);  // column chunk
+  const int blk = blockIdx.x - 1 - (MODE > 0 ? n_ins : 0);
+  const int h = blk / (kLatent / kQaCols);
+  const int nc = blk % (kLatent / kQaCols);  // column chunk
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -76,8 +151,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
     const int p = k * 256 + tid;
     *reinterpret_cast<MLA_LDS u16x8*>(w_lds + (p >> 4) * kQaStride + (p & 15) * 16) = wst[k];
   }
-  // q_pe times the scale (done once per head, by column chunk 0)
-  if (nc == 0) {
+  // q_pe times the scale (done once per head, by column chunk 0; in the
+  // fused step the insert wavefronts write it, rotated)
+  if (MODE == 0 && nc == 0) {
     for (int p = tid; p < rows * 8; p += 256) {
       const int r = p >> 3;
       const int j = p & 7;
@@ -140,8 +216,25 @@ hipError_t launch_prep(const uint16_t* q, const uint16_t* kv_b, int heads, int r
                        int slots, int max_items, int splits_hint, float item_cost_pages,
                        PlanView plan, hipStream_t stream) {
   PlanArgs pa{seq_lens, batch, max_pages, slots, max_items, splits_hint, item_cost_pages, plan};
-  hipLaunchKernelGGL(prep_kernel, dim3(heads * (kLatent / kQaCols) + 1), dim3(256), 0, stream, q,
-                     kv_b, heads, rows, q_scale, q_abs, pa);
+  hipLaunchKernelGGL(prep_kernel<0>, dim3(heads * (kLatent / kQaCols) + 1), dim3(256), 0, stream,
+                     q, kv_b, heads, rows, q_scale, q_abs, pa, InsertArgs{}, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_step(bool fp8, const InsertArgs& ia, const uint16_t* q,
+                            const uint16_t* kv_b, int heads, int rows, float q_scale,
+                            uint16_t* q_abs, const int32_t* seq_lens, int batch, int max_pages,
+                            int slots, int max_items, int splits_hint, float item_cost_pages,
+                            PlanView plan, hipStream_t stream) {
+  PlanArgs pa{seq_lens, batch, max_pages, slots, max_items, splits_hint, item_cost_pages, plan};
+  const int n_ins = rows;  // one workgroup per new token
+  const dim3 grid(1 + n_ins + heads * (kLatent / kQaCols));
+  if (fp8)
+    hipLaunchKernelGGL(prep_kernel<2>, grid, dim3(256), 0, stream, q, kv_b, heads, rows, q_scale,
+                       q_abs, pa, ia, n_ins);
+  else
+    hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(256), 0, stream, q, kv_b, heads, rows, q_scale,
+                       q_abs, pa, ia, n_ins);
   return hipGetLastError();
 }
 

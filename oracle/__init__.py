@@ -13,6 +13,7 @@ from .mla_oracle import (  # noqa: F401
     rmsnorm_bf16,
     rope_pairs_f64,
     rope_bf16,
+    rotate_q,
     cache_insert,
     decode_expanded,
     decode_absorbed,

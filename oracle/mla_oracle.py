@@ -30,7 +30,8 @@ Readings where the pages are silent (each is listed in the design doc):
 * softmax scale = 1/sqrt(qk_nope + qk_rope) (= 1/sqrt(192)) in both forms;
 * RoPE rotates interleaved pairs (2j, 2j+1) as complex numbers, frequency
   base**(-2j/rope), angle = position * frequency, position = 0-based cache
-  index; k_pe is rotated, q_pe arrives already rotated;
+  index; k_pe is rotated; q_pe arrives already rotated for the decode, and
+  the fused step (``rotate_q``) rotates it at its own token's position;
 * RMSNorm: eps inside the square root, two bf16 roundings (normalised value,
   then weight * value);
 * cache entry = latent (first) then rope part, one paged tensor
@@ -134,6 +135,24 @@ def rope_pairs_f64(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
 def rope_bf16(x_bits: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     """RoPE on bf16 input, one rounding of the rotated value back to bf16."""
     return f64_to_bf16_bits(rope_pairs_f64(bf16_bits_to_f64(x_bits), pos, base))
+
+
+def rotate_q(q_bits: np.ndarray, seq_lens: np.ndarray, q_len: int, rope_base: float,
+             nope: int) -> np.ndarray:
+    """q [B, q_len, H, nope + rope] (uint16 bf16 bits) with every head's rope
+    part rotated, one rounding to bf16; the nope part is returned unchanged.
+
+    [V3-src] the query branch of ``MLA.forward`` applies ``apply_rotary_emb``
+    to q_pe with the same ``freqs_cis`` rows as k_pe, those of the current
+    positions start_pos ..: new query i of a sequence whose post-insert length
+    is L sits at position L - q_len + i, the position its own k_pe is cached
+    at.
+    """
+    out = np.array(q_bits, dtype=np.uint16, copy=True)
+    for b in range(q_bits.shape[0]):
+        pos = int(seq_lens[b]) - q_len + np.arange(q_len)
+        out[b, :, :, nope:] = rope_bf16(q_bits[b, :, :, nope:], pos[:, None], rope_base)
+    return out
 
 
 def cache_insert(cache_bits: np.ndarray, kv_a_bits: np.ndarray, w_bits: np.ndarray,
