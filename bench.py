@@ -116,6 +116,108 @@ def cpu_baseline(d, budget_s: float, fp8_cache=None, rotate: bool = True) -> dic
                       f", {t:.1f} s"}
 
 
+def prefill_cpu_baseline(d, budget_s: float) -> dict:
+    """The float64 oracle (expanded form) on one (sequence, head) at a time
+    until the budget is spent; scaled to tokens/s of the whole batch (every
+    head of every sequence costs about the same)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import decode_expanded
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    done, t = 0, 0.0
+    pairs = [(b, h) for h in range(d["heads"]) for b in range(d["batch"])]
+    while done < len(pairs) and t < budget_s:
+        b, h = pairs[done]
+        t0 = time.perf_counter()
+        decode_expanded(d["q"], d["kv_b"], d["cache_ref"], d["block_table"], d["seq_lens"],
+                        d["q_len"], batches=[b], heads=[h])
+        t += time.perf_counter() - t0
+        done += 1
+    per_pair = t / done
+    total = per_pair * len(pairs)
+    return {"value": round(d["batch"] * d["q_len"] / total, 3), "unit": "tokens/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (sequence, head) pairs of {d['name']} through the "
+                      f"float64 expanded-form oracle ({t:.1f} s), scaled to all pairs"}
+
+
+def prefill_main(args):
+    """Prefill in the expanded form: one step = the insert of every new token
+    (mla_cache_insert) and mla_prefill (expansion of K/V, causal attention).
+    value = new tokens per second; roofline = the attention kernel against the
+    bf16 matrix-core peak."""
+    import numpy as np
+    import torch
+    import mla_latent_kv_07_amd as mla
+    import workloads as wl
+
+    d = wl.make_workload(args.workload)
+    bsz, q_len, heads = d["batch"], d["q_len"], d["heads"]
+    seq_lens = d["seq_lens"]
+    max_len = int(seq_lens.max())
+    to = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+                    if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda())
+    cache, kv_a, rms_w = to(d["cache"]), to(d["kv_a"]), to(d["rms_w"])
+    q, kv_b = to(d["q"]), to(d["kv_b"])
+    bt, sl = to(d["block_table"]), to(d["seq_lens"])
+    out = torch.empty((bsz, q_len, heads, wl.VDIM), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.prefill_workspace_bytes(heads, bsz, max_len), dtype=torch.uint8,
+                     device="cuda")
+    eps = float(np.float32(wl.EPS))
+
+    def step():
+        mla.cache_insert(kv_a, rms_w, bt, sl, cache, eps=eps, heads=heads)
+        mla.prefill(q, kv_b, cache, bt, sl, max_len, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mla.profile_enable(args.steps)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    stage_ms, calls = mla.profile_collect()
+    mla.profile_enable(0)
+    ms_step = wall * 1e3 / args.steps
+    exp_flops, att_flops = wl.prefill_flops(seq_lens, q_len, heads)
+    exp_ms = stage_ms["prep"] / calls
+    att_ms = stage_ms["decode"] / calls
+    att_tfs = att_flops / (att_ms * 1e-3) / 1e12
+    result = {
+        "metric": "MLA prefill (expanded form) new tokens/s at V3 shape; % of bf16 MFMA roofline",
+        "value": round(bsz * q_len / (ms_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": bsz, "q_len": q_len, "heads": heads,
+                   "context": "see workloads.py", "page": 64, "kv_lora": 512, "rope": 64,
+                   "step": "mla_cache_insert (all new tokens) + mla_prefill",
+                   "launch": "eager"},
+        "alg_flops_per_step": exp_flops + att_flops,
+        "step_tflops": round((exp_flops + att_flops) / (ms_step * 1e-3) / 1e12, 1),
+        "stage_ms": {"expand": round(exp_ms, 4), "attention": round(att_ms, 4)},
+        "expand_tflops": round(exp_flops / (exp_ms * 1e-3) / 1e12, 1),
+        "roofline": {"kernel": "mla::prefill_attn_kernel (causal attention, 192/128 heads)",
+                     "bound": "mfma", "achieved": round(att_tfs, 1),
+                     "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(att_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                     "per_unit": "2 x (192 + 128) flops per head and visible (query, key) pair",
+                     "units_per_launch": int(heads * wl.visible_pairs(seq_lens, q_len))},
+    }
+    if not args.no_cpu:
+        from oracle import cache_insert
+        d["cache_ref"] = cache_insert(d["cache"], d["kv_a"], d["rms_w"], d["block_table"],
+                                      d["seq_lens"], q_len, eps, wl.ROPE_BASE, wl.LATENT)
+        result["cpu_baseline"] = prefill_cpu_baseline(d, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -127,6 +229,8 @@ def main():
     import workloads as wl
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload in wl.PREFILL:
+        return prefill_main(args)
     d = wl.make_workload(args.workload)
     bsz, q_len, heads = d["batch"], d["q_len"], d["heads"]
     seq_lens = d["seq_lens"]

@@ -29,7 +29,9 @@
  *     caller's contract and are not checked: every used block id must lie in
  *     [0, num_blocks), and q_len <= seq_lens[b] <= max_seq_len.
  *   - Supported dimensions: kv_lora 512, rope 64, qk_nope 128, v_dim 128,
- *     page 64, heads a multiple of 16 in [16, 128], 1 <= q_len <= 8.
+ *     page 64, heads a multiple of 16 in [16, 128]; q_len (new tokens per
+ *     sequence) 1..8 for the decode entry points, 1..65536 for
+ *     mla_cache_insert[_fp8], 1..max_seq_len for mla_prefill.
  *   - Thread safety: calls are re-entrant; two calls that share a workspace
  *     or an output buffer must be ordered by the caller (same stream).
  */
@@ -205,6 +207,40 @@ int mla_decode_step_fp8(const mla_dims* dims, const void* q, const void* kv_a,
                         int32_t q_len, int32_t max_seq_len, float softmax_scale, void* out,
                         void* workspace, size_t workspace_bytes, int32_t num_splits_hint,
                         void* stream);
+
+/*
+ * Prefill: attention for many new tokens per sequence (a prompt, or a chunk
+ * of one) in the expanded multi-head form ([V3-src] "(a) Naive实现":
+ * kv_b_proj expands every cached latent into the head's k_nope and v, the
+ * key is k_nope followed by the shared k_pe).  It computes the same function
+ * as mla_decode (same arguments, same causal rule: new query i of sequence b
+ * sees positions t <= seq_lens[b] - q_len + i, same scale), with no bound on
+ * q_len beyond max_seq_len: the dense 192/128-wide heads suit the
+ * compute-bound case, the absorbed 576/512-wide ones the memory-bound decode.
+ * The new tokens' entries must already be in the cache (mla_cache_insert).
+ *
+ * mla_prefill_workspace_bytes — bytes of device workspace mla_prefill needs
+ * for this batch and max_seq_len (the expanded keys and values of every
+ * head: batch * H * roundup(max_seq_len, 64) * 640 bytes, plus alignment), or
+ * 0 if the arguments are invalid.
+ *
+ * mla_prefill
+ *   q, kv_b, cache, num_blocks, block_table, bt_stride, seq_lens,
+ *   max_seq_len, softmax_scale, out: as mla_decode (q bf16 [B, q_len, H, 192]
+ *   with q_pe rotated; out bf16 [B, q_len, H, 128]); bf16 cache only
+ *   workspace   device memory, >= mla_prefill_workspace_bytes; overwritten
+ * Arithmetic: the expanded keys and values are rounded to bf16; bf16
+ * matrix-core products with fp32 accumulation, fp32 softmax statistics
+ * (running max and sum per row), bf16 output.  Errors as mla_decode.  Two
+ * launches on `stream`; with profiling enabled the stages are recorded as
+ * (expansion, attention, empty).
+ */
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_seq_len);
+int mla_prefill(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+                int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t max_seq_len,
+                float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                void* stream);
 
 /*
  * mla_profile_enable / mla_profile_collect — stage timing for benchmarks.

@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
     decode_workspace_bytes,
     lib_path,
     load,
+    prefill,
+    prefill_workspace_bytes,
     profile_collect,
     profile_enable,
     status_string,

@@ -56,6 +56,10 @@ def load() -> ctypes.CDLL:
     lib.mla_cache_insert_fp8.restype = ctypes.c_int
     lib.mla_decode_fp8.argtypes = lib.mla_decode.argtypes
     lib.mla_decode_fp8.restype = ctypes.c_int
+    lib.mla_prefill_workspace_bytes.argtypes = [DP, I32, I32]
+    lib.mla_prefill_workspace_bytes.restype = SZ
+    lib.mla_prefill.argtypes = [DP, P, P, P, I32, P, I32, P, I32, I32, I32, F, P, P, SZ, P]
+    lib.mla_prefill.restype = ctypes.c_int
     lib.mla_decode_step.argtypes = [DP, P, P, P, F, F, P, P, I32, P, I32, P, I32, I32, I32, F, P,
                                     P, SZ, I32, P]
     lib.mla_decode_step.restype = ctypes.c_int
@@ -220,6 +224,43 @@ def decode_step(q, kv_a, rms_w, kv_b, cache, block_table, seq_lens, max_seq_len:
             num_splits_hint, _stream(stream))
     if st != 0:
         raise MLAError(st, "mla_decode_step_fp8" if fp8 else "mla_decode_step")
+    return out
+
+
+def prefill_workspace_bytes(heads: int, batch: int, max_seq_len: int) -> int:
+    d = dims(heads)
+    return int(load().mla_prefill_workspace_bytes(ctypes.byref(d), batch, max_seq_len))
+
+
+def prefill(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, *,
+            softmax_scale: float | None = None, out=None, workspace=None, stream=None):
+    """mla_prefill: q bf16 [B, S, H, 192] (q_pe rotated), kv_b bf16
+    [H*256, 512], cache bf16 [num_blocks, 64, 576] already holding the S new
+    tokens; returns out bf16 [B, S, H, 128]."""
+    import torch
+    bsz, q_len, heads = q.shape[0], q.shape[1], q.shape[2]
+    dev = cache.device
+    _check(q, "q", torch.bfloat16, (bsz, q_len, heads, NOPE + ROPE), dev)
+    _check(kv_b, "kv_b", torch.bfloat16, (heads * (NOPE + VDIM), LATENT), dev)
+    _check_cache(cache, False, dev)
+    _check(block_table, "block_table", torch.int32, None, dev)
+    _check(seq_lens, "seq_lens", torch.int32, (bsz,), dev)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(NOPE + ROPE)
+    if out is None:
+        out = torch.empty((bsz, q_len, heads, VDIM), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (bsz, q_len, heads, VDIM), dev)
+    need = prefill_workspace_bytes(heads, bsz, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    d = dims(heads)
+    st = load().mla_prefill(ctypes.byref(d), _ptr(q), _ptr(kv_b), _ptr(cache), cache.shape[0],
+                            _ptr(block_table), block_table.shape[1], _ptr(seq_lens), bsz, q_len,
+                            max_seq_len, softmax_scale, _ptr(out), _ptr(workspace),
+                            workspace.numel(), _stream(stream))
+    if st != 0:
+        raise MLAError(st, "mla_prefill")
     return out
 
 

@@ -21,6 +21,7 @@ constexpr int kMaxHint = 64;
 constexpr int kMaxBatch = 1 << 16;
 constexpr int kMaxSeqLen = 1 << 24;
 constexpr int kMaxDevices = 64;
+constexpr int kMaxInsert = 1 << 16;  // new tokens per sequence in one insert
 
 int device_cus() {
   static std::once_flag once[kMaxDevices];
@@ -158,8 +159,8 @@ int cache_insert_any(bool fp8, const mla_dims* dims, const void* kv_a, const voi
                      int32_t num_blocks, void* stream) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (batch < 0 || batch > kMaxBatch || q_len < 1 || q_len > kMaxQLen || bt_stride < 1 ||
-      num_blocks < 1)
+  if (batch < 0 || batch > kMaxBatch || q_len < 1 || q_len > kMaxInsert || bt_stride < 1 ||
+      num_blocks < 1 || (int64_t)batch * q_len > (int64_t)INT32_MAX)
     return MLA_ERR_SHAPE;
   if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(rope_base) || rope_base <= 0.f)
     return MLA_ERR_SHAPE;
@@ -336,6 +337,57 @@ int mla_decode_step_fp8(const mla_dims* dims, const void* q, const void* kv_a, c
   return step_any(true, dims, q, kv_a, rms_w, eps, rope_base, kv_b, cache, num_blocks,
                   block_table, bt_stride, seq_lens, batch, q_len, max_seq_len, softmax_scale, out,
                   workspace, workspace_bytes, num_splits_hint, stream);
+}
+
+namespace {
+
+// rows per (sequence, head) in the prefill workspace: max_seq_len rounded up
+// to the 64-key block
+int64_t prefill_lpad(int32_t max_seq_len) { return ((int64_t)max_seq_len + 63) / 64 * 64; }
+
+}  // namespace
+
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_seq_len) {
+  if (check_dims(dims) != MLA_OK) return 0;
+  if (batch < 0 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeqLen) return 0;
+  return align256((size_t)batch * dims->heads * prefill_lpad(max_seq_len) * (kQk + kVdim) * 2) +
+         256;
+}
+
+int mla_prefill(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+                int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t max_seq_len,
+                float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > kMaxBatch || q_len < 1 || max_seq_len < q_len ||
+      max_seq_len > kMaxSeqLen || num_blocks < 1)
+    return MLA_ERR_SHAPE;
+  const int max_pages = (max_seq_len + kPage - 1) / kPage;
+  if (bt_stride < max_pages) return MLA_ERR_SHAPE;
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q || !kv_b || !cache || !block_table || !seq_lens || !out) return MLA_ERR_NULL;
+  const size_t need = mla_prefill_workspace_bytes(dims, batch, max_seq_len);
+  if (!workspace) return MLA_ERR_WORKSPACE;
+  if (need == 0 || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  const int heads = dims->heads;
+  const int64_t lpad = prefill_lpad(max_seq_len);
+  char* ws = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
+  uint16_t* kx = reinterpret_cast<uint16_t*>(ws);
+  uint16_t* vx = kx + (size_t)batch * heads * lpad * kQk;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int pc = g_prof.used < g_prof.max_calls ? g_prof.used++ : -1;
+  prof_mark(pc, 0, s);
+  hipError_t e = launch_prefill(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_b),
+      static_cast<const uint16_t*>(cache), block_table, bt_stride, seq_lens, batch, heads, q_len,
+      (int)lpad, softmax_scale * 1.4426950408889634f, kx, vx, static_cast<uint16_t*>(out), s,
+      pc >= 0 ? g_prof.ev[pc * kMarks + 1] : nullptr);
+  prof_mark(pc, 2, s);
+  prof_mark(pc, 3, s);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 }  // extern "C"

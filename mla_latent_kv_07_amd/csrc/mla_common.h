@@ -104,6 +104,15 @@ hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_ab
                          uint16_t* o_part, float* lse_part,
                          int* restart_flags, hipStream_t stream);
 
+// prefill in the expanded form (prefill.hip): expansion of K/V into kx/vx
+// (bf16 [B][H][lpad][192] / [B][H][lpad][128]), then causal attention; `mid`
+// (optional) is recorded between the two launches
+hipError_t launch_prefill(const uint16_t* q, const uint16_t* kv_b, const uint16_t* cache,
+                          const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
+                          int batch, int heads, int q_len, int lpad, float scale_log2,
+                          uint16_t* kx, uint16_t* vx, uint16_t* out, hipStream_t stream,
+                          hipEvent_t mid);
+
 hipError_t launch_combine(const uint16_t* o_part, const float* lse_part, PlanView plan,
                           const uint16_t* kv_b, int heads, int q_len, int batch, uint16_t* out,
                           hipStream_t stream);

@@ -68,6 +68,18 @@ WORKLOADS = {
                     "128 heads, context U[1024,16384], insert of the 2 new tokens first"),
 }
 ORDER = ["tiny_v2lite", "v2lite_b32", "v3_b64_l8192", "v3_longskew_b8", "v3_mtp_b128"]
+# prefill in the expanded form: many new tokens per sequence
+WORKLOADS.update({
+    "prefill_v3_b2_s4096": Workload(
+        "prefill_v3_b2_s4096", 2, 4096, 128, "fixed:4096",
+        description="V3 shape prefill: 2 prompts of 4096 new tokens (no cached prefix), "
+                    "128 heads"),
+    "prefill_v3_chunk_b4": Workload(
+        "prefill_v3_chunk_b4", 4, 1024, 128, "uniform:2048:8192",
+        description="V3 shape chunked prefill: 4 sequences, a chunk of 1024 new tokens "
+                    "after a cached prefix (context U[2048,8192]), 128 heads"),
+})
+PREFILL = ["prefill_v3_b2_s4096", "prefill_v3_chunk_b4"]
 
 
 def draw_lens(rng: np.random.Generator, spec: str, batch: int) -> np.ndarray:
@@ -173,6 +185,14 @@ def expanded_macs(heads: int, length: int) -> tuple[int, int]:
     the attention itself over 192-wide keys and 128-wide values)."""
     return (length * LATENT * heads * (NOPE + VDIM),
             heads * length * (NOPE + ROPE + VDIM))
+
+
+def prefill_flops(seq_lens, q_len: int, heads: int) -> tuple[int, int]:
+    """Flops of a prefill in the expanded form: (expanding every cached latent
+    of the batch into all heads' k_nope and v, the attention over 192-wide
+    keys and 128-wide values for every visible (query, position) pair)."""
+    return (2 * int(np.sum(seq_lens)) * LATENT * heads * (NOPE + VDIM),
+            2 * heads * visible_pairs(seq_lens, q_len) * (NOPE + ROPE + VDIM))
 
 
 def insert_bytes(batch: int, q_len: int) -> int:
