@@ -259,7 +259,9 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a,
 // S^T = K Q^T (bf16 MFMA 16x16x32), which leaves each lane one row's scores
 // in the B-operand layout of O^T = V^T P^T (the decode kernel's arrangement:
 // P never leaves registers).  K and V blocks of 64 keys (24 + 16 KB) are
-// copied into LDS by buffer loads to LDS, double-buffered.  Online softmax
+// copied into LDS by buffer loads to LDS, three stages, two blocks in flight
+// while one is computed.  Workgroups of one (sequence, head) run on one XCD
+// (its K and V stay in that XCD's L2).  Online softmax
 // in log2 units with fp32 running max and sum per row; the 128-wide output
 // rows are rescaled only when a row's max grows.
 
@@ -281,22 +283,40 @@ struct PrefillArgs {
   int q_len;
   int lpad;
   int n_qblk;
+  int batch;
   float scale_log2;        // softmax_scale * log2(e)
 };
 
 template <int S>
 using PSlot = std::integral_constant<int, S>;
+constexpr int kPCopies = kPStage / 1024 / kPWaves;  // copies per wavefront per block: 5
 
 __global__ __launch_bounds__(kPWaves * 64) void prefill_attn_kernel(PrefillArgs a) {
+  // three stages, each its own array: block kb in stage kb % 3, named at
+  // compile time (the loop is unrolled by three), so the compiler sees that
+  // the copies in flight never alias the stage being read
   __shared__ __attribute__((aligned(1024))) char st0[kPStage];
   __shared__ __attribute__((aligned(1024))) char st1[kPStage];
+  __shared__ __attribute__((aligned(1024))) char st2[kPStage];
   auto stage = [&](auto s) -> MLA_LDS char* {
-    if constexpr (decltype(s)::value == 0) return (MLA_LDS char*)st0;
-    else return (MLA_LDS char*)st1;
+    constexpr int S = decltype(s)::value;
+    if constexpr (S == 0) return (MLA_LDS char*)st0;
+    else if constexpr (S == 1) return (MLA_LDS char*)st1;
+    else return (MLA_LDS char*)st2;
   };
-  const int qb = a.n_qblk - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  // block id -> (head, sequence, query block): each XCD (block id mod 8)
+  // takes a contiguous range of the (head, sequence) list (head-major, so
+  // every XCD gets the same mix of sequence lengths), all query blocks of
+  // one pair in a row, the latest (most keys) first
+  const int total = a.n_qblk * a.heads * a.batch;
+  const int per_xcd = (total + 7) >> 3;
+  const int local = blockIdx.x >> 3;
+  const int gidx = (blockIdx.x & 7) * per_xcd + local;
+  if (local >= per_xcd || gidx >= total) return;
+  const int pair = gidx / a.n_qblk;
+  const int qb = a.n_qblk - 1 - (gidx - pair * a.n_qblk);
+  const int h = pair / a.batch;
+  const int b = pair - h * a.batch;
   const int len = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);  // uniform: scalar
   const int P = len - a.q_len;  // cached positions before the new tokens
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -462,19 +482,27 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_attn_kernel(PrefillArgs 
       }
     }
   };
-  // block kb in stage kb % 2: wait for its copies, a barrier (every
-  // wavefront is past block kb-1, whose stage takes block kb+1), issue block
-  // kb+1, compute block kb (a wavefront whose rows see no key of it skips)
+  // block kb in stage kb % 3: wait for its copies (block kb+1's may still be
+  // in flight: every step issues one block's copies, an empty one past the
+  // end, so that count is fixed), a barrier (every wavefront is past block
+  // kb-1, whose stage takes block kb+2), issue block kb+2, compute block kb
+  // (a wavefront whose rows see no key of it skips)
   auto step = [&](auto s, int kb) __attribute__((always_inline)) -> void {
-    __builtin_amdgcn_s_waitcnt(pf_vmcnt(0));
+    constexpr int S = decltype(s)::value;
+    __builtin_amdgcn_s_waitcnt(pf_vmcnt(kPCopies));
     pf_barrier();
-    issue(PSlot<1 - decltype(s)::value>{}, kb + 1);
+    issue(PSlot<(S + 2) % 3>{}, kb + 2);
     if (kb < nkb_w) compute(s, kb);
   };
   issue(PSlot<0>{}, 0);
-  for (int kb = 0; kb < nkb; kb += 2) {
+  issue(PSlot<1>{}, 1);
+  // the query rows (loaded before the copies) have arrived once at most the
+  // two blocks' copies are pending
+  __builtin_amdgcn_s_waitcnt(pf_vmcnt(2 * kPCopies));
+  for (int kb = 0; kb < nkb; kb += 3) {
     step(PSlot<0>{}, kb);
     step(PSlot<1>{}, kb + 1);
+    step(PSlot<2>{}, kb + 2);
   }
   __builtin_amdgcn_s_waitcnt(pf_vmcnt(0));
 
@@ -513,8 +541,9 @@ hipError_t launch_prefill(const uint16_t* q, const uint16_t* kv_b, const uint16_
   if (e != hipSuccess) return e;
   if (mid) (void)hipEventRecord(mid, stream);
   PrefillArgs pa{kx, vx, q, out, seq_lens, heads, q_len, lpad, (q_len + kPRows - 1) / kPRows,
-                 scale_log2};
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3(pa.n_qblk, heads, batch), dim3(kPWaves * 64), 0,
+                 batch, scale_log2};
+  const int blocks = pa.n_qblk * heads * batch;
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3(8 * ((blocks + 7) / 8)), dim3(kPWaves * 64), 0,
                      stream, pa);
   return hipGetLastError();
 }
