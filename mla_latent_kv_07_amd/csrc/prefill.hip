@@ -54,21 +54,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pf_rsrc(const void* base, int 
 // ============================================================================
 // Expansion
 // ============================================================================
-// One workgroup per (sequence, span of 1024 positions, head, part), part 0 =
-// K (W_UK rows), part 1 = V (W_UV rows).  Wavefront w keeps its 32 weight
-// rows (all 512 latent columns, 128 VGPRs) in registers as the MFMA A
-// operand; the latent rows stream through LDS in chunks of 32 cache rows
-// (36 KB, half a page) copied straight from the paged cache by buffer loads to
-// LDS, four chunks in flight, with the decode kernel's row layout (1152-byte
+// One workgroup per (sequence, span of 1024 positions, head): eight
+// wavefronts, two per SIMD; wavefronts 0-3 make K (W_UK rows 32 w ..),
+// 4-7 make V (W_UV rows 32 (w - 4) ..).  Each keeps its 32 weight rows (all
+// 512 latent columns, 128 VGPRs) in registers as the MFMA A operand; the
+// latent rows stream through LDS in chunks of 32 cache rows (36 KB, half a
+// page) copied straight from the paged cache by buffer loads to LDS, three
+// slots, two chunks in flight, with the decode kernel's row layout (1152-byte
 // rows, pieces permuted by xswz) so the B-operand reads are conflict-free.
 // D^T = W c^T leaves each lane 4 consecutive output columns of one position:
-// 8-byte stores.  Part 0 also copies each row's k_pe into K's last 64
+// 8-byte stores.  Wavefronts 0-3 also copy each row's k_pe into K's last 64
 // columns.
 
 constexpr int kXChunk = 32;
 constexpr int kXChunkBytes = kXChunk * kEntryBytes;  // 36864
-constexpr int kXPer = kXChunkBytes / 1024 / 4;       // copies per wavefront per chunk: 9
-constexpr int kXSpan = 1024;                         // positions per workgroup
+constexpr int kXWaves = 8;
+constexpr int kXPer = (kXChunkBytes / 1024 + kXWaves - 1) / kXWaves;  // copies per wavefront: 5
+constexpr int kXSlotBytes = kXPer * kXWaves * 1024;                   // 40 KB (4 KB padding)
+constexpr int kXSpan = 1024;                                          // positions per workgroup
 
 __device__ __forceinline__ int xswz(int r) { return (((r >> 1) & 3) << 1) ^ (((r >> 3) & 1) * 7); }
 
@@ -90,34 +93,29 @@ using XSlot = std::integral_constant<int, S>;
 
 // (block_table: a restrict parameter of its own, so its entries come through
 // scalar loads, which do not count against the copies in flight)
-__global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a,
-                                                     const int32_t* __restrict__ block_table) {
-  __shared__ __attribute__((aligned(1024))) char ring0[kXChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char ring1[kXChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char ring2[kXChunkBytes];
-  __shared__ __attribute__((aligned(1024))) char ring3[kXChunkBytes];
+__global__ __launch_bounds__(kXWaves * 64) void expand_kernel(
+    ExpandArgs a, const int32_t* __restrict__ block_table) {
+  __shared__ __attribute__((aligned(1024))) char ring0[kXSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring1[kXSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring2[kXSlotBytes];
   auto ring = [&](auto s) -> MLA_LDS char* {
     constexpr int S = decltype(s)::value;
     if constexpr (S == 0) return (MLA_LDS char*)ring0;
     else if constexpr (S == 1) return (MLA_LDS char*)ring1;
-    else if constexpr (S == 2) return (MLA_LDS char*)ring2;
-    else return (MLA_LDS char*)ring3;
+    else return (MLA_LDS char*)ring2;
   };
-  // block -> (sequence, span, head, part): each XCD (block id mod 8) takes a
-  // contiguous range of the list, so the workgroups reading one span's latent
-  // rows share that XCD's L2
-  const int G = a.heads * 2;
-  const int total = a.batch * a.n_span * G;
+  // block -> (head, sequence, span): each XCD (block id mod 8) takes a
+  // contiguous range of the list (head-major: every XCD gets the same mix of
+  // sequence lengths)
+  const int total = a.heads * a.batch * a.n_span;
   const int per_xcd = (total + 7) >> 3;
   const int k = blockIdx.x >> 3;
   const int gidx = (blockIdx.x & 7) * per_xcd + k;
   if (k >= per_xcd || gidx >= total) return;
-  const int combo = gidx / G;
-  const int g = gidx - combo * G;
-  const int b = combo / a.n_span;
-  const int span = combo - b * a.n_span;
-  const int h = g >> 1;
-  const int part = g & 1;
+  const int h = gidx / (a.batch * a.n_span);
+  const int rest = gidx - h * (a.batch * a.n_span);
+  const int b = rest / a.n_span;
+  const int span = rest - b * a.n_span;
 
   // (values the whole workgroup shares: kept scalar, so the copy descriptors
   // built from them need no per-lane loop)
@@ -125,12 +123,14 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a,
   const int t_begin = span * kXSpan;
   const int nchunks = (min(t_begin + kXSpan, a.lpad) - t_begin) / kXChunk;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = wave >> 2;  // 0: K, 1: V
+  const int wq = wave & 3;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int gq = lane >> 4;
 
   // weight rows of this wavefront: A operand of k-step ks, row tile mt
-  const uint16_t* w = a.kv_b + ((int64_t)h * (kNope + kVdim) + part * kNope + 32 * wave) * kLatent;
+  const uint16_t* w = a.kv_b + ((int64_t)h * (kNope + kVdim) + part * kNope + 32 * wq) * kLatent;
   bf16x8 aw[kLatent / 32][2];
 #pragma unroll
   for (int ks = 0; ks < kLatent / 32; ++ks)
@@ -138,15 +138,18 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a,
     for (int mt = 0; mt < 2; ++mt)
       aw[ks][mt] = *reinterpret_cast<const bf16x8*>(w + (int64_t)(16 * mt + n) * kLatent +
                                                     32 * ks + 8 * gq);
-  // copy offsets (the same for every chunk): copy i of this wavefront fills
-  // LDS pieces 64(4i + wave) + lane from piece (Q % 72) ^ xswz(row) of its row
+  // copy offsets (the same for every chunk): copy k = 8 i + wave fills LDS
+  // pieces 64 k + lane from piece (Q % 72) ^ xswz(row) of its row; copies
+  // past the chunk's 36 read nothing and fill the slot's padding
   uint32_t doff[kXPer];
 #pragma unroll
   for (int i = 0; i < kXPer; ++i) {
-    const int q = 64 * (4 * i + wave) + lane;
+    const int kc = kXWaves * i + wave;
+    const int q = 64 * kc + lane;
     const int row = q / kChunk16;
     const int col = q - row * kChunk16;
-    doff[i] = (uint32_t)(row * kEntryBytes + 16 * (col ^ xswz(row)));
+    doff[i] = kc < kXChunkBytes / 1024 ? (uint32_t)(row * kEntryBytes + 16 * (col ^ xswz(row)))
+                                       : 0x80000000u;
   }
   const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
   // chunk j (positions t_begin + 32 j ..): rows past the sequence end read
@@ -164,8 +167,8 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a,
     const __amdgpu_buffer_rsrc_t rs = pf_rsrc(src, valid * kEntryBytes);
 #pragma unroll
     for (int i = 0; i < kXPer; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ring(s) + (4 * i + wave) * 1024, 16, doff[i],
-                                               0, 0, 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, ring(s) + (kXWaves * i + wave) * 1024, 16,
+                                               doff[i], 0, 0, 2);
   };
 
   const int row_elems = part ? kVdim : kQk;
@@ -196,14 +199,14 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a,
           acc[mt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[ks][mt], bv[tt], acc[mt][tt], 0,
                                                                 0, 0);
     }
-    // lane holds output columns 32 wave + 16 mt + 4 gq + i of position 16 tt + n
+    // lane holds output columns 32 wq + 16 mt + 4 gq + i of position 16 tt + n
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int t = t_begin + j * kXChunk + 16 * tt + n;
       char* row = reinterpret_cast<char*>(dst_base + (int64_t)t * row_elems);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const int d0 = 32 * wave + 16 * mt + 4 * gq;
+        const int d0 = 32 * wq + 16 * mt + 4 * gq;
         const int p = d0 >> 3;
         const int off = 16 * (part ? vx_piece(p, t) : kx_piece(p, t)) + 8 * ((d0 >> 2) & 1);
         u16x4 v;
@@ -223,27 +226,25 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a,
                                 16 * kx_piece(16 + c, t)) = v;
     }
   };
-  // chunk j in slot j % 4; chunk j+3 goes into chunk j-1's slot once every
-  // wavefront is past chunk j-1 (the decode kernel's ring, without the copy
-  // issue inside the matrix work)
+  // chunk j in slot j % 3; chunk j+2 goes into chunk j-1's slot once every
+  // wavefront is past chunk j-1; chunk j has landed once at most chunk j+1's
+  // copies are pending
   auto interval = [&](auto s, int j) __attribute__((always_inline)) -> void {
     constexpr int S = decltype(s)::value;
-    __builtin_amdgcn_s_waitcnt(pf_vmcnt(2 * kXPer));
+    __builtin_amdgcn_s_waitcnt(pf_vmcnt(kXPer));
     pf_barrier();
-    issue(XSlot<(S + 3) & 3>{}, j + 3);
+    issue(XSlot<(S + 2) % 3>{}, j + 2);
     if (j < nchunks) compute(s, j);
   };
   issue(XSlot<0>{}, 0);
   issue(XSlot<1>{}, 1);
-  issue(XSlot<2>{}, 2);
   // the weight rows (loaded before the copies) have arrived once at most the
-  // three chunks' copies are pending
-  __builtin_amdgcn_s_waitcnt(pf_vmcnt(3 * kXPer));
-  for (int j = 0; j < nchunks; j += 4) {
+  // two chunks' copies are pending
+  __builtin_amdgcn_s_waitcnt(pf_vmcnt(2 * kXPer));
+  for (int j = 0; j < nchunks; j += 3) {
     interval(XSlot<0>{}, j);
     interval(XSlot<1>{}, j + 1);
     interval(XSlot<2>{}, j + 2);
-    interval(XSlot<3>{}, j + 3);
   }
   __builtin_amdgcn_s_waitcnt(pf_vmcnt(0));
 }
@@ -534,8 +535,8 @@ hipError_t launch_prefill(const uint16_t* q, const uint16_t* kv_b, const uint16_
                           hipEvent_t mid) {
   ExpandArgs ea{cache, bt_stride, seq_lens, kv_b, heads, batch, lpad,
                 (lpad + kXSpan - 1) / kXSpan, kx, vx};
-  const int total = batch * ea.n_span * heads * 2;
-  hipLaunchKernelGGL(expand_kernel, dim3(8 * ((total + 7) / 8)), dim3(256), 0, stream, ea,
+  const int total = batch * ea.n_span * heads;
+  hipLaunchKernelGGL(expand_kernel, dim3(8 * ((total + 7) / 8)), dim3(kXWaves * 64), 0, stream, ea,
                      block_table);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
