@@ -262,9 +262,9 @@ __global__ __launch_bounds__(kXWaves * 64) void expand_kernel(
 // P never leaves registers).  K and V blocks of 64 keys (24 + 16 KB) are
 // copied into LDS by buffer loads to LDS, three stages, two blocks in flight
 // while one is computed.  Workgroups of one (sequence, head) run on one XCD
-// (its K and V stay in that XCD's L2).  Online softmax
-// in log2 units with fp32 running max and sum per row; the 128-wide output
-// rows are rescaled only when a row's max grows.
+// (its K and V stay in that XCD's L2).  Online softmax in log2 units with
+// fp32 sums; a row's reference max is raised (a cross-lane max and a rescale
+// of its output accumulators) only when a score exceeds it by more than 2^8.
 
 constexpr int kPBlk = 64;
 constexpr int kPRows = 256;
@@ -290,6 +290,9 @@ struct PrefillArgs {
 
 template <int S>
 using PSlot = std::integral_constant<int, S>;
+// a row's reference max is raised only when a score passes it by more than
+// this (log2 units): probabilities stay <= 2^8
+constexpr float kPRefSlack = 8.0f;
 constexpr int kPCopies = kPStage / 1024 / kPWaves;  // copies per wavefront per block: 5
 
 __global__ __launch_bounds__(kPWaves * 64) void prefill_attn_kernel(PrefillArgs a) {
@@ -435,7 +438,7 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_attn_kernel(PrefillArgs 
         // visible: 16 u + j <= lim
         const int lim = P + iw + 16 * rt + n - kPBlk * kb - 32 * kk - 4 * gq;
         float x[2][4];
-        float mloc = -INFINITY;
+        float lmax = -INFINITY;  // this lane's max over its 8 keys
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -443,13 +446,25 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_attn_kernel(PrefillArgs 
             float v = sc[u][rt][j] * a.scale_log2;
             if (mask && 16 * u + j > lim) v = -INFINITY;
             x[u][j] = v;
-            mloc = fmaxf(mloc, v);
+            lmax = fmaxf(lmax, v);
           }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        const float m_new = fmaxf(m[rt], mloc);
-        const float alpha = m[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[rt] - m_new);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        // The row's reference m[rt] is refreshed (row max across its 4 lanes,
+        // accumulators rescaled) only when some score exceeds it by more than
+        // 2^8; otherwise p = 2^(s - m) <= 2^8 (fp32 sums and bf16 products
+        // keep their relative precision), and no cross-lane step is needed.
+        if (__builtin_amdgcn_ballot_w64(lmax > m[rt] + kPRefSlack) != 0) {
+          float mrow = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+          mrow = fmaxf(mrow, __shfl_xor(mrow, 32, 64));
+          const float m_new = fmaxf(m[rt], mrow);
+          const float alpha = m[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[rt] - m_new);
+          l[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[dt][rt][j] *= alpha;
+          m[rt] = m_new;
+        }
+        const float m_use = m[rt] == -INFINITY ? 0.f : m[rt];
         float psum = 0.f;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -459,14 +474,7 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_attn_kernel(PrefillArgs 
             psum += p;
             pb[rt][4 * u + j] = (__bf16)p;
           }
-        l[rt] = l[rt] * alpha + psum;
-        m[rt] = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[dt][rt][j] *= alpha;
-        }
+        l[rt] += psum;
       }
       // ---- O^T += V^T P^T over the 32 keys of the half
 #pragma unroll

@@ -140,3 +140,24 @@ def test_prefill_workload(name):
     mx, rr = errors(got[bs][:, :, hs], ref)
     say(f"   max-abs {mx:.3e} rel-rms {rr:.3e}")
     assert mx <= MAX_ABS and rr <= REL_RMS
+
+
+def test_prefill_wide_score_range():
+    """Queries scaled by 16 (scores spread over tens of log2 units): row
+    maxima keep rising across key blocks, so the running reference is raised
+    and the accumulators rescaled many times; also a late, much larger key
+    (a score jump after many blocks)."""
+    torch = _torch()
+    say("[prefill] wide score range")
+    d = wl.make_inputs(2, 300, 16, [300, 900], permute=True, seed=99, spare_blocks=1)
+    qf = (d["q"].astype(np.uint32) << 16).view(np.float32) * np.float32(16.0)
+    d["q"] = wl.f32_to_bf16_bits(qf)
+    kv_a = (d["kv_a"].astype(np.uint32) << 16).view(np.float32)
+    kv_a[1, -1, :] *= np.float32(8.0)  # the last new token of sequence 1: a larger key
+    d["kv_a"] = wl.f32_to_bf16_bits(kv_a)
+    got, _ = run(d, torch)
+    ref = decode_expanded(d["q"], d["kv_b"], ref_cache(d), d["block_table"], d["seq_lens"], 300)
+    mx, rr = errors(got, ref)
+    say(f"   max-abs {mx:.3e} rel-rms {rr:.3e}")
+    assert np.all(np.isfinite(got))
+    assert mx <= MAX_ABS and rr <= REL_RMS
