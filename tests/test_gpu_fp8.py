@@ -223,3 +223,34 @@ def test_fp8_cache_error_against_bf16_cache():
     mx, rr = errors(a, b)
     say(f"   FP8 vs bf16 cache: max-abs {mx:.3e} rel-rms {rr:.3e}")
     assert rr < 0.1
+
+
+def test_decode_fp8_restart_on_score_jump():
+    """The FP8 cache's restart path: one late position of each sequence scaled
+    20x (before quantisation; its scale byte absorbs it) makes some heads'
+    scores jump far above the first chunk's max, so those items restart (an
+    exact-max pass, then a pass with that reference, each chunk expanded
+    again from its FP8 rows).  Outputs are large here, so the max error is
+    taken relative to the largest output, as for the bf16 cache."""
+    torch = _torch()
+    from oracle import bf16_bits_to_f64, f64_to_bf16_bits
+    say("[decode fp8] large late score (restart path)")
+    d = wl.make_inputs(2, 1, 128, [300, 200], permute=True, seed=45)
+    cbf = finite_bf16(ref_insert_bf16(d))
+    for b, p in ((0, 250), (1, 70)):
+        row = cbf[d["block_table"][b, p // 64], p % 64]
+        row[:] = f64_to_bf16_bits(bf16_bits_to_f64(row) * 20.0)
+    c8 = ofp8.quantize_cache(cbf)
+    got = run_decode(d, dev(c8, torch), torch)
+    ref = ofp8.decode_expanded_fp8(d["q"], d["kv_b"], c8, d["block_table"], d["seq_lens"], 1)
+    mx, rr = errors(got, ref)
+    rel_max = mx / float(np.max(np.abs(ref)))
+    say(f"   max-abs/max|ref| {rel_max:.3e} rel-rms {rr:.3e}")
+    assert np.all(np.isfinite(got))
+    assert rel_max <= MAX_ABS and rr <= REL_RMS
+
+
+def ref_insert_bf16(d):
+    from oracle import cache_insert
+    return cache_insert(d["cache"], d["kv_a"], d["rms_w"], d["block_table"], d["seq_lens"],
+                        d["q_len"], EPS32, wl.ROPE_BASE, wl.LATENT)
