@@ -253,12 +253,11 @@ __device__ __forceinline__ void score_schedule() {
 // path takes roughly 15 cycles per 1 KB copy, and a wavefront that issues
 // copies faster than that stalls, so they go out one at a time between
 // MFMAs instead of all at once.
-template <int NH, class D, int NC>
+template <int NH, class D, int NC, int KPD = 4>
 __device__ __forceinline__ void score_chunk(const MLA_LDS char* buf, int sbase_even,
                                             int sbase_odd, const bf16x8 (&qreg)[NH][18],
                                             f32x4 (&sacc)[NH][2], const ChunkCopy& cc,
                                             const uint32_t* off, int wave) {
-  constexpr int KPD = 4;
 #pragma unroll
   for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -391,6 +390,33 @@ __device__ __forceinline__ void pv_slice(const MLA_LDS char* buf, const int (&vb
   __builtin_amdgcn_sched_group_barrier(kSgMfma, G * VPD, 0);
 }
 
+// The same product with the probabilities read from LDS one row group at a
+// time (`pb_lds`, 1 KB B-operand tile per group): eight wavefronts cannot
+// keep all groups' tiles in registers next to the query and accumulators.
+template <int NW, int NH>
+__device__ __forceinline__ void pv_slice_lds(const MLA_LDS char* buf, const int (&vbase)[4],
+                                             const MLA_LDS char* pb_lds, int lane,
+                                             f32x4 (&oacc)[NW * NH][32 / NW]) {
+  constexpr int G = NW * NH;
+  constexpr int FT = 32 / NW;
+  bf16x8 vb[FT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f) {
+    const int o = vbase[f & 3] + 128 * (f >> 2);
+    const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(buf + o));
+    const bf16x4 a1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(buf + (o + 16 * kEntryBytes)));
+    vb[f] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const bf16x8 pg = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_lds + g * 1024 + lane * 16);
+#pragma unroll
+    for (int f = 0; f < FT; ++f)
+      oacc[g][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[f], pg, oacc[g][f], 0, 0, 0);
+  }
+}
+
 // Row max only (the first pass of a restart).
 template <int NH>
 __device__ __forceinline__ void max_chunk(const f32x4 (&sacc)[NH][2], float (&m)[NH],
@@ -434,17 +460,19 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   constexpr int FT = 32 / NW;  // feature tiles of a wavefront's P.V slice
   constexpr int kRowBytes = FP8 ? kFp8EntryBytes : kEntryBytes;  // cache bytes per position
   using D = Dma<NW, FP8>;
-  // The ring: NS chunk slots (bf16: 4; FP8: 3 next to the two staging
-  // chunks), each its own array.  Chunk j lives in slot j % NS, and the chunk
+  // The ring: NS chunk slots (bf16: 4, or 3 of 40 KB with eight wavefronts;
+  // FP8: 3 next to the two staging chunks), each its own array.  Chunk j lives in slot j % NS, and the chunk
   // loop is unrolled by NS so that every access names its slot at compile
   // time: the compiler then knows that the copies in flight (into the other
   // slots) never alias the slot being read and adds no wait of its own on
   // them.
-  constexpr int NS = FP8 ? 3 : 4;
+  constexpr int NS = (FP8 || NW == 8) ? 3 : 4;
+  // score read-ahead in k-steps (eight wavefronts: two, for registers)
+  constexpr int kKpd = NW == 8 ? 2 : 4;
   __shared__ __attribute__((aligned(1024))) char ring0[D::kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char ring1[D::kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char ring2[D::kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) char ring3[FP8 ? 16 : D::kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring3[NS == 4 ? D::kSlotBytes : 16];
   // FP8: chunks j (read by the compute) and j + 1 (being expanded), bf16 layout
   __shared__ __attribute__((aligned(1024))) char stage[FP8 ? 2 * kBufBytes : 16];
   // probabilities of the chunk, one 1 KB B-operand tile per row group
@@ -610,7 +638,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     f32x4 sacc[NH][2];
     // the phases stay in order: moving the next phase's LDS reads up would
     // keep their registers live across this one
-    score_chunk<NH, D, decltype(nc_c)::value>(buf, sbase_even, sbase_odd, qreg, sacc, cc, doff,
+    score_chunk<NH, D, decltype(nc_c)::value, kKpd>(buf, sbase_even, sbase_odd, qreg, sacc, cc, doff,
                                               wave);
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 pk[NH];
@@ -623,12 +651,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     for (int h = 0; h < NH; ++h)
       *reinterpret_cast<MLA_LDS bf16x8*>(pb_lds + (wave * NH + h) * 1024 + lane * 16) = pk[h];
     ring_barrier();
-    bf16x8 pb[G];
+    if constexpr (NW == 8) {
+      pv_slice_lds<NW, NH>(buf, vbase, pb_lds, lane, oacc);
+    } else {
+      bf16x8 pb[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-      pb[g] = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_lds + g * 1024 + lane * 16);
-    __builtin_amdgcn_sched_barrier(0);
-    pv_slice<NW, NH>(buf, vbase, pb, oacc);
+      for (int g = 0; g < G; ++g)
+        pb[g] = *reinterpret_cast<const MLA_LDS bf16x8*>(pb_lds + g * 1024 + lane * 16);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_slice<NW, NH>(buf, vbase, pb, oacc);
+    }
     if constexpr (decltype(dq_c)::value) {
       // the rows to expand have landed once at most the copies of the two
       // chunks after them are pending
@@ -672,11 +704,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
         for (int i = 0; i < kPer; ++i) copy_piece<D::kWaveBase, D::kStride>(cc, doff, i, wave);
       }
     } else {
-      // chunk j has landed once at most the copies of chunks j+1, j+2 are pending
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
+      // chunk j has landed once at most the copies of chunks j+1 .. j+NS-2
+      // are pending
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * kPer));
       ring_barrier();
-      // chunk j+3 goes into chunk j-1's slot: every wavefront is past it
-      const ChunkCopy cc = chunk_copy(Slot<(S + 3) & 3>{}, j + 3);
+      // chunk j+NS-1 goes into chunk j-1's slot: every wavefront is past it
+      const ChunkCopy cc = chunk_copy(Slot<(S + NS - 1) % NS>{}, j + NS - 1);
       if (j < nchunks) {
         need_restart |= compute(ring(slot_c), first_c, AllCopies{}, F{}, j, cc, nullptr, nullptr);
       } else {
@@ -688,9 +721,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   // (an item always has at least one chunk)
   issue(Slot<0>{}, 0);
   issue(Slot<1>{}, 1);
-  issue(Slot<2>{}, 2);
+  if constexpr (FP8 || NS == 4) issue(Slot<2>{}, 2);
   if constexpr (FP8) {
     dequant_rows<NW>(ring(Slot<0>{}), stage_of(0), wave, lane);
+    interval(Slot<0>{}, T{}, 0);
+    for (int j = 1; j < nchunks; j += 3) {
+      interval(Slot<1>{}, F{}, j);
+      interval(Slot<2>{}, F{}, j + 1);
+      interval(Slot<0>{}, F{}, j + 2);
+    }
+  } else if constexpr (NS == 3) {
     interval(Slot<0>{}, T{}, 0);
     for (int j = 1; j < nchunks; j += 3) {
       interval(Slot<1>{}, F{}, j);
@@ -738,7 +778,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
       int lim[NH];
       chunk_limits(j, lim);
       f32x4 sacc[NH][2];
-      score_chunk<NH, D, 0>(buf, sbase_even, sbase_odd, qreg, sacc, ChunkCopy{}, doff, wave);
+      score_chunk<NH, D, 0, kKpd>(buf, sbase_even, sbase_odd, qreg, sacc, ChunkCopy{}, doff, wave);
       max_chunk<NH>(sacc, m_exact, lim);
       __syncthreads();
     }
@@ -794,8 +834,11 @@ DecodeConfig decode_config(int rows_per_seq) {
   c.chunk = kChunk;
   c.nbuf = 4;
   if (groups % 8 == 0) {
-    c.waves = 4;
-    c.heads_per_wave = 2;
+    // eight wavefronts of one row group each: two per SIMD, so one's LDS
+    // waits and softmax overlap the other's matrix work
+    c.waves = 8;
+    c.heads_per_wave = 1;
+    c.nbuf = 3;
   } else if (groups % 4 == 0) {
     c.waves = 2;
     c.heads_per_wave = 2;
@@ -814,12 +857,19 @@ DecodeConfig decode_config(int rows_per_seq) {
 template <int NW, int NH>
 static hipError_t launch_t(int grid, bool fp8, const DecodeArgs& args,
                           const int32_t* block_table, hipStream_t stream) {
-  if (fp8)
-    hipLaunchKernelGGL((decode_kernel<NW, NH, true>), dim3(grid), dim3(NW * 64), 0, stream, args,
-                       block_table);
-  else
+  if constexpr (NW == 8) {
+    // no FP8 build of the eight-wavefront kernel (launch_decode routes FP8
+    // caches to the four-wavefront one)
+    if (fp8) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((decode_kernel<NW, NH, false>), dim3(grid), dim3(NW * 64), 0, stream,
                        args, block_table);
+  } else if (fp8) {
+    hipLaunchKernelGGL((decode_kernel<NW, NH, true>), dim3(grid), dim3(NW * 64), 0, stream, args,
+                       block_table);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<NW, NH, false>), dim3(grid), dim3(NW * 64), 0, stream,
+                       args, block_table);
+  }
   return hipGetLastError();
 }
 
@@ -843,6 +893,11 @@ hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_ab
   args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
+  // (the FP8 cache runs the four-wavefront kernel: same rows per workgroup,
+  // so the same workspace layout)
+  if (cfg.waves == 8)
+    return fp8 ? launch_t<4, 2>(grid, fp8, args, block_table, stream)
+               : launch_t<8, 1>(grid, fp8, args, block_table, stream);
   if (cfg.waves == 4) return launch_t<4, 2>(grid, fp8, args, block_table, stream);
   if (cfg.waves == 2) return launch_t<2, 2>(grid, fp8, args, block_table, stream);
   if (cfg.heads_per_wave == 2) return launch_t<1, 2>(grid, fp8, args, block_table, stream);
