@@ -6,7 +6,7 @@ product path (the HIP library and its Python binding) never imports it.
 
 Parity status of each function is stated in ``oracle/mla_oracle.py``.
 """
-from . import fp8  # noqa: F401
+from . import dsa, fp8  # noqa: F401
 from .mla_oracle import (  # noqa: F401
     bf16_bits_to_f64,
     f64_to_bf16_bits,

@@ -139,6 +139,28 @@ def make_inputs(batch: int, q_len: int, heads: int, lens, permute: bool = True,
                 softmax_scale=1.0 / math.sqrt(NOPE + ROPE))
 
 
+def make_index_inputs(d: dict, index_heads: int = 64, dim: int = 128, seed: int = 1) -> dict:
+    """Seeded inputs of the sparse-attention index for workload ``d``: FP8
+    (E4M3) codes drawn uniformly over the finite codes (the two NaN codes
+    0x7F / 0xFF replaced by their neighbours), one query of ``index_heads``
+    heads per sequence, one key per cache slot (paged like the latent cache),
+    per-head weights ~ N(0, 1), per-key scales ~ U[0.25, 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nb = d["cache"].shape[0]
+
+    def codes(shape):
+        c = rng.integers(0, 256, size=shape, dtype=np.int64).astype(np.uint8)
+        c[c == 0x7F] = 0x7E
+        c[c == 0xFF] = 0xFE
+        return c
+
+    return dict(index_q=codes((d["batch"], index_heads, dim)),
+                index_w=rng.standard_normal((d["batch"], index_heads), dtype=np.float32),
+                index_k=codes((nb, PAGE, dim)),
+                index_k_scale=rng.uniform(0.25, 1.0, size=(nb, PAGE)).astype(np.float32),
+                index_heads=index_heads, index_dim=dim)
+
+
 def make_workload(name: str) -> dict:
     w = WORKLOADS[name]
     d = make_inputs(w.batch, w.q_len, w.heads, w.lens, w.permute, w.seed)
