@@ -17,6 +17,9 @@
  *   [TAGS]   the "DeepSeek" tag page: excerpt on the 1/sqrt(d_k) scale, and
  *            excerpt on MLA under decode context parallelism (decode runs as
  *            one shared latent head of width 576).
+ *   [V32]    "DeepSeek-V3.2-Exp unboxing", section 初步研读: the FP8 index
+ *            kernel that scores the cached tokens (its signature and the
+ *            shapes observed in a run) and the top-k selection after it.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
@@ -243,6 +246,65 @@ int mla_prefill(const mla_dims* dims, const void* q, const void* kv_b, const voi
                 void* stream);
 
 /*
+ * Sparse decode (DeepSeek Sparse Attention; [V32] "DeepSeek-V3.2-Exp
+ * unboxing", section 初步研读: once the cache is written, an FP8 index kernel
+ * scores the cached tokens and only the highest-scoring ones enter the
+ * attention).  One new token per sequence (q_len 1); its cache entry and its
+ * index key must already be written, so seq_lens[b] >= 1.
+ *
+ * Index score of cached position n of sequence b (fp32 arithmetic):
+ *   o[n] = (sum_h index_w[b,h] * index_q[b,h,:]) . index_k[slot(n),:]
+ *          * index_k_scale[slot(n)]
+ * with E4M3 (FN) values for index_q and index_k; slot(n) is the paged slot
+ * of position n (block_table[b, n / 64] * 64 + n % 64), so the index keys
+ * share the latent cache's pages.  The weighted query sum is taken first;
+ * the pages' per-head form sum_h w_h (q_h . k_n) is the same number up to
+ * fp32 rounding.  Top-k: the min(top_k, seq_lens[b]) largest scores, equal
+ * scores (-0 and +0 included) taken lower position first, kept positions in
+ * ascending order, -1 past the count.  NaN scores rank above every number.
+ *
+ * mla_dsa_select — index scores and top-k only.
+ *   index_heads  Hi, 1..1024; index_q uint8 [B, Hi, 128]; index_w fp32 [B, Hi]
+ *   index_k      uint8 [num_blocks, 64, 128]; index_k_scale fp32 [num_blocks, 64]
+ *   block_table, bt_stride, seq_lens, max_seq_len: as mla_decode
+ *   top_k        1..65536
+ *   scores       fp32 [B, scores_stride] (scores_stride >= max_seq_len), out:
+ *                entries n < seq_lens[b] written, the rest untouched
+ *   indices      int32 [B, top_k], out; counts int32 [B] (NULL allowed), out
+ * Two launches on `stream`; no workspace.  Errors as mla_decode.
+ *
+ * mla_dsa_workspace_bytes — bytes of device workspace mla_dsa_decode needs
+ * (scores, kept positions, the kept rows gathered into dense pages:
+ * batch * ceil(min(top_k, max_seq_len) / 64) * 73728 bytes, and the decode
+ * workspace of q_len 1), or 0 if the arguments are invalid.
+ *
+ * mla_dsa_decode — selection as above, then the MLA decode (as mla_decode,
+ * q_len 1) over the kept positions only.
+ *   q, kv_b, cache (bf16 only), num_blocks, block_table, bt_stride, seq_lens,
+ *   max_seq_len, softmax_scale, out, num_splits_hint: as mla_decode
+ *   index_*, top_k: as mla_dsa_select
+ *   indices_out  int32 [B, top_k] or NULL: the kept positions
+ *   workspace    device memory, >= mla_dsa_workspace_bytes; overwritten
+ * Launches on `stream`: index scores, top-k, gather, then the three decode
+ * launches.  With profiling enabled a call takes two profile slots: (index
+ * scores, top-k, gather), then (prep, decode, combine).
+ */
+int mla_dsa_select(int32_t index_heads, const void* index_q, const float* index_w,
+                   const void* index_k, const float* index_k_scale, const int32_t* block_table,
+                   int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
+                   int32_t max_seq_len, int32_t top_k, float* scores, int32_t scores_stride,
+                   int32_t* indices, int32_t* counts, void* stream);
+size_t mla_dsa_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_seq_len,
+                               int32_t top_k, int32_t num_splits_hint);
+int mla_dsa_decode(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+                   int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                   const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                   int32_t index_heads, const void* index_q, const float* index_w,
+                   const void* index_k, const float* index_k_scale, int32_t top_k,
+                   float softmax_scale, void* out, int32_t* indices_out, void* workspace,
+                   size_t workspace_bytes, int32_t num_splits_hint, void* stream);
+
+/*
  * mla_profile_enable / mla_profile_collect — stage timing for benchmarks.
  * While enabled (max_calls > 0), each mla_decode / mla_decode_fp8 /
  * mla_decode_step / mla_decode_step_fp8 call records
@@ -255,11 +317,14 @@ insert).  Events come from a pool of max_calls sets created here
  * mla_profile_enable(0) releases the pool.  mla_profile_collect waits for the
  * recorded events and writes, per stage, the summed milliseconds over the
  * timed calls into stage_ms[3] (prep, decode, combine) and the call count into
- * *calls, then empties the pool for reuse.  Each recorded event adds a few
+ * *calls, then empties the pool for reuse.  mla_profile_collect_calls writes
+ * each timed call's three stage times instead (stage_ms[3 * c + k] for call
+ * c in order; MLA_ERR_SHAPE if more than max_calls calls were timed).  Each recorded event adds a few
  * microseconds to the stage it closes.  Not thread-safe; for benchmarks only.
  */
 int mla_profile_enable(int32_t max_calls);
 int mla_profile_collect(double* stage_ms, int32_t* calls);
+int mla_profile_collect_calls(double* stage_ms, int32_t max_calls, int32_t* calls);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* mla_status_string(int status);

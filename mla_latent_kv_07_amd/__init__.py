@@ -12,11 +12,15 @@ from ._lib import (  # noqa: F401
     decode,
     decode_step,
     decode_workspace_bytes,
+    dsa_decode,
+    dsa_select,
+    dsa_workspace_bytes,
     lib_path,
     load,
     prefill,
     prefill_workspace_bytes,
     profile_collect,
+    profile_collect_calls,
     profile_enable,
     status_string,
 )

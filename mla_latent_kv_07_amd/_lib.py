@@ -65,6 +65,16 @@ def load() -> ctypes.CDLL:
     lib.mla_decode_step.restype = ctypes.c_int
     lib.mla_decode_step_fp8.argtypes = lib.mla_decode_step.argtypes
     lib.mla_decode_step_fp8.restype = ctypes.c_int
+    lib.mla_dsa_select.argtypes = [I32, P, P, P, P, P, I32, P, I32, I32, I32, P, I32, P, P, P]
+    lib.mla_dsa_select.restype = ctypes.c_int
+    lib.mla_dsa_workspace_bytes.argtypes = [DP, I32, I32, I32, I32]
+    lib.mla_dsa_workspace_bytes.restype = SZ
+    lib.mla_dsa_decode.argtypes = [DP, P, P, P, I32, P, I32, P, I32, I32, I32, P, P, P, P, I32, F,
+                                   P, P, P, SZ, I32, P]
+    lib.mla_dsa_decode.restype = ctypes.c_int
+    lib.mla_profile_collect_calls.argtypes = [ctypes.POINTER(ctypes.c_double), I32,
+                                              ctypes.POINTER(I32)]
+    lib.mla_profile_collect_calls.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_profile_enable.argtypes = [I32]
@@ -264,6 +274,103 @@ def prefill(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, *,
     return out
 
 
+IDX_DIM = 128  # index query / key width of the sparse-attention indexer
+
+
+def _check_index(index_q, index_w, index_k, index_k_scale, bsz, num_blocks, dev):
+    import torch
+    hi = index_q.shape[1]
+    _check(index_q, "index_q", torch.uint8, (bsz, hi, IDX_DIM), dev)
+    _check(index_w, "index_w", torch.float32, (bsz, hi), dev)
+    _check(index_k, "index_k", torch.uint8, (num_blocks, PAGE, IDX_DIM), dev)
+    _check(index_k_scale, "index_k_scale", torch.float32, (num_blocks, PAGE), dev)
+    return hi
+
+
+def dsa_select(index_q, index_w, index_k, index_k_scale, block_table, seq_lens,
+               max_seq_len: int, top_k: int, *, scores=None, indices=None, counts=None,
+               stream=None):
+    """mla_dsa_select: index scores of the cached positions and the top-k
+    selection.  index_q uint8 [B, Hi, 128] (E4M3), index_w fp32 [B, Hi],
+    index_k uint8 [num_blocks, 64, 128] (E4M3), index_k_scale fp32
+    [num_blocks, 64].  Returns (scores fp32 [B, max_seq_len], indices int32
+    [B, top_k] ascending with -1 padding, counts int32 [B])."""
+    import torch
+    bsz = index_q.shape[0]
+    dev = index_q.device
+    hi = _check_index(index_q, index_w, index_k, index_k_scale, bsz, index_k.shape[0], dev)
+    _check(block_table, "block_table", torch.int32, None, dev)
+    _check(seq_lens, "seq_lens", torch.int32, (bsz,), dev)
+    if scores is None:
+        scores = torch.empty((bsz, max_seq_len), dtype=torch.float32, device=dev)
+    if indices is None:
+        indices = torch.empty((bsz, top_k), dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty((bsz,), dtype=torch.int32, device=dev)
+    _check(scores, "scores", torch.float32, None, dev)
+    if scores.dim() != 2 or scores.shape[0] != bsz:
+        raise ValueError("scores: expected [B, stride]")
+    _check(indices, "indices", torch.int32, (bsz, top_k), dev)
+    _check(counts, "counts", torch.int32, (bsz,), dev)
+    st = load().mla_dsa_select(hi, _ptr(index_q), _ptr(index_w), _ptr(index_k),
+                               _ptr(index_k_scale), _ptr(block_table), block_table.shape[1],
+                               _ptr(seq_lens), bsz, max_seq_len, top_k, _ptr(scores),
+                               scores.shape[1], _ptr(indices), _ptr(counts), _stream(stream))
+    if st != 0:
+        raise MLAError(st, "mla_dsa_select")
+    return scores, indices, counts
+
+
+def dsa_workspace_bytes(heads: int, batch: int, max_seq_len: int, top_k: int,
+                        num_splits_hint: int = 0) -> int:
+    d = dims(heads)
+    return int(load().mla_dsa_workspace_bytes(ctypes.byref(d), batch, max_seq_len, top_k,
+                                              num_splits_hint))
+
+
+def dsa_decode(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, index_q, index_w,
+               index_k, index_k_scale, top_k: int, *, softmax_scale: float | None = None,
+               out=None, indices_out=None, workspace=None, num_splits_hint: int = 0,
+               stream=None):
+    """mla_dsa_decode: top-k selection by the index scores, then the MLA
+    decode of one new token per sequence (q bf16 [B, 1, H, 192], q_pe rotated)
+    over the kept positions of the bf16 cache.  Returns out bf16
+    [B, 1, H, 128]; ``indices_out`` (int32 [B, top_k]), when given, receives
+    the kept positions."""
+    import torch
+    bsz, q_len, heads = q.shape[0], q.shape[1], q.shape[2]
+    dev = cache.device
+    if q_len != 1:
+        raise ValueError("dsa_decode: one new token per sequence (q_len 1)")
+    _check(q, "q", torch.bfloat16, (bsz, 1, heads, NOPE + ROPE), dev)
+    _check(kv_b, "kv_b", torch.bfloat16, (heads * (NOPE + VDIM), LATENT), dev)
+    _check_cache(cache, False, dev)
+    _check(block_table, "block_table", torch.int32, None, dev)
+    _check(seq_lens, "seq_lens", torch.int32, (bsz,), dev)
+    hi = _check_index(index_q, index_w, index_k, index_k_scale, bsz, cache.shape[0], dev)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(NOPE + ROPE)
+    if out is None:
+        out = torch.empty((bsz, 1, heads, VDIM), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (bsz, 1, heads, VDIM), dev)
+    if indices_out is not None:
+        _check(indices_out, "indices_out", torch.int32, (bsz, top_k), dev)
+    need = dsa_workspace_bytes(heads, bsz, max_seq_len, top_k, num_splits_hint)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    d = dims(heads)
+    st = load().mla_dsa_decode(ctypes.byref(d), _ptr(q), _ptr(kv_b), _ptr(cache), cache.shape[0],
+                               _ptr(block_table), block_table.shape[1], _ptr(seq_lens), bsz,
+                               max_seq_len, hi, _ptr(index_q), _ptr(index_w), _ptr(index_k),
+                               _ptr(index_k_scale), top_k, softmax_scale, _ptr(out),
+                               _ptr(indices_out), _ptr(workspace), workspace.numel(),
+                               num_splits_hint, _stream(stream))
+    if st != 0:
+        raise MLAError(st, "mla_dsa_decode")
+    return out
+
+
 STAGES = ("prep", "decode", "combine")
 
 
@@ -282,3 +389,13 @@ def profile_collect() -> tuple[dict, int]:
     if st != 0:
         raise MLAError(st, "mla_profile_collect")
     return {k: ms[i] for i, k in enumerate(STAGES)}, int(calls.value)
+
+
+def profile_collect_calls(max_calls: int) -> list[tuple[float, float, float]]:
+    """Each timed call's three stage times in milliseconds, in call order."""
+    ms = (ctypes.c_double * (3 * max(int(max_calls), 1)))()
+    calls = ctypes.c_int32()
+    st = load().mla_profile_collect_calls(ms, int(max_calls), ctypes.byref(calls))
+    if st != 0:
+        raise MLAError(st, "mla_profile_collect_calls")
+    return [(ms[3 * c], ms[3 * c + 1], ms[3 * c + 2]) for c in range(int(calls.value))]

@@ -136,6 +136,24 @@ int mla_profile_collect(double* stage_ms, int32_t* calls) {
   return MLA_OK;
 }
 
+int mla_profile_collect_calls(double* stage_ms, int32_t max_calls, int32_t* calls) {
+  if (!stage_ms || !calls) return MLA_ERR_NULL;
+  if (max_calls < g_prof.used) return MLA_ERR_SHAPE;
+  for (int c = 0; c < g_prof.used; ++c) {
+    if (hipEventSynchronize(g_prof.ev[c * kMarks + kStages]) != hipSuccess) return MLA_ERR_HIP;
+    for (int k = 0; k < kStages; ++k) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, g_prof.ev[c * kMarks + k], g_prof.ev[c * kMarks + k + 1]) !=
+          hipSuccess)
+        return MLA_ERR_HIP;
+      stage_ms[c * kStages + k] = ms;
+    }
+  }
+  *calls = g_prof.used;
+  g_prof.used = 0;
+  return MLA_OK;
+}
+
 int mla_abi_version(void) { return 1; }
 
 const char* mla_status_string(int status) {
@@ -388,6 +406,136 @@ int mla_prefill(const mla_dims* dims, const void* q, const void* kv_b, const voi
   prof_mark(pc, 2, s);
   prof_mark(pc, 3, s);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+namespace {
+
+constexpr int kMaxTopK = 1 << 16;
+constexpr int kMaxIndexHeads = 1024;
+
+int64_t dsa_lpad(int32_t max_seq_len) { return ((int64_t)max_seq_len + 63) / 64 * 64; }
+int dsa_kpages(int32_t max_seq_len, int32_t top_k) {
+  const int ks = top_k < max_seq_len ? top_k : max_seq_len;
+  return (ks + kPage - 1) / kPage;
+}
+
+struct DsaLayout {
+  size_t off_scores = 0, off_kept = 0, off_counts = 0, off_dbt = 0, off_dense = 0, off_dec = 0,
+         total = 0;
+};
+
+DsaLayout make_dsa_layout(int heads, int batch, int32_t max_seq_len, int32_t top_k, int hint) {
+  DsaLayout L;
+  const int kp = dsa_kpages(max_seq_len, top_k);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.off_scores = take((size_t)batch * dsa_lpad(max_seq_len) * 4);
+  L.off_kept = take((size_t)batch * top_k * 4);
+  L.off_counts = take((size_t)batch * 4);
+  L.off_dbt = take((size_t)batch * kp * 4);
+  L.off_dense = take((size_t)batch * kp * kPageBytes);
+  L.off_dec = take(make_layout(heads, batch, 1, hint).total);
+  L.total = off + 256;  // the workspace pointer is rounded up to 256 bytes
+  return L;
+}
+
+int check_index(int32_t index_heads, const void* index_q, const float* index_w,
+                const void* index_k, const float* index_k_scale, int32_t top_k) {
+  if (index_heads < 1 || index_heads > kMaxIndexHeads || top_k < 1 || top_k > kMaxTopK)
+    return MLA_ERR_SHAPE;
+  if (!index_q || !index_w || !index_k || !index_k_scale) return MLA_ERR_NULL;
+  return MLA_OK;
+}
+
+}  // namespace
+
+int mla_dsa_select(int32_t index_heads, const void* index_q, const float* index_w,
+                   const void* index_k, const float* index_k_scale, const int32_t* block_table,
+                   int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
+                   int32_t max_seq_len, int32_t top_k, float* scores, int32_t scores_stride,
+                   int32_t* indices, int32_t* counts, void* stream) {
+  if (batch < 0 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeqLen ||
+      scores_stride < max_seq_len)
+    return MLA_ERR_SHAPE;
+  if (bt_stride < (max_seq_len + kPage - 1) / kPage) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  int st = check_index(index_heads, index_q, index_w, index_k, index_k_scale, top_k);
+  if (st != MLA_OK) return st;
+  if (!block_table || !seq_lens || !scores || !indices) return MLA_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_index_scores(static_cast<const uint8_t*>(index_q), index_w, index_heads,
+                                     static_cast<const uint8_t*>(index_k), index_k_scale,
+                                     block_table, bt_stride, seq_lens, batch, max_seq_len, scores,
+                                     scores_stride, s);
+  if (e == hipSuccess) e = launch_topk(scores, scores_stride, seq_lens, batch, top_k, indices,
+                                       counts, s);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+size_t mla_dsa_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_seq_len,
+                               int32_t top_k, int32_t num_splits_hint) {
+  if (check_dims(dims) != MLA_OK) return 0;
+  if (batch < 0 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeqLen ||
+      top_k < 1 || top_k > kMaxTopK || num_splits_hint < 0 || num_splits_hint > kMaxHint)
+    return 0;
+  return make_dsa_layout(dims->heads, batch, max_seq_len, top_k, num_splits_hint).total;
+}
+
+int mla_dsa_decode(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+                   int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                   const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                   int32_t index_heads, const void* index_q, const float* index_w,
+                   const void* index_k, const float* index_k_scale, int32_t top_k,
+                   float softmax_scale, void* out, int32_t* indices_out, void* workspace,
+                   size_t workspace_bytes, int32_t num_splits_hint, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeqLen ||
+      num_blocks < 1 || num_splits_hint < 0 || num_splits_hint > kMaxHint)
+    return MLA_ERR_SHAPE;
+  if (bt_stride < (max_seq_len + kPage - 1) / kPage) return MLA_ERR_SHAPE;
+  if (!std::isfinite(softmax_scale) || softmax_scale <= 0.f) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  st = check_index(index_heads, index_q, index_w, index_k, index_k_scale, top_k);
+  if (st != MLA_OK) return st;
+  if (!q || !kv_b || !cache || !block_table || !seq_lens || !out) return MLA_ERR_NULL;
+  if (!workspace) return MLA_ERR_WORKSPACE;
+  const DsaLayout L = make_dsa_layout(dims->heads, batch, max_seq_len, top_k, num_splits_hint);
+  if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  char* ws = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
+  float* scores = reinterpret_cast<float*>(ws + L.off_scores);
+  int32_t* kept = indices_out ? indices_out : reinterpret_cast<int32_t*>(ws + L.off_kept);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.off_counts);
+  int32_t* dense_bt = reinterpret_cast<int32_t*>(ws + L.off_dbt);
+  uint16_t* dense = reinterpret_cast<uint16_t*>(ws + L.off_dense);
+  const int kp = dsa_kpages(max_seq_len, top_k);
+  const int ks = top_k < max_seq_len ? top_k : max_seq_len;
+  const int lpad = (int)dsa_lpad(max_seq_len);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // stage marks of the selection (index scores, top-k, gather); the decode
+  // over the kept rows takes the next profile slot
+  const int pc = g_prof.used < g_prof.max_calls ? g_prof.used++ : -1;
+  prof_mark(pc, 0, s);
+  hipError_t e = launch_index_scores(static_cast<const uint8_t*>(index_q), index_w, index_heads,
+                                     static_cast<const uint8_t*>(index_k), index_k_scale,
+                                     block_table, bt_stride, seq_lens, batch, max_seq_len, scores,
+                                     lpad, s);
+  prof_mark(pc, 1, s);
+  if (e == hipSuccess) e = launch_topk(scores, lpad, seq_lens, batch, top_k, kept, counts, s);
+  prof_mark(pc, 2, s);
+  if (e == hipSuccess)
+    e = launch_gather(static_cast<const uint16_t*>(cache), block_table, bt_stride, kept, top_k,
+                      counts, batch, kp, dense, dense_bt, s);
+  prof_mark(pc, 3, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  return decode_any(false, nullptr, dims, q, kv_b, dense, batch * kp, dense_bt, kp, counts, batch,
+                    1, ks, softmax_scale, out, ws + L.off_dec,
+                    make_layout(dims->heads, batch, 1, num_splits_hint).total, num_splits_hint,
+                    stream);
 }
 
 }  // extern "C"
