@@ -20,6 +20,12 @@ float64 oracle on a bounded sample of the same workload.
 ``value`` and the roofline then count 656 bytes per cached position, and the
 CPU baseline times the FP8 oracle.  The FP8 cache is filled from the same
 synthetic latent rows (times 2^6, cast to E4M3 by torch; scale byte 2^-6).
+
+``--workload prefill_v3_b2_s4096`` / ``prefill_v3_chunk_b4`` time the prefill
+(mla_cache_insert of every new token + mla_prefill) in new tokens/s against the
+bf16 matrix-core peak; ``--workload dsa_v3_b64_l8192_k2048`` times the sparse
+decode (mla_cache_insert + mla_dsa_decode keeping 2048 of 8192 positions) in
+new tokens/s, with the roofline of its longest launch.
 """
 from __future__ import annotations
 
@@ -218,6 +224,141 @@ def prefill_main(args):
     print(json.dumps(result), flush=True)
 
 
+def dsa_cpu_baseline(d, budget_s: float) -> dict:
+    """The float64 oracle of the sparse decode (index scores, top-k, decode
+    over the kept positions) one sequence at a time until the budget is
+    spent; scaled to new tokens/s of the whole batch."""
+    from threadpoolctl import threadpool_info
+    from oracle import dsa
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    done, t = 0, 0.0
+    while done < d["batch"] and t < budget_s:
+        b = done
+        n = int(d["seq_lens"][b])
+        t0 = time.perf_counter()
+        sc = dsa.index_scores(d["index_q"], d["index_w"], d["index_k"], d["index_k_scale"],
+                              d["block_table"], n, b)
+        pos = dsa.topk_positions(sc, d["top_k"])
+        dsa.decode_sparse(d["q"][b:b + 1], d["kv_b"], d["cache_ref"], d["block_table"][b:b + 1],
+                          d["seq_lens"][b:b + 1], [pos], softmax_scale=d["softmax_scale"])
+        t += time.perf_counter() - t0
+        done += 1
+    return {"value": round(done / t, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {d['batch']} sequences of {d['name']} through the float64 "
+                      f"oracle (index scores, top-{d['top_k']}, expanded-form decode over the "
+                      f"kept positions; {t:.1f} s), scaled to the batch"}
+
+
+def dsa_main(args):
+    """Sparse decode: one step = the insert of the new token (mla_cache_insert)
+    and mla_dsa_decode (index scores, top-k, gather of the kept rows, then
+    prep / decode / combine over them); q_pe arrives rotated.  value = new
+    tokens per second; the roofline reports the launch that takes the most
+    time, against HBM bandwidth."""
+    import numpy as np
+    import torch
+    import mla_latent_kv_07_amd as mla
+    import workloads as wl
+
+    d = wl.make_dsa_workload(args.workload)
+    bsz, q_len, heads, top_k = d["batch"], d["q_len"], d["heads"], d["top_k"]
+    seq_lens = d["seq_lens"]
+    max_len = int(seq_lens.max())
+    to = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+                    if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda())
+    cache, kv_a, rms_w = to(d["cache"]), to(d["kv_a"]), to(d["rms_w"])
+    q, kv_b = to(d["q"]), to(d["kv_b"])
+    bt, sl = to(d["block_table"]), to(d["seq_lens"])
+    iq, iw, ik, iks = (to(d["index_q"]), to(d["index_w"]), to(d["index_k"]),
+                       to(d["index_k_scale"]))
+    out = torch.empty((bsz, q_len, heads, wl.VDIM), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.dsa_workspace_bytes(heads, bsz, max_len, top_k), dtype=torch.uint8,
+                     device="cuda")
+    eps = float(np.float32(wl.EPS))
+
+    def step():
+        mla.cache_insert(kv_a, rms_w, bt, sl, cache, eps=eps, heads=heads)
+        mla.dsa_decode(q, kv_b, cache, bt, sl, max_len, iq, iw, ik, iks, top_k, out=out,
+                       workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    run = step
+    if not args.eager:
+        # captured once and replayed: the library allocates nothing and records
+        # no memset
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mla.profile_enable(2 * args.steps)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    per_call = mla.profile_collect_calls(2 * args.steps)
+    mla.profile_enable(0)
+    assert len(per_call) == 2 * args.steps
+    names = ("index", "topk", "gather", "prep", "decode", "combine")
+    stage = {k: 0.0 for k in names}
+    for c in range(args.steps):
+        for i in range(3):
+            stage[names[i]] += per_call[2 * c][i] / args.steps
+            stage[names[3 + i]] += per_call[2 * c + 1][i] / args.steps
+    ms_step = wall * 1e3 / args.steps
+    kept = int(np.minimum(seq_lens, top_k).sum())
+    kept_lens = np.minimum(seq_lens, top_k)
+    launches = {
+        "index": ("mla::index_score_kernel (FP8 index scores)",
+                  wl.index_bytes(seq_lens, bsz, d["index_heads"]),
+                  "136 B per cached position (128 B E4M3 key, 4 B scale, 4 B score)",
+                  int(seq_lens.sum())),
+        "gather": ("mla::gather_kernel (kept rows into dense pages)", wl.gather_bytes(kept),
+                   "2304 B per kept position (1152 B read, 1152 B written)", kept),
+        "decode": ("mla::decode_kernel (split-KV decode over the kept rows)",
+                   kept * wl.BYTES_PER_TOKEN, "1152 B per kept position (576 bf16)", kept),
+    }
+    dom = max(launches, key=lambda k: stage[k])
+    kname, kbytes, per_unit, units = launches[dom]
+    gbs = kbytes / (stage[dom] * 1e-3) / 1e9
+    result = {
+        "metric": "MLA sparse decode (DSA top-k) new tokens/s at V3 shape; % of HBM roofline",
+        "value": round(bsz * q_len / (ms_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": bsz, "q_len": q_len, "heads": heads,
+                   "context": "8192 each", "top_k": top_k, "index_heads": d["index_heads"],
+                   "page": 64, "kv_lora": 512, "rope": 64,
+                   "step": "mla_cache_insert + mla_dsa_decode (index, top-k, gather, prep, "
+                           "decode, combine)",
+                   "launch": "eager" if args.eager else "hip graph"},
+        "stage_ms": {k: round(v, 4) for k, v in stage.items()},
+        "stage_gbs": {k: round(launches[k][1] / (stage[k] * 1e-3) / 1e9, 1) for k in launches},
+        "alg_bytes_per_step": int(wl.index_bytes(seq_lens, bsz, d["index_heads"])
+                                  + wl.decode_bytes(kept_lens, bsz, q_len, heads)),
+        "roofline": {"kernel": kname, "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "per_unit": per_unit, "units_per_launch": units},
+    }
+    if not args.no_cpu:
+        from oracle import cache_insert
+        d["cache_ref"] = cache_insert(d["cache"], d["kv_a"], d["rms_w"], d["block_table"],
+                                      d["seq_lens"], q_len, eps, wl.ROPE_BASE, wl.LATENT)
+        result["cpu_baseline"] = dsa_cpu_baseline(d, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -231,6 +372,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.workload in wl.PREFILL:
         return prefill_main(args)
+    if args.workload in wl.DSA:
+        return dsa_main(args)
     d = wl.make_workload(args.workload)
     bsz, q_len, heads = d["batch"], d["q_len"], d["heads"]
     seq_lens = d["seq_lens"]

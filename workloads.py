@@ -81,6 +81,25 @@ WORKLOADS.update({
 })
 PREFILL = ["prefill_v3_b2_s4096", "prefill_v3_chunk_b4"]
 
+# Sparse decode (DeepSeek Sparse Attention) workloads: a decode workload, the
+# number of kept positions and the index heads (64 heads of width 128, the
+# indexer shapes observed in the V3.2 run).
+DSA = {
+    "dsa_v3_b64_l8192_k2048": dict(base="v3_b64_l8192", top_k=2048, index_heads=64,
+                                   description="the V3 decode workload (64 sequences of 8192 "
+                                               "positions, 128 heads) keeping 2048 positions "
+                                               "per sequence by 64 FP8 index heads"),
+}
+
+
+def make_dsa_workload(name: str) -> dict:
+    w = DSA[name]
+    d = make_workload(w["base"])
+    d.update(make_index_inputs(d, index_heads=w["index_heads"], seed=1))
+    d["top_k"] = w["top_k"]
+    d["name"] = name
+    return d
+
 
 def draw_lens(rng: np.random.Generator, spec: str, batch: int) -> np.ndarray:
     kind, *args = spec.split(":")
@@ -219,3 +238,17 @@ def prefill_flops(seq_lens, q_len: int, heads: int) -> tuple[int, int]:
 
 def insert_bytes(batch: int, q_len: int) -> int:
     return batch * q_len * ENTRY * 2 * 2 + LATENT * 2 + 8 * batch
+
+
+INDEX_BYTES_PER_TOKEN = 128 + 4 + 4  # E4M3 key, its fp32 scale, the fp32 score written
+
+
+def index_bytes(seq_lens, batch: int, index_heads: int) -> int:
+    """Bytes the index-score launch must move: every cached position's key,
+    scale and score, the queries and weights once."""
+    return int(np.sum(seq_lens)) * INDEX_BYTES_PER_TOKEN + batch * index_heads * (128 + 4)
+
+
+def gather_bytes(kept: int) -> int:
+    """Bytes the gather launch moves: each kept row read and written once."""
+    return kept * BYTES_PER_TOKEN * 2
