@@ -351,6 +351,20 @@ def dsa_main(args):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": None, "per_unit": per_unit, "units_per_launch": units},
     }
+    tr_path = os.path.join(ROOT, "profiles", "dsa_kernel_traffic.json")
+    if os.path.exists(tr_path):
+        tr = json.load(open(tr_path))
+        got = tr.get("kernels", {}).get(dom)
+        if (tr.get("workload") == args.workload and got is not None
+                and tr.get("kernel_source_sha") == kernel_sha(("dsa.hip", "decode.hip",
+                                                               "mla_common.h"))):
+            result["roofline"]["traffic"] = got
+    if args.calib_copy_mib > 0:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu:
         from oracle import cache_insert
         d["cache_ref"] = cache_insert(d["cache"], d["kv_a"], d["rms_w"], d["block_table"],
@@ -500,10 +514,10 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def kernel_sha() -> str:
+def kernel_sha(files=("decode.hip", "mla_common.h")) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("decode.hip", "mla_common.h"):
+    for f in files:
         h.update(open(os.path.join(ROOT, "mla_latent_kv_07_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

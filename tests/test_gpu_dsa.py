@@ -144,6 +144,8 @@ SMALL = [
     ("multi_page_k200", 3, 32, [2000, 257, 1500], 200, 64),
     ("keep_all", 3, 16, [5, 130, 190], 256, 4),
     ("k1", 2, 16, [77, 1], 1, 16),
+    # longer than the 16384 positions top-k holds in registers: the re-read path
+    ("long_reread", 2, 16, [20000, 300], 3000, 8),
 ]
 
 
