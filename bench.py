@@ -224,6 +224,33 @@ def prefill_main(args):
     print(json.dumps(result), flush=True)
 
 
+def finite_bf16(bits):
+    """bf16 bit patterns with the non-finite ones (the unused-slot sentinels)
+    replaced by zero."""
+    import numpy as np
+    v = (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return np.where(np.isfinite(v), bits, np.uint16(0)).astype(np.uint16)
+
+
+def fp8_cache(cache):
+    """FP8 rows from the synthetic bf16 latent rows: x * 2^6 cast to E4M3 by
+    torch, scale byte 127 - 6, rope bf16 bytes, zero padding."""
+    import torch
+    import mla_latent_kv_07_amd as mla
+    import workloads as wl
+    lat = torch.nan_to_num(cache[..., :wl.LATENT].float(), nan=0.0, posinf=0.0, neginf=0.0)
+    codes = (lat * 64.0).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    rope = torch.nan_to_num(cache[..., wl.LATENT:].float(), nan=0.0).to(torch.bfloat16)
+    rope = rope.contiguous().view(torch.uint8)
+    tail = torch.zeros((*codes.shape[:2], mla.FP8_ROW_BYTES - 640), dtype=torch.uint8,
+                       device="cuda")
+    tail[..., 0] = 127 - 6
+    out = torch.cat([codes, rope, tail], dim=-1).contiguous()
+    del lat, codes, rope, tail
+    torch.cuda.synchronize()
+    return out
+
+
 def dsa_cpu_baseline(d, budget_s: float) -> dict:
     """The float64 oracle of the sparse decode (index scores, top-k, decode
     over the kept positions) one sequence at a time until the budget is
@@ -276,11 +303,15 @@ def dsa_main(args):
     ws = torch.empty(mla.dsa_workspace_bytes(heads, bsz, max_len, top_k), dtype=torch.uint8,
                      device="cuda")
     eps = float(np.float32(wl.EPS))
+    fp8 = args.cache == "fp8"
+    row_bytes = mla.FP8_ROW_BYTES if fp8 else wl.BYTES_PER_TOKEN
+    if fp8:
+        cache = fp8_cache(cache)
 
     def step():
-        mla.cache_insert(kv_a, rms_w, bt, sl, cache, eps=eps, heads=heads)
+        mla.cache_insert(kv_a, rms_w, bt, sl, cache, eps=eps, heads=heads, fp8=fp8)
         mla.dsa_decode(q, kv_b, cache, bt, sl, max_len, iq, iw, ik, iks, top_k, out=out,
-                       workspace=ws)
+                       workspace=ws, fp8=fp8)
 
     for _ in range(args.warmup):
         step()
@@ -323,10 +354,12 @@ def dsa_main(args):
                   wl.index_bytes(seq_lens, bsz, d["index_heads"]),
                   "136 B per cached position (128 B E4M3 key, 4 B scale, 4 B score)",
                   int(seq_lens.sum())),
-        "gather": ("mla::gather_kernel (kept rows into dense pages)", wl.gather_bytes(kept),
-                   "2304 B per kept position (1152 B read, 1152 B written)", kept),
+        "gather": ("mla::gather_kernel (kept rows into dense pages)", 2 * kept * row_bytes,
+                   f"{2 * row_bytes} B per kept position ({row_bytes} B read, {row_bytes} B "
+                   f"written)", kept),
         "decode": ("mla::decode_kernel (split-KV decode over the kept rows)",
-                   kept * wl.BYTES_PER_TOKEN, "1152 B per kept position (576 bf16)", kept),
+                   kept * row_bytes, f"{row_bytes} B per kept position "
+                   f"({'FP8 row' if fp8 else '576 bf16'})", kept),
     }
     dom = max(launches, key=lambda k: stage[k])
     kname, kbytes, per_unit, units = launches[dom]
@@ -340,9 +373,10 @@ def dsa_main(args):
         "config": {"workload": args.workload, "batch": bsz, "q_len": q_len, "heads": heads,
                    "context": "8192 each", "top_k": top_k, "index_heads": d["index_heads"],
                    "page": 64, "kv_lora": 512, "rope": 64,
-                   "step": "mla_cache_insert + mla_dsa_decode (index, top-k, gather, prep, "
-                           "decode, combine)",
-                   "launch": "eager" if args.eager else "hip graph"},
+                   "step": ("mla_cache_insert_fp8 + mla_dsa_decode_fp8" if fp8 else
+                            "mla_cache_insert + mla_dsa_decode") + " (index, top-k, gather, "
+                           "prep, decode, combine)",
+                   "cache": args.cache, "launch": "eager" if args.eager else "hip graph"},
         "stage_ms": {k: round(v, 4) for k, v in stage.items()},
         "stage_gbs": {k: round(launches[k][1] / (stage[k] * 1e-3) / 1e9, 1) for k in launches},
         "alg_bytes_per_step": int(wl.index_bytes(seq_lens, bsz, d["index_heads"])
@@ -356,6 +390,7 @@ def dsa_main(args):
         tr = json.load(open(tr_path))
         got = tr.get("kernels", {}).get(dom)
         if (tr.get("workload") == args.workload and got is not None
+                and tr.get("cache", "bf16") == args.cache
                 and tr.get("kernel_source_sha") == kernel_sha(("dsa.hip", "decode.hip",
                                                                "mla_common.h"))):
             result["roofline"]["traffic"] = got
@@ -369,6 +404,12 @@ def dsa_main(args):
         from oracle import cache_insert
         d["cache_ref"] = cache_insert(d["cache"], d["kv_a"], d["rms_w"], d["block_table"],
                                       d["seq_lens"], q_len, eps, wl.ROPE_BASE, wl.LATENT)
+        if fp8:
+            # the oracle's own FP8 rows of that cache, decoded as their
+            # dequantised entries (exact in bf16)
+            from oracle import fp8 as ofp8
+            d["cache_ref"] = ofp8.f64_to_bf16_bits(
+                ofp8.dequantize_cache(ofp8.quantize_cache(finite_bf16(d["cache_ref"]))))
         result["cpu_baseline"] = dsa_cpu_baseline(d, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
@@ -405,18 +446,7 @@ def main():
     fp8 = args.cache == "fp8"
     row_bytes = mla.FP8_ROW_BYTES if fp8 else wl.BYTES_PER_TOKEN
     if fp8:
-        # FP8 rows from the same synthetic latent rows: x * 2^6 cast to E4M3 by
-        # torch, scale byte 127 - 6, rope bf16 bytes, zero padding
-        lat = torch.nan_to_num(cache[..., :wl.LATENT].float(), nan=0.0, posinf=0.0, neginf=0.0)
-        codes = (lat * 64.0).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
-        rope = torch.nan_to_num(cache[..., wl.LATENT:].float(), nan=0.0).to(torch.bfloat16)
-        rope = rope.contiguous().view(torch.uint8)
-        tail = torch.zeros((*codes.shape[:2], mla.FP8_ROW_BYTES - 640), dtype=torch.uint8,
-                           device="cuda")
-        tail[..., 0] = 127 - 6
-        cache = torch.cat([codes, rope, tail], dim=-1).contiguous()
-        del lat, codes, rope, tail
-        torch.cuda.synchronize()
+        cache = fp8_cache(cache)
 
     def step():
         if args.path == "step":
@@ -508,7 +538,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if not args.no_cpu:
-        fp8_host = cache.cpu().numpy() if fp8 else None
+        # FP8: the oracle quantises the same synthetic rows itself
+        fp8_host = None
+        if fp8:
+            from oracle import fp8 as ofp8
+            fp8_host = ofp8.quantize_cache(finite_bf16(d["cache"]))
         result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds, fp8_host,
                                               rotate=args.path == "step")
     print(json.dumps(result), flush=True)

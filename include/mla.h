@@ -273,15 +273,18 @@ int mla_prefill(const mla_dims* dims, const void* q, const void* kv_b, const voi
  *   indices      int32 [B, top_k], out; counts int32 [B] (NULL allowed), out
  * Two launches on `stream`; no workspace.  Errors as mla_decode.
  *
- * mla_dsa_workspace_bytes — bytes of device workspace mla_dsa_decode needs
- * (scores, kept positions, the kept rows gathered into dense pages:
- * batch * ceil(min(top_k, max_seq_len) / 64) * 73728 bytes, and the decode
- * workspace of q_len 1), or 0 if the arguments are invalid.
+ * mla_dsa_workspace_bytes — bytes of device workspace mla_dsa_decode and
+ * mla_dsa_decode_fp8 need (scores, kept positions, the kept rows gathered
+ * into dense pages: batch * ceil(min(top_k, max_seq_len) / 64) * 73728
+ * bytes, and the decode workspace of q_len 1), or 0 if the arguments are
+ * invalid.
  *
- * mla_dsa_decode — selection as above, then the MLA decode (as mla_decode,
- * q_len 1) over the kept positions only.
- *   q, kv_b, cache (bf16 only), num_blocks, block_table, bt_stride, seq_lens,
- *   max_seq_len, softmax_scale, out, num_splits_hint: as mla_decode
+ * mla_dsa_decode / mla_dsa_decode_fp8 — selection as above, then the MLA
+ * decode (as mla_decode / mla_decode_fp8, q_len 1) over the kept positions
+ * only.
+ *   q, kv_b, cache (bf16 rows, or the FP8 rows of mla_decode_fp8), num_blocks,
+ *   block_table, bt_stride, seq_lens, max_seq_len, softmax_scale, out,
+ *   num_splits_hint: as mla_decode
  *   index_*, top_k: as mla_dsa_select
  *   indices_out  int32 [B, top_k] or NULL: the kept positions
  *   workspace    device memory, >= mla_dsa_workspace_bytes; overwritten
@@ -303,6 +306,13 @@ int mla_dsa_decode(const mla_dims* dims, const void* q, const void* kv_b, const 
                    const void* index_k, const float* index_k_scale, int32_t top_k,
                    float softmax_scale, void* out, int32_t* indices_out, void* workspace,
                    size_t workspace_bytes, int32_t num_splits_hint, void* stream);
+int mla_dsa_decode_fp8(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+                       int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                       const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                       int32_t index_heads, const void* index_q, const float* index_w,
+                       const void* index_k, const float* index_k_scale, int32_t top_k,
+                       float softmax_scale, void* out, int32_t* indices_out, void* workspace,
+                       size_t workspace_bytes, int32_t num_splits_hint, void* stream);
 
 /*
  * mla_profile_enable / mla_profile_collect — stage timing for benchmarks.

@@ -72,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.mla_dsa_decode.argtypes = [DP, P, P, P, I32, P, I32, P, I32, I32, I32, P, P, P, P, I32, F,
                                    P, P, P, SZ, I32, P]
     lib.mla_dsa_decode.restype = ctypes.c_int
+    lib.mla_dsa_decode_fp8.argtypes = lib.mla_dsa_decode.argtypes
+    lib.mla_dsa_decode_fp8.restype = ctypes.c_int
     lib.mla_profile_collect_calls.argtypes = [ctypes.POINTER(ctypes.c_double), I32,
                                               ctypes.POINTER(I32)]
     lib.mla_profile_collect_calls.restype = ctypes.c_int
@@ -331,10 +333,11 @@ def dsa_workspace_bytes(heads: int, batch: int, max_seq_len: int, top_k: int,
 def dsa_decode(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, index_q, index_w,
                index_k, index_k_scale, top_k: int, *, softmax_scale: float | None = None,
                out=None, indices_out=None, workspace=None, num_splits_hint: int = 0,
-               stream=None):
-    """mla_dsa_decode: top-k selection by the index scores, then the MLA
-    decode of one new token per sequence (q bf16 [B, 1, H, 192], q_pe rotated)
-    over the kept positions of the bf16 cache.  Returns out bf16
+               stream=None, fp8: bool = False):
+    """mla_dsa_decode (fp8=False: cache bf16 [num_blocks, 64, 576]) or
+    mla_dsa_decode_fp8 (fp8=True: cache uint8 [num_blocks, 64, 656]): top-k
+    selection by the index scores, then the MLA decode of one new token per
+    sequence (q bf16 [B, 1, H, 192], q_pe rotated) over the kept positions.  Returns out bf16
     [B, 1, H, 128]; ``indices_out`` (int32 [B, top_k]), when given, receives
     the kept positions."""
     import torch
@@ -344,7 +347,7 @@ def dsa_decode(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, index_q,
         raise ValueError("dsa_decode: one new token per sequence (q_len 1)")
     _check(q, "q", torch.bfloat16, (bsz, 1, heads, NOPE + ROPE), dev)
     _check(kv_b, "kv_b", torch.bfloat16, (heads * (NOPE + VDIM), LATENT), dev)
-    _check_cache(cache, False, dev)
+    _check_cache(cache, fp8, dev)
     _check(block_table, "block_table", torch.int32, None, dev)
     _check(seq_lens, "seq_lens", torch.int32, (bsz,), dev)
     hi = _check_index(index_q, index_w, index_k, index_k_scale, bsz, cache.shape[0], dev)
@@ -360,14 +363,14 @@ def dsa_decode(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, index_q,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check(workspace, "workspace", torch.uint8, None, dev)
     d = dims(heads)
-    st = load().mla_dsa_decode(ctypes.byref(d), _ptr(q), _ptr(kv_b), _ptr(cache), cache.shape[0],
-                               _ptr(block_table), block_table.shape[1], _ptr(seq_lens), bsz,
-                               max_seq_len, hi, _ptr(index_q), _ptr(index_w), _ptr(index_k),
-                               _ptr(index_k_scale), top_k, softmax_scale, _ptr(out),
-                               _ptr(indices_out), _ptr(workspace), workspace.numel(),
-                               num_splits_hint, _stream(stream))
+    fn = load().mla_dsa_decode_fp8 if fp8 else load().mla_dsa_decode
+    st = fn(ctypes.byref(d), _ptr(q), _ptr(kv_b), _ptr(cache), cache.shape[0], _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), bsz, max_seq_len, hi, _ptr(index_q),
+            _ptr(index_w), _ptr(index_k), _ptr(index_k_scale), top_k, softmax_scale, _ptr(out),
+            _ptr(indices_out), _ptr(workspace), workspace.numel(), num_splits_hint,
+            _stream(stream))
     if st != 0:
-        raise MLAError(st, "mla_dsa_decode")
+        raise MLAError(st, "mla_dsa_decode_fp8" if fp8 else "mla_dsa_decode")
     return out
 
 

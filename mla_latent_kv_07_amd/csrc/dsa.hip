@@ -21,8 +21,9 @@
 //                       re-read them): radix select of the k-th largest score
 //                       (4 passes of 8 bits over order-preserving integer
 //                       keys), then a stable compaction in position order.
-//   gather_kernel       8 kept rows per wavefront: their 1152-byte cache rows
-//                       into a dense run of pages (identity block table).
+//   gather_kernel       8 kept rows per wavefront: their cache rows (1152-byte
+//                       bf16 or 656-byte FP8 rows) into a dense run of pages
+//                       (identity block table).
 #include "mla_common.h"
 
 namespace mla {
@@ -338,19 +339,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 }
 
 constexpr int kGatherRows = 8;  // kept rows per wavefront
-constexpr int kGatherLoads = kGatherRows * kChunk16 / 64;  // 16-byte pieces per lane
-static_assert(kGatherRows * kChunk16 % 64 == 0, "whole loads per lane");
 
-// Gather: each wavefront copies kGatherRows kept rows (consecutive kept
-// ranks, so consecutive dense rows); lanes 0 .. 7 look up the rows' cache
-// slots, every lane then issues all of its loads before its stores.
-__global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ cache,
+// Gather: each wavefront copies kGatherRows kept rows of ROW bytes (consecutive
+// kept ranks, so consecutive dense rows); lanes 0 .. 7 look up the rows' cache
+// slots, every lane then issues all of its 16-byte loads before its stores.
+// ROW: 1152 (bf16 rows) or 656 (FP8 rows).
+template <int ROW>
+__global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ cache,
                                                      const int32_t* __restrict__ block_table,
                                                      int bt_stride,
                                                      const int32_t* __restrict__ kept, int top_k,
                                                      const int32_t* __restrict__ counts, int kpages,
-                                                     uint16_t* __restrict__ dense,
+                                                     char* __restrict__ dense,
                                                      int32_t* __restrict__ dense_bt) {
+  constexpr int kPieces = ROW / 16;                         // 16-byte pieces per row
+  constexpr int kLoads = (kGatherRows * kPieces + 63) / 64;  // per lane
+  static_assert(ROW % 16 == 0, "rows of whole 16-byte pieces");
   const int b = blockIdx.y;
   if (blockIdx.x == 0)
     for (int p = threadIdx.x; p < kpages; p += 256) dense_bt[(int64_t)b * kpages + p] = b * kpages + p;
@@ -364,20 +368,20 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict_
     my_slot = (int64_t)block_table[(int64_t)b * bt_stride + p / kPage] * kPage + p % kPage;
   }
   // dense rows of sequence b are contiguous: rank j sits at row b * kpages * 64 + j
-  u16x8* dst = reinterpret_cast<u16x8*>(dense + ((int64_t)b * kpages * kPage + j0) * kEntry);
-  u16x8 v[kGatherLoads];
+  u16x8* dst = reinterpret_cast<u16x8*>(dense + ((int64_t)b * kpages * kPage + j0) * ROW);
+  u16x8 v[kLoads];
 #pragma unroll
-  for (int i = 0; i < kGatherLoads; ++i) {
+  for (int i = 0; i < kLoads; ++i) {
     const int q = i * 64 + lane;  // piece of the wavefront's rows
-    const int r = q / kChunk16;
-    const int64_t slot = __shfl(my_slot, r, 64);
-    if (j0 + r < n)
-      v[i] = reinterpret_cast<const u16x8*>(cache + slot * kEntry)[q - r * kChunk16];
+    const int r = q / kPieces;
+    const int64_t slot = __shfl(my_slot, r < kGatherRows ? r : 0, 64);
+    if (q < kGatherRows * kPieces && j0 + r < n)
+      v[i] = reinterpret_cast<const u16x8*>(cache + slot * ROW)[q - r * kPieces];
   }
 #pragma unroll
-  for (int i = 0; i < kGatherLoads; ++i) {
+  for (int i = 0; i < kLoads; ++i) {
     const int q = i * 64 + lane;
-    if (j0 + q / kChunk16 < n) dst[q] = v[i];
+    if (q < kGatherRows * kPieces && j0 + q / kPieces < n) dst[q] = v[i];
   }
 }
 
@@ -401,12 +405,18 @@ hipError_t launch_topk(const float* scores, int lpad, const int32_t* seq_lens, i
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const uint16_t* cache, const int32_t* block_table, int bt_stride,
+hipError_t launch_gather(bool fp8, const void* cache, const int32_t* block_table, int bt_stride,
                          const int32_t* kept, int top_k, const int32_t* counts, int batch,
-                         int kpages, uint16_t* dense, int32_t* dense_bt, hipStream_t stream) {
-  hipLaunchKernelGGL(gather_kernel, dim3((top_k + 4 * kGatherRows - 1) / (4 * kGatherRows), batch),
-                     dim3(256), 0, stream, cache,
-                     block_table, bt_stride, kept, top_k, counts, kpages, dense, dense_bt);
+                         int kpages, void* dense, int32_t* dense_bt, hipStream_t stream) {
+  const dim3 grid((top_k + 4 * kGatherRows - 1) / (4 * kGatherRows), batch);
+  if (fp8)
+    hipLaunchKernelGGL(gather_kernel<kFp8EntryBytes>, grid, dim3(256), 0, stream,
+                       static_cast<const char*>(cache), block_table, bt_stride, kept, top_k, counts,
+                       kpages, static_cast<char*>(dense), dense_bt);
+  else
+    hipLaunchKernelGGL(gather_kernel<kEntryBytes>, grid, dim3(256), 0, stream,
+                       static_cast<const char*>(cache), block_table, bt_stride, kept, top_k, counts,
+                       kpages, static_cast<char*>(dense), dense_bt);
   return hipGetLastError();
 }
 

@@ -485,13 +485,17 @@ size_t mla_dsa_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_
   return make_dsa_layout(dims->heads, batch, max_seq_len, top_k, num_splits_hint).total;
 }
 
-int mla_dsa_decode(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
-                   int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
-                   const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
-                   int32_t index_heads, const void* index_q, const float* index_w,
-                   const void* index_k, const float* index_k_scale, int32_t top_k,
-                   float softmax_scale, void* out, int32_t* indices_out, void* workspace,
-                   size_t workspace_bytes, int32_t num_splits_hint, void* stream) {
+namespace {
+
+// The two cache formats share the selection; the gather copies whole rows of
+// either format and the decode reads them as it reads the paged cache.
+int dsa_any(bool fp8, const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+            int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+            const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, int32_t index_heads,
+            const void* index_q, const float* index_w, const void* index_k,
+            const float* index_k_scale, int32_t top_k, float softmax_scale, void* out,
+            int32_t* indices_out, void* workspace, size_t workspace_bytes,
+            int32_t num_splits_hint, void* stream) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (batch < 0 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeqLen ||
@@ -511,7 +515,7 @@ int mla_dsa_decode(const mla_dims* dims, const void* q, const void* kv_b, const 
   int32_t* kept = indices_out ? indices_out : reinterpret_cast<int32_t*>(ws + L.off_kept);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.off_counts);
   int32_t* dense_bt = reinterpret_cast<int32_t*>(ws + L.off_dbt);
-  uint16_t* dense = reinterpret_cast<uint16_t*>(ws + L.off_dense);
+  char* dense = ws + L.off_dense;  // bf16 or FP8 rows, 64 per page
   const int kp = dsa_kpages(max_seq_len, top_k);
   const int ks = top_k < max_seq_len ? top_k : max_seq_len;
   const int lpad = (int)dsa_lpad(max_seq_len);
@@ -528,14 +532,42 @@ int mla_dsa_decode(const mla_dims* dims, const void* q, const void* kv_b, const 
   if (e == hipSuccess) e = launch_topk(scores, lpad, seq_lens, batch, top_k, kept, counts, s);
   prof_mark(pc, 2, s);
   if (e == hipSuccess)
-    e = launch_gather(static_cast<const uint16_t*>(cache), block_table, bt_stride, kept, top_k,
-                      counts, batch, kp, dense, dense_bt, s);
+    e = launch_gather(fp8, cache, block_table, bt_stride, kept, top_k, counts, batch, kp, dense,
+                      dense_bt, s);
   prof_mark(pc, 3, s);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  return decode_any(false, nullptr, dims, q, kv_b, dense, batch * kp, dense_bt, kp, counts, batch,
+  return decode_any(fp8, nullptr, dims, q, kv_b, dense, batch * kp, dense_bt, kp, counts, batch,
                     1, ks, softmax_scale, out, ws + L.off_dec,
                     make_layout(dims->heads, batch, 1, num_splits_hint).total, num_splits_hint,
                     stream);
+}
+
+}  // namespace
+
+int mla_dsa_decode(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+                   int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                   const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                   int32_t index_heads, const void* index_q, const float* index_w,
+                   const void* index_k, const float* index_k_scale, int32_t top_k,
+                   float softmax_scale, void* out, int32_t* indices_out, void* workspace,
+                   size_t workspace_bytes, int32_t num_splits_hint, void* stream) {
+  return dsa_any(false, dims, q, kv_b, cache, num_blocks, block_table, bt_stride, seq_lens, batch,
+                 max_seq_len, index_heads, index_q, index_w, index_k, index_k_scale, top_k,
+                 softmax_scale, out, indices_out, workspace, workspace_bytes, num_splits_hint,
+                 stream);
+}
+
+int mla_dsa_decode_fp8(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+                       int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                       const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                       int32_t index_heads, const void* index_q, const float* index_w,
+                       const void* index_k, const float* index_k_scale, int32_t top_k,
+                       float softmax_scale, void* out, int32_t* indices_out, void* workspace,
+                       size_t workspace_bytes, int32_t num_splits_hint, void* stream) {
+  return dsa_any(true, dims, q, kv_b, cache, num_blocks, block_table, bt_stride, seq_lens, batch,
+                 max_seq_len, index_heads, index_q, index_w, index_k, index_k_scale, top_k,
+                 softmax_scale, out, indices_out, workspace, workspace_bytes, num_splits_hint,
+                 stream);
 }
 
 }  // extern "C"

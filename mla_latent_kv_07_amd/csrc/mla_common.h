@@ -116,7 +116,7 @@ hipError_t launch_prefill(const uint16_t* q, const uint16_t* kv_b, const uint16_
 // sparse decode (dsa.hip): index scores [B][lpad] of the cached positions,
 // top-k selection (kept positions ascending, -1 past the count; counts may be
 // NULL) and the gather of the kept rows into kpages dense pages per sequence
-// with their identity block table [B][kpages]
+// (bf16 or FP8 rows) with their identity block table [B][kpages]
 hipError_t launch_index_scores(const uint8_t* index_q, const float* index_w, int index_heads,
                                const uint8_t* index_k, const float* index_k_scale,
                                const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
@@ -124,9 +124,9 @@ hipError_t launch_index_scores(const uint8_t* index_q, const float* index_w, int
                                hipStream_t stream);
 hipError_t launch_topk(const float* scores, int lpad, const int32_t* seq_lens, int batch,
                        int top_k, int32_t* kept, int32_t* counts, hipStream_t stream);
-hipError_t launch_gather(const uint16_t* cache, const int32_t* block_table, int bt_stride,
+hipError_t launch_gather(bool fp8, const void* cache, const int32_t* block_table, int bt_stride,
                          const int32_t* kept, int top_k, const int32_t* counts, int batch,
-                         int kpages, uint16_t* dense, int32_t* dense_bt, hipStream_t stream);
+                         int kpages, void* dense, int32_t* dense_bt, hipStream_t stream);
 
 hipError_t launch_combine(const uint16_t* o_part, const float* lse_part, PlanView plan,
                           const uint16_t* kv_b, int heads, int q_len, int batch, uint16_t* out,

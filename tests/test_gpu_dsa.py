@@ -257,3 +257,87 @@ def test_dsa_rejects_bad_arguments():
     small_ws = torch.empty(256, dtype=torch.uint8, device="cuda")
     with pytest.raises(MLAError):
         dsa_decode(*args, 64, workspace=small_ws)
+
+
+def test_dsa_decode_fp8_cache():
+    """mla_dsa_decode_fp8: the same selection (it does not depend on the latent
+    cache), the decode over the kept FP8 rows within the decode bound of the
+    oracle on the dequantised entries (exact in bf16), and, keeping every
+    position, bit-identical to mla_decode_fp8."""
+    torch = _torch()
+    from oracle import fp8 as ofp8
+    from mla_latent_kv_07_amd import decode, dsa_decode
+    say("dsa decode fp8 cache")
+    d = wl.make_inputs(3, 1, 128, [2000, 300, 4100], permute=True, seed=81)
+    ix = wl.make_index_inputs(d, index_heads=64, seed=82)
+    cache = filled(d)
+    v = (cache.astype(np.uint32) << 16).view(np.float32)
+    c8 = ofp8.quantize_cache(np.where(np.isfinite(v), cache, np.uint16(0)).astype(np.uint16))
+    deq = ofp8.f64_to_bf16_bits(ofp8.dequantize_cache(c8))
+    args = (dev(d["q"], torch), dev(d["kv_b"], torch), dev(c8, torch),
+            dev(d["block_table"], torch), dev(d["seq_lens"], torch), int(d["seq_lens"].max()),
+            dev(ix["index_q"], torch), dev(ix["index_w"], torch), dev(ix["index_k"], torch),
+            dev(ix["index_k_scale"], torch))
+    for top_k in (256, 1000):
+        idx_t = torch.empty((3, top_k), dtype=torch.int32, device="cuda")
+        out = dsa_decode(*args, top_k, softmax_scale=d["softmax_scale"], indices_out=idx_t,
+                         fp8=True)
+        torch.cuda.synchronize()
+        got, idx = out.float().cpu().numpy(), idx_t.cpu().numpy()
+        _, idx2, _ = run_select(d, ix, top_k, torch)
+        assert np.array_equal(idx, idx2)
+        check_decode(d, deq, got, idx, top_k, range(3))
+    out = dsa_decode(*args, 8192, softmax_scale=d["softmax_scale"], fp8=True)
+    dense = decode(args[0], args[1], args[2], args[3], args[4], args[5],
+                   softmax_scale=d["softmax_scale"], fp8=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dense)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_dsa_graph_replay_matches_eager(fp8):
+    """The sparse step (insert of the new token, then mla_dsa_decode) captured
+    as a HIP graph and replayed, as the benchmark runs it: every replay equals
+    the eager result bit for bit, with eager work between replays."""
+    torch = _torch()
+    import mla_latent_kv_07_amd as mla
+    from oracle import fp8 as ofp8
+    say(f"dsa graph replay fp8={fp8}")
+    d = wl.make_inputs(4, 1, 128, [3000, 700, 64, 5000], permute=True, seed=83)
+    ix = wl.make_index_inputs(d, index_heads=64, seed=84)
+    cache0 = d["cache"]
+    if fp8:
+        v = (cache0.astype(np.uint32) << 16).view(np.float32)
+        cache0 = ofp8.quantize_cache(np.where(np.isfinite(v), cache0, np.uint16(0)).astype(np.uint16))
+    kv_a, rms_w, q, kv_b = (dev(d[k], torch) for k in ("kv_a", "rms_w", "q", "kv_b"))
+    bt, sl = dev(d["block_table"], torch), dev(d["seq_lens"], torch)
+    iq, iw, ik, iks = (dev(ix[k], torch) for k in ("index_q", "index_w", "index_k",
+                                                   "index_k_scale"))
+    max_len, top_k = int(d["seq_lens"].max()), 1024
+    eps = float(np.float32(wl.EPS))
+    ws = torch.empty(mla.dsa_workspace_bytes(128, 4, max_len, top_k), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(cache, out):
+        mla.cache_insert(kv_a, rms_w, bt, sl, cache, eps=eps, heads=128, fp8=fp8)
+        return mla.dsa_decode(q, kv_b, cache, bt, sl, max_len, iq, iw, ik, iks, top_k, out=out,
+                              workspace=ws, fp8=fp8)
+
+    cache_e = dev(cache0, torch)
+    ref = step(cache_e, None).clone()
+    torch.cuda.synchronize()
+    cache_g = dev(cache0, torch)
+    out_g = torch.empty_like(ref)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(cache_g, out_g)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, ref), f"replay {r} differs from the eager result"
+        other = step(cache_e, None)
+        torch.cuda.synchronize()
+        assert torch.equal(other, ref)
