@@ -267,7 +267,7 @@ int mla_prefill(const mla_dims* dims, const void* q, const void* kv_b, const voi
  *   index_heads  Hi, 1..1024; index_q uint8 [B, Hi, 128]; index_w fp32 [B, Hi]
  *   index_k      uint8 [num_blocks, 64, 128]; index_k_scale fp32 [num_blocks, 64]
  *   block_table, bt_stride, seq_lens, max_seq_len: as mla_decode
- *   top_k        1..65536
+ *   top_k        1..65536; batch at most 65535 (all three sparse entry points)
  *   scores       fp32 [B, scores_stride] (scores_stride >= max_seq_len), out:
  *                entries n < seq_lens[b] written, the rest untouched
  *   indices      int32 [B, top_k], out; counts int32 [B] (NULL allowed), out

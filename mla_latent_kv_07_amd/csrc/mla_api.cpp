@@ -412,6 +412,7 @@ namespace {
 
 constexpr int kMaxTopK = 1 << 16;
 constexpr int kMaxIndexHeads = 1024;
+constexpr int kMaxDsaBatch = 65535;  // the batch is a grid dimension of the selection launches
 
 int64_t dsa_lpad(int32_t max_seq_len) { return ((int64_t)max_seq_len + 63) / 64 * 64; }
 int dsa_kpages(int32_t max_seq_len, int32_t top_k) {
@@ -458,7 +459,7 @@ int mla_dsa_select(int32_t index_heads, const void* index_q, const float* index_
                    int32_t bt_stride, const int32_t* seq_lens, int32_t batch,
                    int32_t max_seq_len, int32_t top_k, float* scores, int32_t scores_stride,
                    int32_t* indices, int32_t* counts, void* stream) {
-  if (batch < 0 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeqLen ||
+  if (batch < 0 || batch > kMaxDsaBatch || max_seq_len < 1 || max_seq_len > kMaxSeqLen ||
       scores_stride < max_seq_len)
     return MLA_ERR_SHAPE;
   if (bt_stride < (max_seq_len + kPage - 1) / kPage) return MLA_ERR_SHAPE;
@@ -479,7 +480,7 @@ int mla_dsa_select(int32_t index_heads, const void* index_q, const float* index_
 size_t mla_dsa_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_seq_len,
                                int32_t top_k, int32_t num_splits_hint) {
   if (check_dims(dims) != MLA_OK) return 0;
-  if (batch < 0 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeqLen ||
+  if (batch < 0 || batch > kMaxDsaBatch || max_seq_len < 1 || max_seq_len > kMaxSeqLen ||
       top_k < 1 || top_k > kMaxTopK || num_splits_hint < 0 || num_splits_hint > kMaxHint)
     return 0;
   return make_dsa_layout(dims->heads, batch, max_seq_len, top_k, num_splits_hint).total;
@@ -498,7 +499,7 @@ int dsa_any(bool fp8, const mla_dims* dims, const void* q, const void* kv_b, con
             int32_t num_splits_hint, void* stream) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (batch < 0 || batch > kMaxBatch || max_seq_len < 1 || max_seq_len > kMaxSeqLen ||
+  if (batch < 0 || batch > kMaxDsaBatch || max_seq_len < 1 || max_seq_len > kMaxSeqLen ||
       num_blocks < 1 || num_splits_hint < 0 || num_splits_hint > kMaxHint)
     return MLA_ERR_SHAPE;
   if (bt_stride < (max_seq_len + kPage - 1) / kPage) return MLA_ERR_SHAPE;
