@@ -28,7 +28,6 @@ import pytest
 
 import workloads as wl
 from oracle import cache_insert as oracle_insert
-from oracle import decode_expanded
 from oracle import dsa
 from oracle.fp8 import e4m3_decode
 
