@@ -638,9 +638,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     f32x4 sacc[NH][2];
     // the phases stay in order: moving the next phase's LDS reads up would
     // keep their registers live across this one
+    // wavefront priority: raised for the two matrix phases and lowered for
+    // the softmax, so that of the two wavefronts sharing a SIMD the one in a
+    // matrix phase issues first and the other's softmax fills its gaps
+    // (same-process A/B at the V3 shape: 142.7 -> 137.9 us per launch)
+    __builtin_amdgcn_s_setprio(1);
     score_chunk<NH, D, decltype(nc_c)::value, kKpd>(buf, sbase_even, sbase_odd, qreg, sacc, cc, doff,
                                               wave);
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     bf16x8 pk[NH];
     bool need;
     if (j >= jm)
@@ -651,6 +657,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     for (int h = 0; h < NH; ++h)
       *reinterpret_cast<MLA_LDS bf16x8*>(pb_lds + (wave * NH + h) * 1024 + lane * 16) = pk[h];
     ring_barrier();
+    __builtin_amdgcn_s_setprio(1);
     if constexpr (NW == 8) {
       pv_slice_lds<NW, NH>(buf, vbase, pb_lds, lane, oacc);
     } else {
@@ -668,6 +675,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
       dequant_rows<NW>(dq_src, dq_dst, wave, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     return need;
   };
 
