@@ -340,3 +340,19 @@ def test_dsa_graph_replay_matches_eager(fp8):
         other = step(cache_e, None)
         torch.cuda.synchronize()
         assert torch.equal(other, ref)
+
+
+@pytest.mark.parametrize("hint", [1, 3, 8])
+def test_dsa_decode_split_hint(hint):
+    """The sparse decode with an explicit split count per sequence (the
+    caller's num_splits_hint instead of the planner's choice): the same
+    selection, the decode within the bound of the oracle."""
+    torch = _torch()
+    say(f"dsa decode hint={hint}")
+    d = wl.make_inputs(3, 1, 128, [3000, 200, 5000], permute=True, seed=85)
+    ix = wl.make_index_inputs(d, index_heads=64, seed=86)
+    cache = filled(d)
+    got, idx = run_decode(d, cache, ix, 1500, torch, hint=hint)
+    _, idx2, _ = run_select(d, ix, 1500, torch)
+    assert np.array_equal(idx, idx2)
+    check_decode(d, cache, got, idx, 1500, range(3))
