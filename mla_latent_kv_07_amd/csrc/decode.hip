@@ -638,10 +638,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     f32x4 sacc[NH][2];
     // the phases stay in order: moving the next phase's LDS reads up would
     // keep their registers live across this one
-    // wavefront priority: raised for the two matrix phases and lowered for
+    // wavefront priority: raised for the two matrix phases (the P.V one
+    // from the probability writes and the barrier before it) and lowered for
     // the softmax, so that of the two wavefronts sharing a SIMD the one in a
     // matrix phase issues first and the other's softmax fills its gaps
-    // (same-process A/B at the V3 shape: 142.7 -> 137.9 us per launch)
+    // (same-process A/Bs at the V3 shape: 142.7 -> 137.9 us per launch, then
+    // 141.5 -> 138.1 us for raising it before the barrier)
     __builtin_amdgcn_s_setprio(1);
     score_chunk<NH, D, decltype(nc_c)::value, kKpd>(buf, sbase_even, sbase_odd, qreg, sacc, cc, doff,
                                               wave);
@@ -653,11 +655,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
       need = softmax_chunk<NH, kFirst, true>(sacc, pk, m_ref, l_run, lim);
     else
       need = softmax_chunk<NH, kFirst, false>(sacc, pk, m_ref, l_run, lim);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int h = 0; h < NH; ++h)
       *reinterpret_cast<MLA_LDS bf16x8*>(pb_lds + (wave * NH + h) * 1024 + lane * 16) = pk[h];
     ring_barrier();
-    __builtin_amdgcn_s_setprio(1);
     if constexpr (NW == 8) {
       pv_slice_lds<NW, NH>(buf, vbase, pb_lds, lane, oacc);
     } else {
