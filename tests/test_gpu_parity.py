@@ -138,20 +138,18 @@ def test_decode_parity_small(case):
     assert mx <= MAX_ABS and rr <= REL_RMS
 
 
-SAMPLES = {  # sampled (sequence, head) pairs checked at full size
-    "tiny_v2lite": ([0], None),
-    "v2lite_b32": ([0, 7, 31], [0, 5, 15]),
-    "v3_b64_l8192": ([0, 33, 63], [0, 77, 127]),
-    "v3_longskew_b8": ([0, 3, 7], [1, 64, 126]),
-    "v3_mtp_b128": ([0, 64, 127], [2, 50, 127]),
-}
+# Sequences the oracle checks at full size: every sequence (all heads, all
+# query tokens) except for the 128-sequence multi-token workload, where every
+# fourth sequence is checked (32 sequences spread over the whole item list, so
+# over every XCD's range of work items), all 128 heads and both tokens.
+FULL_BATCHES = {"v3_mtp_b128": list(range(0, 128, 4))}
 
 
 @pytest.mark.parametrize("name", wl.ORDER)
 def test_decode_parity_workload(name):
     """Full-size workload, chained insert -> decode on the GPU, in the launch
-    configuration the benchmark times (automatic split plan); the oracle
-    checks sampled sequences and heads."""
+    configuration the benchmark times (automatic split plan); every output
+    element of the checked sequences is compared with the float64 oracle."""
     torch = _torch()
     say(f"[decode workload] {name}")
     d = wl.make_workload(name)
@@ -159,11 +157,37 @@ def test_decode_parity_workload(name):
     got = run_decode(d, cache_dev, torch)
     assert np.all(np.isfinite(got))
     cache = ref_cache(d)
-    bs, hs = SAMPLES[name]
+    bs = FULL_BATCHES.get(name, list(range(d["batch"])))
+    say(f"   oracle over {len(bs)} of {d['batch']} sequences, all {d['heads']} heads")
     ref = decode_expanded(d["q"], d["kv_b"], cache, d["block_table"], d["seq_lens"], d["q_len"],
-                          batches=bs, heads=hs)
-    g = got[bs][:, :, hs if hs is not None else slice(None)]
-    mx, rr = errors(g, ref)
+                          batches=bs)
+    mx, rr = errors(got[bs], ref)
+    say(f"   max-abs {mx:.3e} rel-rms {rr:.3e}")
+    assert mx <= MAX_ABS and rr <= REL_RMS
+
+
+def test_decode_step_parity_v3_full():
+    """The benchmarked path at its full size: mla_decode_step (insert of the
+    new token, RoPE on q_pe, absorption, split-KV decode, combine) on the
+    64 x 8192 V3 workload; every output element against the float64 oracle
+    run on the oracle's insert and the oracle-rotated query."""
+    torch = _torch()
+    import mla_latent_kv_07_amd as mla
+    from oracle import rotate_q
+    say("[decode step] v3_b64_l8192 full size")
+    d = wl.make_workload("v3_b64_l8192")
+    cache_dev = dev(d["cache"], torch)
+    out = mla.decode_step(dev(d["q"], torch), dev(d["kv_a"], torch), dev(d["rms_w"], torch),
+                          dev(d["kv_b"], torch), cache_dev, dev(d["block_table"], torch),
+                          dev(d["seq_lens"], torch), int(d["seq_lens"].max()), eps=EPS32)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    cache = ref_cache(d)
+    check_insert(d, host_u16(cache_dev), cache)
+    q_rot = rotate_q(d["q"], d["seq_lens"], 1, wl.ROPE_BASE, wl.NOPE)
+    ref = decode_expanded(q_rot, d["kv_b"], cache, d["block_table"], d["seq_lens"], 1)
+    mx, rr = errors(got, ref)
     say(f"   max-abs {mx:.3e} rel-rms {rr:.3e}")
     assert mx <= MAX_ABS and rr <= REL_RMS
 
@@ -248,3 +272,37 @@ def test_decode_restart_on_score_jump():
     rel_max = mx / float(np.max(np.abs(ref)))
     say(f"   max-abs/max|ref| {rel_max:.3e} rel-rms {rr:.3e}")
     assert rel_max <= MAX_ABS and rr <= REL_RMS
+
+
+def test_debug_checks_reject_bad_tables():
+    """With the debug checks on, a block id outside [0, num_blocks) or a
+    length above max_seq_len is reported as MLA_ERR_BOUNDS before anything
+    is launched (the kernels never see the bad table); valid inputs give the
+    same output as with the checks off."""
+    torch = _torch()
+    import mla_latent_kv_07_amd as mla
+    say("[decode] debug checks")
+    d = wl.make_inputs(2, 1, 128, [100, 150], permute=True, seed=46, spare_blocks=1)
+    cache = ref_cache(d)
+    prev = mla.debug_checks(1)
+    try:
+        good = run_decode(d, dev(cache, torch), torch)
+        mla.debug_checks(0)
+        assert np.array_equal(good, run_decode(d, dev(cache, torch), torch))
+        mla.debug_checks(1)
+        bad = d["block_table"].copy()
+        bad[1, 2] = cache.shape[0]  # one past the last block
+        with pytest.raises(mla.MLAError) as ei:
+            mla.decode(dev(d["q"], torch), dev(d["kv_b"], torch), dev(cache, torch),
+                       dev(bad, torch), dev(d["seq_lens"], torch), 150)
+        assert ei.value.status == 6
+        with pytest.raises(mla.MLAError) as ei:
+            mla.decode(dev(d["q"], torch), dev(d["kv_b"], torch), dev(cache, torch),
+                       dev(d["block_table"], torch), dev(d["seq_lens"], torch), 120)
+        assert ei.value.status == 6
+        with pytest.raises(mla.MLAError) as ei:
+            mla.cache_insert(dev(d["kv_a"], torch), dev(d["rms_w"], torch), dev(bad, torch),
+                             dev(d["seq_lens"], torch), dev(cache, torch), eps=EPS32, heads=128)
+        assert ei.value.status == 6
+    finally:
+        mla.debug_checks(prev)
