@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cache-state", choices=("auto", "cold", "warm"), default="auto",
+                    help="cold: flush the last-level cache before every timed step (auto: "
+                         "for the workloads whose cache fits in it)")
     ap.add_argument("--eager", action="store_true",
                     help="launch the step's kernels one call at a time instead of replaying a "
                          "captured HIP graph of the step")
@@ -424,6 +427,7 @@ def main():
     import mla_latent_kv_07_amd as mla
     import workloads as wl
 
+    from mla_latent_kv_07_amd import _lib
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.workload in wl.PREFILL:
         return prefill_main(args)
@@ -456,6 +460,14 @@ def main():
             mla.cache_insert(kv_a, rms_w, bt, sl, cache, eps=eps, heads=heads, fp8=fp8)
             mla.decode(q, kv_b, cache, bt, sl, max_len, out=out, workspace=ws, fp8=fp8)
 
+    cold = wl.fits_llc(d) if args.cache_state == "auto" else args.cache_state == "cold"
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda") if cold else None
+
+    def flush():
+        # writing 512 MiB evicts the cache rows (and everything else) from the
+        # 256 MB last-level cache and the L2s: the next step reads cold
+        flush_buf.fill_(1)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -472,34 +484,82 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
         run = graph.replay
-    # the timed steps: nothing else on the stream
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    step_ms = []
+    if cold:
+        # each step timed alone with HIP events, the flush outside the events
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            flush()
+            e0.record()
+            run()
+            e1.record()
+        torch.cuda.synchronize()
+        step_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        ms_step = sum(step_ms) / len(step_ms)
+    else:
+        # the timed steps: nothing else on the stream
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     # the same steps again with HIP events recorded by the library around each
-    # stage (the events themselves cost a few microseconds, so they stay out
-    # of the timed loop above)
+    # stage on its launch stream (the events themselves cost a few
+    # microseconds, so they stay out of the timed loop above)
     mla.profile_enable(args.steps)
     for _ in range(args.steps):
+        if cold:
+            flush()
         step()
     torch.cuda.synchronize()
-    stage_ms, calls = mla.profile_collect()
+    per_call = mla.profile_collect_calls(args.steps)
     mla.profile_enable(0)
-    assert calls == args.steps
-    ms_step = wall * 1e3 / args.steps
+    assert len(per_call) == args.steps
+    stage_mean = {k: sum(c[i] for c in per_call) / len(per_call)
+                  for i, k in enumerate(_lib.STAGES)}
+    dec_all = sorted(c[1] for c in per_call)
+    dec_ms = stage_mean["decode"]
     kv_bytes = int(seq_lens.sum()) * row_bytes
-    alg_bytes = wl.decode_bytes(seq_lens, bsz, q_len, heads, bt.numel())
+    alg_bytes = wl.decode_bytes(seq_lens, bsz, q_len, heads, bt.numel(), row_bytes=row_bytes)
     alg_flops = wl.decode_flops(seq_lens, bsz, q_len, heads)
-    dec_ms = stage_ms["decode"] / calls
+    dec_flops = 2 * heads * wl.visible_pairs(seq_lens, q_len) * (wl.ENTRY + wl.LATENT)
     dec_gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+    dec_tfs = dec_flops / (dec_ms * 1e-3) / 1e12
+    copy_gbs = copy_ceiling(torch)
     traffic = None
     if os.path.exists(args.traffic):
         tr = json.load(open(args.traffic))
-        if (tr.get("workload") == args.workload and tr.get("kernel_source_sha") == kernel_sha()
-                and tr.get("cache", "bf16") == args.cache):
-            traffic = tr.get("bytes_per_launch")
+        rec = tr.get(args.workload) if args.workload in tr else tr
+        if (rec.get("workload") == args.workload and rec.get("kernel_source_sha") == kernel_sha()
+                and rec.get("cache", "bf16") == args.cache):
+            traffic = rec.get("bytes_per_launch")
+    per_unit = ("656 B per cached position (FP8 row)" if fp8 else
+                "1152 B per cached position (576 bf16)")
+    if wl.decode_bytes(seq_lens, bsz, q_len, heads) / 8.0e12 < alg_flops / 2.5e15:
+        # more flops per byte than the chip's ridge point (the multi-token
+        # shape): the decode kernel is priced against the bf16 matrix peak
+        roof = {"kernel": "mla::decode_kernel (split-KV decode)", "bound": "mfma",
+                "achieved": round(dec_tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(dec_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic,
+                "per_unit": "2 x (576 + 512) flops per head and visible (query, position) pair",
+                "units_per_launch": int(heads * wl.visible_pairs(seq_lens, q_len)),
+                "hbm_gbs": round(dec_gbs, 1), "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"kernel": "mla::decode_kernel (split-KV decode)", "bound": "hbm",
+                "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "per_unit": per_unit, "units_per_launch": int(seq_lens.sum()),
+                "mfma_tflops": round(dec_tfs, 1),
+                "mfma_frac": round(dec_tfs / MFMA_BF16_PEAK_TFS, 4)}
+    roof["basis"] = ("mean of the decode kernel's HIP-event durations, recorded by the "
+                     "library on its launch stream, over the timed steps")
+    roof["launch_ms"] = {"mean": round(dec_ms, 4), "min": round(dec_all[0], 4),
+                         "median": round(dec_all[len(dec_all) // 2], 4),
+                         "max": round(dec_all[-1], 4)}
+    roof["frac_of_copy_ceiling"] = round(dec_gbs / copy_gbs, 4)
     result = {
         "metric": "MLA decode KV-cache GB/s & tokens/s at V3 shape; % of HBM roofline",
         "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -513,24 +573,23 @@ def main():
                    "page": 64, "kv_lora": 512, "rope": 64, "step": ("mla_decode_step: insert + q_pe RoPE + absorption in one launch, "
                             "decode, combine" if args.path == "step" else
                             "mla_cache_insert + mla_decode"),
-                   "cache": args.cache, "launch": "eager" if args.eager else "hip graph"},
+                   "cache": args.cache, "launch": "eager" if args.eager else "hip graph",
+                   "timing": ("cold: the 256 MB last-level cache flushed (512 MiB written) "
+                              "before every step, each step timed alone with HIP events"
+                              if cold else "warm: steps back to back, wall clock")},
         "tokens_per_s": round(bsz * q_len / (ms_step * 1e-3), 1),
         "alg_bytes_per_step": alg_bytes,
         "alg_flops_per_step": alg_flops,
         "step_alg_hbm_frac": round(alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "stage_ms": {k: round(v / calls, 4) for k, v in stage_ms.items()},
-        "roofline": {"kernel": "mla::decode_kernel (split-KV decode)", "bound": "hbm",
-                     "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "per_unit": ("656 B per cached position (FP8 row)" if fp8 else
-                                  "1152 B per cached position (576 bf16)"),
-                     "units_per_launch": int(seq_lens.sum()),
-                     "mfma_tflops": round(2 * heads * wl.visible_pairs(seq_lens, q_len)
-                                          * (wl.ENTRY + wl.LATENT) / (dec_ms * 1e-3) / 1e12, 1),
-                     "mfma_frac": round(2 * heads * wl.visible_pairs(seq_lens, q_len)
-                                        * (wl.ENTRY + wl.LATENT) / (dec_ms * 1e-3) / 1e12
-                                        / MFMA_BF16_PEAK_TFS, 4)},
+        "step_alg_mfma_frac": round(alg_flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+        "stage_ms": {k: round(v, 4) for k, v in stage_mean.items()},
+        "copy_ceiling": {"gbs": round(copy_gbs, 1),
+                         "kind": f"device-to-device copy of {COPY_MIB} MiB (read + write bytes), "
+                                 "best of 5, HIP events"},
+        "roofline": roof,
     }
+    if step_ms:
+        result["step_ms_median"] = round(sorted(step_ms)[len(step_ms) // 2], 4)
     if args.calib_copy_mib > 0:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -546,6 +605,28 @@ def main():
         result["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds, fp8_host,
                                               rotate=args.path == "step")
     print(json.dumps(result), flush=True)
+
+
+COPY_MIB = 1024
+FLUSH_BYTES = 512 << 20
+
+
+def copy_ceiling(torch) -> float:
+    """Measured copy bandwidth of the device: a plain device-to-device copy of
+    COPY_MIB MiB, read + write bytes over the best of five HIP-event timings."""
+    src = torch.empty(COPY_MIB << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return 2 * (COPY_MIB << 20) / (best * 1e-3) / 1e9
 
 
 def kernel_sha(files=("decode.hip", "mla_common.h")) -> str:

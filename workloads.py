@@ -194,11 +194,13 @@ def make_workload(name: str) -> dict:
 BYTES_PER_TOKEN = ENTRY * 2  # one cache entry in bf16
 
 
-def decode_bytes(seq_lens, batch: int, q_len: int, heads: int, bt_entries: int = 0) -> int:
+def decode_bytes(seq_lens, batch: int, q_len: int, heads: int, bt_entries: int = 0,
+                 row_bytes: int = BYTES_PER_TOKEN) -> int:
     """Bytes a decode call must move at minimum: every visible cache entry
-    once, kv_b once, q in, out back, the block table."""
+    once (``row_bytes`` each: 1152 for the bf16 cache, 656 for the FP8 rows),
+    kv_b once, q in, out back, the block table."""
     total_tokens = int(np.sum(seq_lens))
-    return (total_tokens * BYTES_PER_TOKEN
+    return (total_tokens * row_bytes
             + heads * (NOPE + VDIM) * LATENT * 2
             + batch * q_len * heads * (NOPE + ROPE) * 2
             + batch * q_len * heads * VDIM * 2
@@ -238,6 +240,15 @@ def prefill_flops(seq_lens, q_len: int, heads: int) -> tuple[int, int]:
 
 def insert_bytes(batch: int, q_len: int) -> int:
     return batch * q_len * ENTRY * 2 * 2 + LATENT * 2 + 8 * batch
+
+
+# Workloads whose cache fits in the 256 MB last-level cache (Infinity Cache)
+# of the MI355X are timed cold: that cache is flushed before every step.
+LLC_BYTES = 256 << 20
+
+
+def fits_llc(d: dict) -> bool:
+    return decode_bytes(d["seq_lens"], d["batch"], d["q_len"], d["heads"]) < LLC_BYTES
 
 
 INDEX_BYTES_PER_TOKEN = 128 + 4 + 4  # E4M3 key, its fp32 scale, the fp32 score written
