@@ -54,7 +54,8 @@ typedef enum {
   MLA_ERR_SHAPE = 2,        /* a size argument is out of range or inconsistent */
   MLA_ERR_UNSUPPORTED = 3,  /* dimensions this build does not implement */
   MLA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
-  MLA_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+  MLA_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
+  MLA_ERR_BOUNDS = 6        /* debug checks: a block id or length breaks the contract */
 } mla_status;
 
 /* Model dimensions ([V3-src] MLA: kv_lora_rank, qk_rope_head_dim,
@@ -341,6 +342,21 @@ const char* mla_status_string(int status);
 
 /* ABI version of this header: 1. */
 int mla_abi_version(void);
+
+/*
+ * mla_debug_checks — host-side checks of the device-side contract (block ids
+ * in [0, num_blocks), lengths in [q_len, max_seq_len] and within the block
+ * table's width): enable > 0 turns them on, 0 off, < 0 only queries.  Returns
+ * the previous setting.  The initial setting is MLA_DEBUG_CHECKS from the
+ * environment (unset or "0": off).  While on, every entry point that takes a
+ * block table first copies it and seq_lens to the host on its stream and
+ * waits for the copy (the call then synchronises); a violation returns
+ * MLA_ERR_BOUNDS with nothing enqueued.  mla_cache_insert checks the blocks
+ * that receive the new tokens, the decode, prefill and sparse entry points
+ * every block of each sequence, mla_dsa_select the lengths and table width
+ * (it has no block count).  For debugging: the copy costs a round trip.
+ */
+int mla_debug_checks(int32_t enable);
 
 #ifdef __cplusplus
 }

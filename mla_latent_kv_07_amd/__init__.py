@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     MLAError,
     abi_version,
     cache_insert,
+    debug_checks,
     decode,
     decode_step,
     decode_workspace_bytes,

@@ -31,7 +31,9 @@ class Dims(ctypes.Structure):
 
 
 def lib_path() -> str:
-    return os.path.join(PKG, LIB_NAME)
+    """libmla.so next to this file, or the file MLA_LIB names (the sanitizer
+    build of the same sources, for the ABI tests)."""
+    return os.environ.get("MLA_LIB") or os.path.join(PKG, LIB_NAME)
 
 
 def load() -> ctypes.CDLL:
@@ -85,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.mla_profile_collect.restype = ctypes.c_int
     lib.mla_abi_version.argtypes = []
     lib.mla_abi_version.restype = ctypes.c_int
+    lib.mla_debug_checks.argtypes = [I32]
+    lib.mla_debug_checks.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -95,6 +99,12 @@ def status_string(status: int) -> str:
 
 def abi_version() -> int:
     return int(load().mla_abi_version())
+
+
+def debug_checks(enable: int = -1) -> int:
+    """mla_debug_checks: enable (1) or disable (0) the host-side checks of
+    block tables and lengths; -1 only queries.  Returns the previous setting."""
+    return int(load().mla_debug_checks(int(enable)))
 
 
 def dims(heads: int) -> Dims:

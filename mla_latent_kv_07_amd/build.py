@@ -68,6 +68,54 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+ASAN_LIB = os.path.join(BUILD, "libmla_asan.so")
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime matching hipcc's host compiler."""
+    out = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True).stdout.strip()
+    if out and os.path.isabs(out) and os.path.exists(out):
+        return out
+    base = os.path.join(os.path.dirname(os.path.dirname(hipcc())), "lib", "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(base), reverse=True) if os.path.isdir(base) else []:
+        cand = os.path.join(base, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(cand):
+            return cand
+    raise RuntimeError("clang AddressSanitizer runtime not found")
+
+
+def build_asan(verbose: bool = False) -> str:
+    """The same library with AddressSanitizer on the host code of the C ABI
+    (argument validation, workspace layout, debug checks) and the kernels
+    unchanged; load it with the runtime from asan_runtime() preloaded.  For
+    the CPU tests of the ABI."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        if src == "mla_api.cpp":
+            obj = os.path.join(BUILD, "mla_api_asan.o")
+            cmd = [hipcc(), *common_flags(), "-g", "-Xarch_host", "-fsanitize=address",
+                   "-Xarch_host", "-fno-omit-frame-pointer", "-c", os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
+        elif not os.path.exists(obj):
+            obj = _compile(src)
+        objs.append(obj)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host",
+           "-fsanitize=address", "-shared-libsan", "-o", ASAN_LIB, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    if len(sys.argv) > 1 and sys.argv[1] == "asan":
+        build_asan(verbose=True)
     sys.exit(0)

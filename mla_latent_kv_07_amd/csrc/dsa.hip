@@ -40,6 +40,7 @@ struct IndexArgs {
   int heads;               // Hi
   int lpad;                // row stride of `scores`
   float* scores;           // [B, lpad]
+  int max_len;             // host-side bound on seq_lens (lengths are clamped to it)
 };
 
 constexpr int kIdxRowsPerWG = 512;  // cached positions per index-score workgroup
@@ -60,7 +61,9 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a,
   __shared__ float part[2][kIdxDim];
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int len = a.seq_lens[b];
+  // (a length beyond the documented bound is clamped: no score row, block
+  // table row or kept list is ever addressed past its size)
+  const int len = min(a.seq_lens[b], a.max_len);
   const int n0 = blockIdx.x * kIdxRowsPerWG;
   if (n0 >= len) return;  // uniform over the workgroup
   {
@@ -316,7 +319,8 @@ __device__ __forceinline__ void topk_body(const float* sc, int len, int kk, int3
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
                                                             int lpad,
                                                             const int32_t* __restrict__ seq_lens,
-                                                            int top_k, int32_t* __restrict__ out,
+                                                            int max_len, int top_k,
+                                                            int32_t* __restrict__ out,
                                                             int32_t* __restrict__ counts) {
   __shared__ int hist[256];
   __shared__ int wave_sums[kTopkThreads / 64];
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   __shared__ int s_rem;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
-  const int len = seq_lens[b];
+  const int len = min(seq_lens[b], max_len);  // clamped as in the index scores
   const int kk = min(top_k, len);
   const float* sc = scores + (int64_t)b * lpad;
   int32_t* ob = out + (int64_t)b * top_k;
@@ -391,17 +395,17 @@ hipError_t launch_index_scores(const uint8_t* index_q, const float* index_w, int
                                int batch, int max_seq_len, float* scores, int lpad,
                                hipStream_t stream) {
   IndexArgs ia{index_q, index_w, index_k, index_k_scale, bt_stride, seq_lens, index_heads, lpad,
-               scores};
+               scores, max_seq_len};
   hipLaunchKernelGGL(index_score_kernel,
                      dim3((max_seq_len + kIdxRowsPerWG - 1) / kIdxRowsPerWG, batch), dim3(256), 0,
                      stream, ia, block_table);
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* scores, int lpad, const int32_t* seq_lens, int batch,
-                       int top_k, int32_t* kept, int32_t* counts, hipStream_t stream) {
+hipError_t launch_topk(const float* scores, int lpad, const int32_t* seq_lens, int max_seq_len,
+                       int batch, int top_k, int32_t* kept, int32_t* counts, hipStream_t stream) {
   hipLaunchKernelGGL(topk_kernel, dim3(batch), dim3(kTopkThreads), 0, stream, scores, lpad,
-                     seq_lens, top_k, kept, counts);
+                     seq_lens, max_seq_len, top_k, kept, counts);
   return hipGetLastError();
 }
 

@@ -2,9 +2,12 @@
 // See include/mla.h for the contract of every entry point.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -47,6 +50,59 @@ int check_dims(const mla_dims* d) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---- debug checks of the device-side contract -------------------------------
+// With MLA_DEBUG_CHECKS=1 in the environment (read once) or after
+// mla_debug_checks(1), every entry point that takes a block table first
+// copies the block table and the sequence lengths to the host (a synchronising
+// copy on the call's stream) and checks them; a violation returns
+// MLA_ERR_BOUNDS and nothing is enqueued.
+std::atomic<int> g_debug{-1};
+
+bool debug_checks() {
+  int v = g_debug.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = std::getenv("MLA_DEBUG_CHECKS");
+    v = (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
+    int expected = -1;
+    if (!g_debug.compare_exchange_strong(expected, v)) v = expected;
+  }
+  return v > 0;
+}
+
+// seq_lens[b] must lie in [lo, hi] and the block ids of the first
+// ceil(seq_lens[b] / 64) logical blocks of sequence b (from logical block
+// `first_page(len)` on) in [0, num_blocks).  Returns MLA_OK, MLA_ERR_BOUNDS, or
+// MLA_ERR_HIP when the copies fail.
+template <class FirstPage>
+int check_tables(const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                 int32_t batch, int64_t lo, int64_t hi, int32_t num_blocks, hipStream_t s,
+                 FirstPage first_page) {
+  std::vector<int32_t> sl((size_t)batch), bt((size_t)batch * bt_stride);
+  if (hipMemcpyAsync(sl.data(), seq_lens, sl.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(bt.data(), block_table, bt.size() * 4, hipMemcpyDeviceToHost, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MLA_ERR_HIP;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t len = sl[b];
+    if (len < lo || len > hi) return MLA_ERR_BOUNDS;
+    const int64_t pages = (len + kPage - 1) / kPage;
+    if (pages > bt_stride) return MLA_ERR_BOUNDS;
+    for (int64_t p = first_page(len); p < pages; ++p) {
+      const int32_t blk = bt[(size_t)b * bt_stride + p];
+      if (blk < 0 || blk >= num_blocks) return MLA_ERR_BOUNDS;
+    }
+  }
+  return MLA_OK;
+}
+
+// every page of the sequence
+int check_all_pages(const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                    int32_t batch, int64_t lo, int64_t hi, int32_t num_blocks, hipStream_t s) {
+  return check_tables(block_table, bt_stride, seq_lens, batch, lo, hi, num_blocks, s,
+                      [](int64_t) { return (int64_t)0; });
+}
 
 struct Layout {
   int max_items = 0;
@@ -156,6 +212,12 @@ int mla_profile_collect_calls(double* stage_ms, int32_t max_calls, int32_t* call
 
 int mla_abi_version(void) { return 1; }
 
+int mla_debug_checks(int32_t enable) {
+  const int prev = debug_checks() ? 1 : 0;
+  if (enable >= 0) g_debug.store(enable ? 1 : 0, std::memory_order_relaxed);
+  return prev;
+}
+
 const char* mla_status_string(int status) {
   switch (status) {
     case MLA_OK: return "ok";
@@ -164,6 +226,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "unsupported dimensions (need kv_lora 512, rope 64, qk_nope 128, v_dim 128, page 64, heads 16..128 in steps of 16)";
     case MLA_ERR_WORKSPACE: return "workspace missing or too small";
     case MLA_ERR_HIP: return "HIP runtime error at kernel launch";
+    case MLA_ERR_BOUNDS: return "block table or sequence lengths break the contract (debug checks)";
     default: return "unknown status";
   }
 }
@@ -184,6 +247,13 @@ int cache_insert_any(bool fp8, const mla_dims* dims, const void* kv_a, const voi
     return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
   if (!kv_a || !rms_w || !block_table || !seq_lens || !cache) return MLA_ERR_NULL;
+  if (debug_checks()) {
+    // the pages that receive the new tokens
+    st = check_tables(block_table, bt_stride, seq_lens, batch, q_len, (int64_t)bt_stride * kPage,
+                      num_blocks, static_cast<hipStream_t>(stream),
+                      [q_len](int64_t len) { return (len - q_len) / kPage; });
+    if (st != MLA_OK) return st;
+  }
   hipError_t e =
       fp8 ? launch_insert_fp8(static_cast<const uint16_t*>(kv_a),
                               static_cast<const uint16_t*>(rms_w), eps, rope_base, block_table,
@@ -247,6 +317,11 @@ int decode_any(bool fp8, const InsertArgs* ins, const mla_dims* dims, const void
   const int heads = dims->heads;
   const Layout L = make_layout(heads, batch, q_len, num_splits_hint);
   if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  if (debug_checks()) {
+    st = check_all_pages(block_table, bt_stride, seq_lens, batch, q_len, max_seq_len, num_blocks,
+                         static_cast<hipStream_t>(stream));
+    if (st != MLA_OK) return st;
+  }
 
   char* ws = static_cast<char*>(workspace);
   PlanView plan;
@@ -390,6 +465,11 @@ int mla_prefill(const mla_dims* dims, const void* q, const void* kv_b, const voi
   const size_t need = mla_prefill_workspace_bytes(dims, batch, max_seq_len);
   if (!workspace) return MLA_ERR_WORKSPACE;
   if (need == 0 || workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  if (debug_checks()) {
+    st = check_all_pages(block_table, bt_stride, seq_lens, batch, q_len, max_seq_len, num_blocks,
+                         static_cast<hipStream_t>(stream));
+    if (st != MLA_OK) return st;
+  }
   const int heads = dims->heads;
   const int64_t lpad = prefill_lpad(max_seq_len);
   char* ws = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
@@ -468,11 +548,17 @@ int mla_dsa_select(int32_t index_heads, const void* index_q, const float* index_
   if (st != MLA_OK) return st;
   if (!block_table || !seq_lens || !scores || !indices) return MLA_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    // (the index keys have no block count here: lengths and table width only)
+    st = check_tables(block_table, bt_stride, seq_lens, batch, 1, max_seq_len, INT32_MAX, s,
+                      [](int64_t) { return (int64_t)0; });
+    if (st != MLA_OK) return st;
+  }
   hipError_t e = launch_index_scores(static_cast<const uint8_t*>(index_q), index_w, index_heads,
                                      static_cast<const uint8_t*>(index_k), index_k_scale,
                                      block_table, bt_stride, seq_lens, batch, max_seq_len, scores,
                                      scores_stride, s);
-  if (e == hipSuccess) e = launch_topk(scores, scores_stride, seq_lens, batch, top_k, indices,
+  if (e == hipSuccess) e = launch_topk(scores, scores_stride, seq_lens, max_seq_len, batch, top_k, indices,
                                        counts, s);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -511,6 +597,11 @@ int dsa_any(bool fp8, const mla_dims* dims, const void* q, const void* kv_b, con
   if (!workspace) return MLA_ERR_WORKSPACE;
   const DsaLayout L = make_dsa_layout(dims->heads, batch, max_seq_len, top_k, num_splits_hint);
   if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  if (debug_checks()) {
+    st = check_all_pages(block_table, bt_stride, seq_lens, batch, 1, max_seq_len, num_blocks,
+                         static_cast<hipStream_t>(stream));
+    if (st != MLA_OK) return st;
+  }
   char* ws = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + 255) & ~(uintptr_t)255);
   float* scores = reinterpret_cast<float*>(ws + L.off_scores);
   int32_t* kept = indices_out ? indices_out : reinterpret_cast<int32_t*>(ws + L.off_kept);
@@ -530,7 +621,8 @@ int dsa_any(bool fp8, const mla_dims* dims, const void* q, const void* kv_b, con
                                      block_table, bt_stride, seq_lens, batch, max_seq_len, scores,
                                      lpad, s);
   prof_mark(pc, 1, s);
-  if (e == hipSuccess) e = launch_topk(scores, lpad, seq_lens, batch, top_k, kept, counts, s);
+  if (e == hipSuccess)
+    e = launch_topk(scores, lpad, seq_lens, max_seq_len, batch, top_k, kept, counts, s);
   prof_mark(pc, 2, s);
   if (e == hipSuccess)
     e = launch_gather(fp8, cache, block_table, bt_stride, kept, top_k, counts, batch, kp, dense,

@@ -34,9 +34,20 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
-        assert lib.mla_status_string(s)
+    for s in range(7):
+        assert lib.mla_status_string(s) and lib.mla_status_string(s) != b"unknown status"
     assert lib.mla_status_string(99) == b"unknown status"
+
+
+def test_debug_checks_toggle(lib):
+    """mla_debug_checks: -1 queries, 1/0 set, and the previous value comes back."""
+    start = lib.mla_debug_checks(-1)
+    assert start in (0, 1)
+    assert lib.mla_debug_checks(1) == start
+    assert lib.mla_debug_checks(-1) == 1
+    assert lib.mla_debug_checks(0) == 1
+    assert lib.mla_debug_checks(-1) == 0
+    lib.mla_debug_checks(start)
 
 
 def _dims(heads=16, **kw):
@@ -109,5 +120,6 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     from mla_latent_kv_07_amd import _lib
     monkeypatch.setattr(_lib, "PKG", str(tmp_path))
     monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.delenv("MLA_LIB", raising=False)
     with pytest.raises(RuntimeError, match="no fallback"):
         _lib.load()
