@@ -78,8 +78,13 @@ constexpr int kChunk = 32;                     // positions per LDS stage
 constexpr int kBufBytes = kChunk * kEntryBytes;  // 36864
 constexpr float kSlackPow = 65536.0f;          // 2^16: headroom above the reference max
 
-// Encoding of "s_waitcnt vmcnt(n)" (expcnt and lgkmcnt left unconstrained).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// Encoding of "s_waitcnt vmcnt(N)" (expcnt and lgkmcnt left unconstrained).
+// The count has 6 bits: N above 63 is a compile error.
+template <int N>
+constexpr int vmcnt_imm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt has 6 bits");
+  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+}
 
 // Copies of one chunk: 1 KB per wavefront-wide instruction.
 //   bf16: the chunk's 36 KB is dealt to the wavefronts round robin (copy i of
@@ -466,7 +471,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   // time: the compiler then knows that the copies in flight (into the other
   // slots) never alias the slot being read and adds no wait of its own on
   // them.
-  constexpr int NS = (FP8 || NW == 8) ? 3 : 4;
+  // (one wavefront: 36 copies per chunk, so only one chunk can be waited on
+  // within vmcnt's 6 bits: three slots, two chunks in flight)
+  constexpr int NS = (FP8 || NW == 8 || NW == 1) ? 3 : 4;
   // score read-ahead in k-steps (eight wavefronts: two, for registers)
   constexpr int kKpd = NW == 8 ? 2 : 4;
   __shared__ __attribute__((aligned(1024))) char ring0[D::kSlotBytes];
@@ -673,7 +680,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     if constexpr (decltype(dq_c)::value) {
       // the rows to expand have landed once at most the copies of the two
       // chunks after them are pending
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPer));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<FP8 ? 2 * kPer : 0>());
       dequant_rows<NW>(dq_src, dq_dst, wave, lane);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -716,7 +723,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     } else {
       // chunk j has landed once at most the copies of chunks j+1 .. j+NS-2
       // are pending
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * kPer));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<(NS - 2) * kPer>());
       ring_barrier();
       // chunk j+NS-1 goes into chunk j-1's slot: every wavefront is past it
       const ChunkCopy cc = chunk_copy(Slot<(S + NS - 1) % NS>{}, j + NS - 1);
@@ -757,11 +764,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     }
   }
   // every wavefront's verdict, then one decision for the workgroup
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
   __syncthreads();
   if (__builtin_amdgcn_ballot_w64(need_restart) != 0 && lane == 0)
     __atomic_store_n(flag, 1, __ATOMIC_RELAXED);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
   __syncthreads();
   const bool restart = __atomic_load_n(flag, __ATOMIC_RELAXED) != 0;
 
@@ -770,7 +777,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   if (restart) {
     auto fetch = [&](int j) -> const MLA_LDS char* {
       issue(Slot<0>{}, j);
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
       if constexpr (FP8) {
         dequant_rows<NW>(ring(Slot<0>{}), stage_of(0), wave, lane);
         __syncthreads();
@@ -838,17 +845,485 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined decode for 128 query rows per workgroup (H = 128 at q_len 1; one
+// of the two row groups at q_len 2): four wavefronts, one per SIMD, each
+// owning two groups of 16 rows and ALL 512 latent features of their outputs
+// (O^T in 256 accumulation registers, the absorbed query in 144).  A row's
+// probabilities therefore never leave the wavefront that computed them: no
+// probability tiles go through LDS and the only barrier of a chunk is the one
+// that hands out its ring slot.  The cost is that every wavefront reads the
+// whole V^T of a chunk (32 KB) next to its whole K (36 KB): 68 KB of LDS
+// reads per wavefront per 32 positions, one 1 KB read per two MFMAs.
+//
+// Software pipeline: while chunk j's P.V runs, the scores of chunk j+1 are
+// taken (one fused stream of 18 score k-steps and 32 P.V feature tiles, with
+// the LDS reads of each unit issued kFusedAhead units before its MFMAs), then
+// the softmax of chunk j+1.  Chunk j lives in ring slot j % 4; at the top of
+// interval j, chunk j+1 has landed and chunk j+3's copies go into the slot of
+// chunk j-1, so two chunks are in flight while two are read.
+
+// MFMAs with pinned register classes.  With 256 output accumulators per
+// lane the kernel needs every AGPR for O; the compiler's own MFMA selection
+// puts every accumulator (the scores' too) in AGPRs and then shuffles tiles
+// between the two files.  Written as asm, the score tiles accumulate in
+// VGPRs and the output tiles in AGPRs, with no copies.  The compiler does not
+// know these are matrix instructions, so the one hazard it would miss is
+// handled where it occurs: a vector instruction that reads an MFMA result
+// (the softmax on the scores, the final read of O) must come at least eight
+// wait states after it (mfma_drain below).  Their operands come from LDS or
+// global loads (waited for by the compiler's counters) or, for P, from
+// vector instructions many cycles earlier.
+__device__ __forceinline__ void mfma_sc0(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_sc(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_o(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// 12 wait states after the last score MFMA, ordered before every read of the
+// scores (they pass through this statement).
+template <int NH>
+__device__ __forceinline__ void mfma_drain(f32x4 (&sacc)[NH][2]) {
+  static_assert(NH == 2, "four score tiles");
+  asm volatile("s_nop 7\n\ts_nop 3"
+               : "+v"(sacc[0][0]), "+v"(sacc[0][1]), "+v"(sacc[1][0]), "+v"(sacc[1][1]));
+}
+// The same for the output tiles before they are read (after the chunk loop):
+// the wait states first, then every tile passes through an (empty) statement
+// ordered after them.
+template <int NH>
+__device__ __forceinline__ void mfma_drain_o(f32x4 (&oacc)[NH][32]) {
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int f = 0; f < 32; f += 8)
+      asm volatile(""
+                   : "+a"(oacc[h][f]), "+a"(oacc[h][f + 1]), "+a"(oacc[h][f + 2]),
+                     "+a"(oacc[h][f + 3]), "+a"(oacc[h][f + 4]), "+a"(oacc[h][f + 5]),
+                     "+a"(oacc[h][f + 6]), "+a"(oacc[h][f + 7]));
+}
+
+// Score k-step ks of the chunk at (be, bo) (see score_chunk) for NH row
+// groups, the two 16-position tiles' K pieces already in kb.
+template <int NH>
+__device__ __forceinline__ void score_step(int ks, const bf16x8 (&kb)[2],
+                                           const bf16x8 (&qreg)[NH][18], f32x4 (&sacc)[NH][2]) {
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (ks == 0)
+        mfma_sc0(sacc[h][t], kb[t], qreg[h][ks]);
+      else
+        mfma_sc(sacc[h][t], kb[t], qreg[h][ks]);
+    }
+}
+
+// Unit map of one fused interval: kFusedScore score k-steps spread over the
+// first kFusedSpan of the kFusedUnits slots, P.V feature tiles in the others.
+constexpr int kFusedScore = 18;
+constexpr int kFusedPv = 32;
+constexpr int kFusedUnits = kFusedScore + kFusedPv;
+constexpr int kFusedSpan = 44;
+constexpr int kFusedAhead = 3;
+struct FusedMap {
+  int kind[kFusedUnits];  // 0: score k-step, 1: P.V feature tile
+  int idx[kFusedUnits];   // the k-step or the tile
+  int copy[kFusedUnits];  // copy instructions issued at this unit
+  constexpr FusedMap(int ncopies) : kind(), idx(), copy() {
+    int s = 0, p = 0;
+    for (int u = 0; u < kFusedUnits; ++u) {
+      if (s < kFusedScore && u == s * kFusedSpan / kFusedScore) {
+        kind[u] = 0;
+        idx[u] = s++;
+      } else {
+        kind[u] = 1;
+        idx[u] = p++;
+      }
+      copy[u] = 0;
+    }
+    // one copy per unit, from unit 1 on (every other unit while they last)
+    for (int c = 0; c < ncopies; ++c) copy[(1 + 2 * c) % kFusedUnits] += 1;
+  }
+};
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Reads of fused unit v into rb: a score k-step's two K pieces from the
+// chunk at (be, bo), or a P.V feature tile of V^T from the chunk at pv.
+template <int V>
+__device__ __forceinline__ void fused_reads(bf16x8 (&rb)[2], const MLA_LDS char* be,
+                                            const MLA_LDS char* bo, const MLA_LDS char* pv,
+                                            const int (&vbase)[4]) {
+  constexpr FusedMap m(0);
+  constexpr int i = m.idx[V];
+  if constexpr (m.kind[V] == 0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      rb[t] = *reinterpret_cast<const MLA_LDS bf16x8*>((i & 1 ? bo : be) + 64 * i +
+                                                       16 * kEntryBytes * t);
+  } else {
+    const int o = vbase[i & 3] + 128 * (i >> 2);
+    const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pv + o));
+    const bf16x4 a1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(pv + (o + 16 * kEntryBytes)));
+    rb[0] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+// P.V of chunk j (slot `pv`, probabilities pk) fused with the scores of
+// chunk j+1 (slot `sc`, into sacc), the copies of `cc` issued along the way.
+// Every matrix instruction is an ordered asm statement, so the stream runs in
+// the order written: per unit its copies, the LDS reads of the unit
+// kFusedAhead later, then its MFMAs.
+template <int NH, int KPER, int WB, int ST>
+__device__ __forceinline__ void fused_interval(const MLA_LDS char* pv, const int (&vbase)[4],
+                                               const bf16x8 (&pk)[NH], f32x4 (&oacc)[NH][32],
+                                               const MLA_LDS char* sc, int sbase_even,
+                                               int sbase_odd, const bf16x8 (&qreg)[NH][18],
+                                               f32x4 (&sacc)[NH][2], const ChunkCopy& cc,
+                                               const uint32_t* off, int wave) {
+  constexpr FusedMap m(KPER);
+  const MLA_LDS char* be = sc + sbase_even;
+  const MLA_LDS char* bo = sc + sbase_odd;
+  bf16x8 rb[kFusedAhead + 1][2];
+  static_for<0, kFusedAhead>([&](auto v_c) __attribute__((always_inline)) {
+    constexpr int v = decltype(v_c)::value;
+    fused_reads<v>(rb[v % (kFusedAhead + 1)], be, bo, pv, vbase);
+  });
+  static_for<0, kFusedUnits>([&](auto u_c) __attribute__((always_inline)) {
+    constexpr int u = decltype(u_c)::value;
+    constexpr int r = u % (kFusedAhead + 1);
+    constexpr int i = m.idx[u];
+    constexpr int c0 = [] {
+      constexpr FusedMap mm(KPER);
+      int c = 0;
+      for (int k = 0; k < u; ++k) c += mm.copy[k];
+      return c;
+    }();
+#pragma unroll
+    for (int c = 0; c < m.copy[u]; ++c) copy_piece<WB, ST>(cc, off, c0 + c, wave);
+    if constexpr (u + kFusedAhead < kFusedUnits)
+      fused_reads<u + kFusedAhead>(rb[(u + kFusedAhead) % (kFusedAhead + 1)], be, bo, pv, vbase);
+    if constexpr (m.kind[u] == 0) {
+      score_step<NH>(i, rb[r], qreg, sacc);
+    } else {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) mfma_o(oacc[h][i], rb[r][0], pk[h]);
+    }
+  });
+}
+
+// Scores of one chunk alone (the first chunk of an item, and the restart
+// passes), with the same asm MFMAs: reads of k-step ks + 3 issued before the
+// MFMAs of k-step ks.
+template <int NH>
+__device__ __forceinline__ void score_only(const MLA_LDS char* buf, int sbase_even, int sbase_odd,
+                                           const bf16x8 (&qreg)[NH][18], f32x4 (&sacc)[NH][2]) {
+  const MLA_LDS char* be = buf + sbase_even;
+  const MLA_LDS char* bo = buf + sbase_odd;
+  constexpr int A = 3;
+  bf16x8 kb[A + 1][2];
+  auto kload = [&](int ks, bf16x8 (&dst)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      dst[t] = *reinterpret_cast<const MLA_LDS bf16x8*>((ks & 1 ? bo : be) + 64 * ks +
+                                                        16 * kEntryBytes * t);
+  };
+#pragma unroll
+  for (int ks = 0; ks < A; ++ks) kload(ks, kb[ks]);
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) {
+    if (ks + A < 18) kload(ks + A, kb[(ks + A) % (A + 1)]);
+    score_step<NH>(ks, kb[ks % (A + 1)], qreg, sacc);
+  }
+}
+
+// P.V of one chunk alone (the last chunk of an item, and the restart pass).
+template <int NH>
+__device__ __forceinline__ void pv_only(const MLA_LDS char* buf, const int (&vbase)[4],
+                                        const bf16x8 (&pk)[NH], f32x4 (&oacc)[NH][32]) {
+  constexpr int A = 3;
+  bf16x8 vb[A + 1];
+  auto vload = [&](int f, bf16x8& dst) {
+    const int o = vbase[f & 3] + 128 * (f >> 2);
+    const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(buf + o));
+    const bf16x4 a1 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)(buf + (o + 16 * kEntryBytes)));
+    dst = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+#pragma unroll
+  for (int f = 0; f < A; ++f) vload(f, vb[f]);
+#pragma unroll
+  for (int f = 0; f < 32; ++f) {
+    if (f + A < 32) vload(f + A, vb[(f + A) % (A + 1)]);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) mfma_o(oacc[h][f], vb[f % (A + 1)], pk[h]);
+  }
+}
+
+template <int NH>
+__global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
+                                                             const int32_t* __restrict__ block_table) {
+  constexpr int NW = 4;
+  constexpr int NS = 4;
+  using D = Dma<NW, false>;
+  constexpr int kPer = D::kPerWave;
+  static_assert(D::kSlotBytes == kBufBytes, "the chunk's copies fill the slot exactly");
+  static_assert(NS * kBufBytes <= 160 * 1024, "the ring fits in LDS");
+  static_assert(2 * kPer <= 63, "copies in flight within the 6-bit vmcnt");
+  __shared__ __attribute__((aligned(1024))) char ring0[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) char ring1[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) char ring2[kBufBytes];
+  __shared__ __attribute__((aligned(1024))) char ring3[kBufBytes];
+  auto ring = [&](auto slot_c) -> MLA_LDS char* {
+    constexpr int S = decltype(slot_c)::value % NS;
+    if constexpr (S == 0) return (MLA_LDS char*)ring0;
+    else if constexpr (S == 1) return (MLA_LDS char*)ring1;
+    else if constexpr (S == 2) return (MLA_LDS char*)ring2;
+    else return (MLA_LDS char*)ring3;
+  };
+
+  // blockIdx -> (item, row group): as decode_kernel (items of one XCD form a
+  // contiguous range of the item list)
+  const int gid = blockIdx.x;
+  const int xcd = gid & 7;
+  const int gslot = gid >> 3;
+  const int n_items = a.plan.header[0];
+  const int per_xcd = (n_items + 7) >> 3;
+  const int local = gslot / a.row_groups;
+  const int rg = gslot - local * a.row_groups;
+  const int item = xcd * per_xcd + local;
+  if (local >= per_xcd || item >= n_items) return;
+
+  const int b = a.plan.item_b[item];
+  const int p0 = a.plan.item_p0[item];
+  const int p1 = a.plan.item_p1[item];
+  const int len = a.seq_lens[b];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int gq = lane >> 4;
+  const int row0 = rg * NW * NH * 16 + wave * 16 * NH;  // first row of this wavefront
+  int tmax[NH];
+  int tmax_min = 0x7fffffff;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    tmax[h] = len - a.q_len + (row0 + 16 * h) / a.heads;
+    tmax_min = min(tmax_min, tmax[h]);
+  }
+  const int xs = gq ^ swz(n);
+  const int sbase_even = n * kEntryBytes + 16 * xs;
+  const int sbase_odd = n * kEntryBytes + 16 * (xs ^ 4) - 64;
+  int vbase[4];
+  {
+    const int r4 = (lane & 15) >> 2;
+    const int qq = lane & 3;
+    const int row = 4 * gq + r4;
+    const int y = (qq >> 1) ^ swz(row);
+#pragma unroll
+    for (int f4 = 0; f4 < 4; ++f4) {
+      vbase[f4] = row * kEntryBytes + 16 * ((2 * f4) ^ y) + 8 * (qq & 1);
+      asm volatile("" : "+v"(vbase[f4]));
+    }
+  }
+  bf16x8 qreg[NH][18];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+        a.q_abs + ((int64_t)b * a.rows_per_seq + row0 + 16 * h + n) * kEntry + 8 * gq);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) qreg[h][ks] = qp[4 * ks];
+  }
+  f32x4 oacc[NH][32];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int f = 0; f < 32; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[NH], l_run[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    m_ref[h] = -INFINITY;
+    l_run[h] = 0.f;
+  }
+  int* flag = a.restart_flag + blockIdx.x;
+  if (threadIdx.x == 0) __atomic_store_n(flag, 0, __ATOMIC_RELAXED);
+
+  const int tok_begin = p0 * kPage;
+  const int tok_end = min(p1 * kPage, len);
+  const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
+  const int jm = (tmax_min - tok_begin + 1) / kChunk;
+  const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
+  const char* cache = reinterpret_cast<const char*>(a.cache);
+  uint32_t doff[kPer];
+  dma_offsets<NW, kPer, false>(wave, lane, doff);
+  auto chunk_copy = [&](auto slot_c, int j) -> ChunkCopy {
+    const bool real = j < nchunks;
+    const int t = tok_begin + (real ? j : 0) * kChunk;
+    const int64_t blk = bt[t / kPage];
+    const int bytes = real ? min(tok_end - t, kChunk) * kEntryBytes : 0;
+    const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kEntryBytes;
+    return ChunkCopy{
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, bytes, kRsrcWord3),
+        ring(slot_c)};
+  };
+  auto issue_all = [&](const ChunkCopy& cc) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) copy_piece<D::kWaveBase, D::kStride>(cc, doff, i, wave);
+  };
+  auto chunk_limits = [&](int j, int (&lim)[NH]) {
+    const int t0 = tok_begin + j * kChunk;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) lim[h] = tmax[h] - t0 - 4 * gq;
+  };
+  bool need_restart = false;
+  bf16x8 pk[NH];
+  auto softmax = [&](f32x4 (&sacc)[NH][2], int j, auto first_c) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first_c)::value;
+    int lim[NH];
+    chunk_limits(j, lim);
+    if (j >= jm)
+      need_restart |= softmax_chunk<NH, kFirst, true>(sacc, pk, m_ref, l_run, lim);
+    else
+      need_restart |= softmax_chunk<NH, kFirst, false>(sacc, pk, m_ref, l_run, lim);
+  };
+
+  using T = std::true_type;
+  using F = std::false_type;
+  // prologue: chunks 0..2 in flight; the scores and softmax of chunk 0
+  issue_all(chunk_copy(Slot<0>{}, 0));
+  issue_all(chunk_copy(Slot<1>{}, 1));
+  issue_all(chunk_copy(Slot<2>{}, 2));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * kPer>());
+  ring_barrier();
+  {
+    f32x4 sacc[NH][2];
+    score_only<NH>(ring(Slot<0>{}), sbase_even, sbase_odd, qreg, sacc);
+    mfma_drain<NH>(sacc);
+    softmax(sacc, 0, T{});
+  }
+  // interval j: P.V of chunk j (slot j % 4) with the scores of chunk j+1
+  // (slot (j+1) % 4); chunk j+3 goes into slot (j+3) % 4, chunk j-1's.
+  auto interval = [&](auto s_c, int j) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_c)::value;
+    // chunk j+1 has landed once at most chunk j+2's copies are pending; the
+    // barrier also tells that every wavefront is done with chunk j-1
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<kPer>());
+    ring_barrier();
+    const ChunkCopy cc = chunk_copy(Slot<S + 3>{}, j + 3);
+    if (j + 1 < nchunks) {
+      f32x4 sacc[NH][2];
+      fused_interval<NH, kPer, D::kWaveBase, D::kStride>(ring(Slot<S>{}), vbase, pk, oacc,
+                                                         ring(Slot<S + 1>{}), sbase_even,
+                                                         sbase_odd, qreg, sacc, cc, doff, wave);
+      mfma_drain<NH>(sacc);
+      softmax(sacc, j + 1, F{});
+    } else if (j < nchunks) {
+      issue_all(cc);
+      pv_only<NH>(ring(Slot<S>{}), vbase, pk, oacc);
+    } else {
+      issue_all(cc);
+    }
+  };
+  for (int j = 0; j < nchunks; j += 4) {
+    interval(Slot<0>{}, j);
+    interval(Slot<1>{}, j + 1);
+    interval(Slot<2>{}, j + 2);
+    interval(Slot<3>{}, j + 3);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+  __syncthreads();
+  if (__builtin_amdgcn_ballot_w64(need_restart) != 0 && lane == 0)
+    __atomic_store_n(flag, 1, __ATOMIC_RELAXED);
+  __syncthreads();
+  const bool restart = __atomic_load_n(flag, __ATOMIC_RELAXED) != 0;
+
+  // ---- restart (rare): exact row max, then a pass with it as the reference --
+  if (restart) {
+    auto fetch = [&](int j) -> const MLA_LDS char* {
+      issue_all(chunk_copy(Slot<0>{}, j));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+      __syncthreads();
+      return ring(Slot<0>{});
+    };
+    float m_exact[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) m_exact[h] = -INFINITY;
+    for (int j = 0; j < nchunks; ++j) {
+      const MLA_LDS char* buf = fetch(j);
+      int lim[NH];
+      chunk_limits(j, lim);
+      f32x4 sacc[NH][2];
+      score_only<NH>(buf, sbase_even, sbase_odd, qreg, sacc);
+      mfma_drain<NH>(sacc);
+      max_chunk<NH>(sacc, m_exact, lim);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      m_ref[h] = m_exact[h];
+      l_run[h] = 0.f;
+    }
+    // (the wait states before the accumulators are overwritten)
+    mfma_drain_o<NH>(oacc);
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int f = 0; f < 32; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < nchunks; ++j) {
+      const MLA_LDS char* buf = fetch(j);
+      f32x4 sacc[NH][2];
+      score_only<NH>(buf, sbase_even, sbase_odd, qreg, sacc);
+      mfma_drain<NH>(sacc);
+      softmax(sacc, j, F{});
+      pv_only<NH>(buf, vbase, pk, oacc);
+      __syncthreads();
+    }
+  }
+  mfma_drain_o<NH>(oacc);
+
+  // ---- finalise: each wavefront normalises its own rows --------------------
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    float l = l_run[h];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float lse = l > 0.f ? m_ref[h] + __builtin_amdgcn_logf(l) : -INFINITY;
+    if (gq == 0) a.lse_part[(int64_t)item * a.rows_per_seq + row0 + 16 * h + n] = lse;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t orow = (int64_t)item * a.rows_per_seq + row0 + 16 * h + n;
+    uint16_t* op = a.o_part + orow * kLatent + 4 * gq;
+#pragma unroll
+    for (int f = 0; f < 32; ++f) {
+      u16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(oacc[h][f][i] * inv);
+      *reinterpret_cast<u16x4*>(op + 16 * f) = v;
+    }
+  }
+}
+
 DecodeConfig decode_config(int rows_per_seq) {
   const int groups = rows_per_seq / 16;
   DecodeConfig c;
   c.chunk = kChunk;
   c.nbuf = 4;
   if (groups % 8 == 0) {
-    // eight wavefronts of one row group each: two per SIMD, so one's LDS
-    // waits and softmax overlap the other's matrix work
-    c.waves = 8;
-    c.heads_per_wave = 1;
-    c.nbuf = 3;
+    // the pipelined kernel: four wavefronts of two row groups each, every
+    // wavefront accumulating all 512 features of its own rows
+    c.waves = 4;
+    c.heads_per_wave = 2;
+    c.pipe = 1;
   } else if (groups % 4 == 0) {
     c.waves = 2;
     c.heads_per_wave = 2;
@@ -859,6 +1334,7 @@ DecodeConfig decode_config(int rows_per_seq) {
     c.waves = 1;
     c.heads_per_wave = 1;
   }
+  if (c.waves == 1) c.nbuf = 3;
   c.lds_bytes = c.nbuf * kBufBytes + c.waves * c.heads_per_wave * (1024 + 64);
   c.wgs_per_cu = 1;  // the ring fills the LDS
   return c;
@@ -903,6 +1379,11 @@ hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_ab
   args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
+  if (cfg.pipe && !fp8) {
+    hipLaunchKernelGGL((decode_pipe_kernel<2>), dim3(grid), dim3(256), 0, stream, args,
+                       block_table);
+    return hipGetLastError();
+  }
   // (the FP8 cache runs the four-wavefront kernel: same rows per workgroup,
   // so the same workspace layout)
   if (cfg.waves == 8)

@@ -94,6 +94,7 @@ struct DecodeConfig {
   int nbuf;     // LDS ring depth (chunks)
   int lds_bytes;
   int wgs_per_cu;
+  int pipe = 0;  // 1: the pipelined kernel (four wavefronts owning their rows' outputs)
 };
 DecodeConfig decode_config(int rows_per_seq);
 
@@ -122,7 +123,8 @@ hipError_t launch_index_scores(const uint8_t* index_q, const float* index_w, int
                                const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
                                int batch, int max_seq_len, float* scores, int lpad,
                                hipStream_t stream);
-hipError_t launch_topk(const float* scores, int lpad, const int32_t* seq_lens, int batch,
+hipError_t launch_topk(const float* scores, int lpad, const int32_t* seq_lens, int max_seq_len,
+                       int batch,
                        int top_k, int32_t* kept, int32_t* counts, hipStream_t stream);
 hipError_t launch_gather(bool fp8, const void* cache, const int32_t* block_table, int bt_stride,
                          const int32_t* kept, int top_k, const int32_t* counts, int batch,
