@@ -740,6 +740,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   issue(Slot<1>{}, 1);
   if constexpr (FP8 || NS == 4) issue(Slot<2>{}, 2);
   if constexpr (FP8) {
+    // chunk 0 has landed once at most the copies of chunks 1 and 2 are
+    // pending.  The wait is explicit: left to the compiler, the 8-wavefront
+    // build read the rows' scale bytes before the wait it inserted for the
+    // codes (the scheduler moved the byte loads above it), so every item's
+    // first chunk was expanded with stale scales.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * kPer>());
     dequant_rows<NW>(ring(Slot<0>{}), stage_of(0), wave, lane);
     interval(Slot<0>{}, T{}, 0);
     for (int j = 1; j < nchunks; j += 3) {
@@ -1343,13 +1349,7 @@ DecodeConfig decode_config(int rows_per_seq) {
 template <int NW, int NH>
 static hipError_t launch_t(int grid, bool fp8, const DecodeArgs& args,
                           const int32_t* block_table, hipStream_t stream) {
-  if constexpr (NW == 8) {
-    // no FP8 build of the eight-wavefront kernel (launch_decode routes FP8
-    // caches to the four-wavefront one)
-    if (fp8) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_kernel<NW, NH, false>), dim3(grid), dim3(NW * 64), 0, stream,
-                       args, block_table);
-  } else if (fp8) {
+  if (fp8) {
     hipLaunchKernelGGL((decode_kernel<NW, NH, true>), dim3(grid), dim3(NW * 64), 0, stream, args,
                        block_table);
   } else {
@@ -1379,17 +1379,13 @@ hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_ab
   args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
-  if (cfg.pipe && !fp8) {
+  if (cfg.pipe) {
+    // FP8 rows: the eight-wavefront kernel, same 128 rows per workgroup
+    if (fp8) return launch_t<8, 1>(grid, fp8, args, block_table, stream);
     hipLaunchKernelGGL((decode_pipe_kernel<2>), dim3(grid), dim3(256), 0, stream, args,
                        block_table);
     return hipGetLastError();
   }
-  // (the FP8 cache runs the four-wavefront kernel: same rows per workgroup,
-  // so the same workspace layout)
-  if (cfg.waves == 8)
-    return fp8 ? launch_t<4, 2>(grid, fp8, args, block_table, stream)
-               : launch_t<8, 1>(grid, fp8, args, block_table, stream);
-  if (cfg.waves == 4) return launch_t<4, 2>(grid, fp8, args, block_table, stream);
   if (cfg.waves == 2) return launch_t<2, 2>(grid, fp8, args, block_table, stream);
   if (cfg.heads_per_wave == 2) return launch_t<1, 2>(grid, fp8, args, block_table, stream);
   return launch_t<1, 1>(grid, fp8, args, block_table, stream);

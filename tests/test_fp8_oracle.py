@@ -150,3 +150,58 @@ def test_decode_fp8_equals_bf16_decode_on_exactly_representable_cache():
     a = fp8.decode_expanded_fp8(d["q"], d["kv_b"], c8, d["block_table"], d["seq_lens"], 2)
     b = decode_expanded(d["q"], d["kv_b"], cbf, d["block_table"], d["seq_lens"], 2)
     assert np.array_equal(a, b)
+
+
+# ---- what the FP8 format costs against the bf16 cache (error budget) --------
+#
+# Derivation.  An E4M3 value with mantissa m in [1, 2) and exponent k sits in a
+# binade whose quantum is 2^(k-3); round to nearest even leaves an error
+# uniform in half a quantum, so the relative error of x = m 2^k is uniform in
+# +-2^-4 / m and its mean square is (2^-4)^2 E[m^-2] / 3.  E[m^-2] is 1/2 for
+# mantissas uniform in [1, 2) and 0.541 for log-uniform ones (N(0, 1) draws lie
+# between), so the per-element relative RMS error is
+#     eps = 2^-4 sqrt(E[m^-2] / 3)  in [0.0255, 0.0266].
+# (The per-token power-of-two scale only moves exponents, it never rounds.)
+# In the decode, the latent error enters the values directly (relative eps)
+# and the scores through q_lat . dc (a fraction f of the score variance comes
+# from the latent, the rope part stays bf16); a score error ds moves each
+# weight by p ds, so for independent value rows the output's relative RMS
+# error is about
+#     eps sqrt(1 + f sigma_s^2)
+# with sigma_s the score spread in natural-log units.  The workloads draw
+# q, c ~ N(0, 1) and kv_b with variance 1/512: q_lat . c has variance 128 and
+# q_pe . k_pe 64, so f = 2/3 and sigma_s = 1 after the 1/sqrt(192) scale,
+# giving a budget of 0.0266 sqrt(5/3) = 0.0343 (plus the bf16 pipeline's own
+# ~3e-3 when both sides run on the GPU, added in quadrature).
+FP8_EPS_LO, FP8_EPS_HI = 2.0 ** -4 * np.sqrt(0.5 / 3), 2.0 ** -4 * np.sqrt(0.541 / 3)
+FP8_OUT_BUDGET = FP8_EPS_HI * np.sqrt(1.0 + 2.0 / 3.0)
+
+
+def _finite_bf16(c):
+    v = (np.asarray(c, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return np.where(np.isfinite(v), c, np.uint16(0)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("case", [(2, 128, [2048, 777], 69), (2, 16, [3000, 1500], 70),
+                                  (1, 128, [300], 71)])
+def test_fp8_error_budget_matches_derivation(case):
+    """The oracle's FP8 decode against its bf16 decode of the same rows: the
+    per-element latent error matches eps (within 5 % of the derived band) and
+    the output's relative RMS error stays within the derived budget."""
+    bsz, heads, lens, seed = case
+    d = wl.make_inputs(bsz, 1, heads, lens, permute=True, seed=seed)
+    c = _finite_bf16(cache_insert(d["cache"], d["kv_a"], d["rms_w"], d["block_table"],
+                                  d["seq_lens"], 1, float(np.float32(wl.EPS)), wl.ROPE_BASE,
+                                  wl.LATENT))
+    deq = fp8.dequantize_cache(fp8.quantize_cache(c))
+    lat = bf16_bits_to_f64(c[..., :512])
+    nz = lat != 0
+    eps = np.sqrt(np.mean(((deq[..., :512][nz] - lat[nz]) / lat[nz]) ** 2))
+    assert 0.95 * FP8_EPS_LO <= eps <= 1.05 * FP8_EPS_HI, eps
+    # the rope part is copied exactly
+    assert np.array_equal(deq[..., 512:], bf16_bits_to_f64(c[..., 512:]))
+    ref = decode_expanded(d["q"], d["kv_b"], c, d["block_table"], d["seq_lens"], 1)
+    out = decode_expanded(d["q"], d["kv_b"], deq, d["block_table"], d["seq_lens"], 1)
+    err = out - ref
+    rr = np.sqrt(np.mean(err ** 2) / np.mean(ref ** 2))
+    assert 0.5 * FP8_EPS_LO <= rr <= FP8_OUT_BUDGET, (rr, FP8_OUT_BUDGET)

@@ -200,10 +200,19 @@ def test_decode_fp8_ignores_rows_beyond_length_and_split_count():
         assert mx <= MAX_ABS and rr <= REL_RMS
 
 
+# The FP8 format's cost against the bf16 cache, derived from E4M3's 3-bit
+# mantissa (tests/test_fp8_oracle.py, FP8_OUT_BUDGET: 2^-4 sqrt(0.541 / 3)
+# sqrt(1 + 2/3) = 0.0343 relative RMS at these workloads' score statistics),
+# plus the bf16 pipeline error of the two GPU decodes (about 3.5e-3 each,
+# measured against the oracle) in quadrature.
+FP8_GPU_BUDGET = float(np.hypot(2.0 ** -4 * np.sqrt(0.541 / 3) * np.sqrt(5.0 / 3.0),
+                                2 * 3.5e-3))
+
+
 def test_fp8_cache_error_against_bf16_cache():
     """What the format costs (a property of the method, not a parity claim):
     the same tokens inserted into a bf16 and an FP8 cache, decoded on the
-    GPU; reported, and bounded loosely."""
+    GPU, within the budget derived from the format."""
     torch = _torch()
     import mla_latent_kv_07_amd as mla
     say("[decode fp8] quantisation error against the bf16 cache")
@@ -221,8 +230,8 @@ def test_fp8_cache_error_against_bf16_cache():
                    dev(d["block_table"], torch), dev(d["seq_lens"], torch),
                    int(d["seq_lens"].max())).float().cpu().numpy().astype(np.float64)
     mx, rr = errors(a, b)
-    say(f"   FP8 vs bf16 cache: max-abs {mx:.3e} rel-rms {rr:.3e}")
-    assert rr < 0.1
+    say(f"   FP8 vs bf16 cache: max-abs {mx:.3e} rel-rms {rr:.3e} (budget {FP8_GPU_BUDGET:.3e})")
+    assert rr <= FP8_GPU_BUDGET
 
 
 def test_decode_fp8_restart_on_score_jump():
