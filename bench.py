@@ -61,6 +61,10 @@ def parse():
     ap.add_argument("--cache-state", choices=("auto", "cold", "warm"), default="auto",
                     help="cold: flush the last-level cache before every timed step (auto: "
                          "for the workloads whose cache fits in it)")
+    ap.add_argument("--settle-ms", type=float, default=1500.0,
+                    help="after the warmup steps, keep running the step for this long (untimed) "
+                         "so that the GPU's clocks reach their steady state under this load "
+                         "before the timed steps (0: off)")
     ap.add_argument("--eager", action="store_true",
                     help="launch the step's kernels one call at a time instead of replaying a "
                          "captured HIP graph of the step")
@@ -484,6 +488,7 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
         run = graph.replay
+    settle(run, args.settle_ms, torch)
     step_ms = []
     if cold:
         # each step timed alone with HIP events, the flush outside the events
@@ -576,7 +581,8 @@ def main():
                    "cache": args.cache, "launch": "eager" if args.eager else "hip graph",
                    "timing": ("cold: the 256 MB last-level cache flushed (512 MiB written) "
                               "before every step, each step timed alone with HIP events"
-                              if cold else "warm: steps back to back, wall clock")},
+                              if cold else "warm: steps back to back, wall clock"),
+                   "settle_ms": args.settle_ms},
         "tokens_per_s": round(bsz * q_len / (ms_step * 1e-3), 1),
         "alg_bytes_per_step": alg_bytes,
         "alg_flops_per_step": alg_flops,
@@ -609,6 +615,21 @@ def main():
 
 COPY_MIB = 1024
 FLUSH_BYTES = 512 << 20
+
+
+def settle(run, ms: float, torch) -> None:
+    """Run the step back to back for about ``ms`` milliseconds of wall time,
+    untimed.  The shader clock ramps up over the first few hundred
+    milliseconds of sustained load (same-process repeats of the V3 decode
+    took 175, 148, 137, 130 and 128 us in successive rounds of 23 calls), so
+    the timed steps start from the steady state a serving loop runs in."""
+    if ms <= 0:
+        return
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(20):
+            run()
+        torch.cuda.synchronize()
 
 
 def copy_ceiling(torch) -> float:
