@@ -20,24 +20,37 @@
 
 namespace mla {
 
-constexpr int kCombRows = 32;                 // query rows per workgroup
 constexpr int kCombRowBytes = kLatent * 2 + 16;  // padded LDS row (bank spread)
 
+// RB query rows per workgroup; SP wavefronts share each row, each merging
+// every SP-th split of it (SP = 1: every wavefront owns RB/4 rows and all
+// their splits; SP = 4: all four wavefronts take the same RB rows and a
+// quarter of the splits each, for few rows with many splits).  Every
+// wavefront weighs its splits by exp2(lse - M) with M the row's maximum over
+// ALL splits, so the SP partial sums of a row simply add (through LDS).
+template <int RB, int SP>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       PlanView plan,
                                                       const uint16_t* __restrict__ kv_b,
                                                       int heads, int q_len, int batch,
                                                       uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) char olat[kCombRows * kCombRowBytes];
+  constexpr int R = RB * SP / 4;  // rows per wavefront
+  static_assert(R * 4 == RB * SP && RB % R == 0, "four wavefronts: RB / R row groups x SP");
+  constexpr int kPartBytes = SP > 1 ? 4 * R * kLatent * 4 : 16;  // fp32 partial sums
+  __shared__ __attribute__((aligned(16))) char olat[(RB < 16 ? 16 : RB) * kCombRowBytes];
+  __shared__ __attribute__((aligned(16))) char part[kPartBytes];
+  __shared__ float psum[4 * R];
   const int h = blockIdx.x;
-  const int row_base = blockIdx.y * kCombRows;  // first (b, i) row of this workgroup
+  const int row_base = blockIdx.y * RB;  // first (b, i) row of this workgroup
   const int total_rows = batch * q_len;
   const int rows_per_seq = heads * q_len;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
+  const int row_off = (wave / SP) * R;  // first row of this wavefront in the block
+  const int ws = wave % SP;             // first split of this wavefront
 
   // ---- W_UV rows of this wavefront's outputs d in [32w, 32w+32), all of K --
   // (A operand of D^T = W_UV o_lat^T; independent of the merge, so loaded
@@ -51,19 +64,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
       aw[ks][mt] = *reinterpret_cast<const bf16x8*>(
           wuv + (int64_t)(wave * 32 + mt * 16 + n) * kLatent + 32 * ks + 8 * g);
 
-  // ---- merge: wave w handles rows w*8 .. w*8+7 together; lane covers 8 columns
+  // ---- merge: lane covers 8 columns of each of the wavefront's R rows ------
   // The split weights are lane-parallel (lane s <-> split s, 64 splits per
   // pass); the bf16 partial rows are loaded KB splits at a time with
   // independent loads before any is used.
   {
-    constexpr int R = kCombRows / 4;
     constexpr int KB = 4;
     int s0[R], ns[R];
     int64_t srow[R];
     bool live[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      const int bi = row_base + wave * R + u;
+      const int bi = row_base + row_off + u;
       live[u] = bi < total_rows;
       const int b = live[u] ? bi / q_len : 0;
       const int i = live[u] ? bi - b * q_len : 0;
@@ -84,21 +96,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
       const float v = lse_part[(int64_t)split_of(u, s) * rows_per_seq + srow[u]];
       return s < ns[u] ? v : -INFINITY;
     };
-    // first pass: the lse of split `lane` and the partial rows of splits 0..KB-1
+    // this wavefront's k-th split is ws + SP k; the first pass: the lse of
+    // splits 0..63 (lane s) and the partial rows of this wavefront's first KB
     float lse0[R];
     u16x8 v0[R][KB];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       lse0[u] = lse_of(u, lane);
 #pragma unroll
-      for (int k = 0; k < KB; ++k) v0[u][k] = part_row(u, k);
+      for (int k = 0; k < KB; ++k) v0[u][k] = part_row(u, ws + SP * k);
     }
     int nmax = 0;
 #pragma unroll
     for (int u = 0; u < R; ++u) nmax = max(nmax, ns[u]);
-    // (KB is a multiple of 4 and divides 64: a batch never straddles two
-    // 64-split blocks of weights)
-    // max log2-sum-exp over all splits of each row
+    // max log2-sum-exp over all splits of each row (every wavefront: the same M)
     float mx[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
@@ -114,12 +125,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int u = 0; u < R; ++u)
       w_l[u] = lse0[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lse0[u] - mx[u]);
+    // (KB SP is a multiple of 4 dividing 64: a batch never straddles two
+    // 64-split blocks of weights)
     auto accumulate = [&](const u16x8 (&v)[R][KB], int s, bool first) {
 #pragma unroll
       for (int u = 0; u < R; ++u)
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
-          const float w = __shfl(w_l[u], (s + k) & 63, 64);  // 0 beyond ns (lse -inf)
+          const float w = __shfl(w_l[u], (s + SP * k) & 63, 64);  // 0 beyond ns (lse -inf)
           wsum[u] = (first && k == 0) ? w : wsum[u] + w;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -127,12 +140,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                                            : macc[u][e] + w * bf16_to_f32(v[u][k][e]);
         }
     };
-    accumulate(v0, 0, true);
-    for (int s = KB; s < nmax; s += KB) {
-      if ((s & 63) == 0) {
+    accumulate(v0, ws, true);
+    for (int s = ws + SP * KB; s < nmax; s += SP * KB) {
+      if ((s >> 6) != ((s - SP * KB) >> 6)) {
+        // a new block of 64 splits: their weights, lane-parallel
 #pragma unroll
         for (int u = 0; u < R; ++u) {
-          const float lse = lse_of(u, s + lane);
+          const float lse = lse_of(u, (s & ~63) + lane);
           w_l[u] = lse == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lse - mx[u]);
         }
       }
@@ -140,23 +154,65 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int u = 0; u < R; ++u)
 #pragma unroll
-        for (int k = 0; k < KB; ++k)
-          v[u][k] = part_row(u, s + k);
+        for (int k = 0; k < KB; ++k) v[u][k] = part_row(u, s + SP * k);
       accumulate(v, s, false);
     }
+    if constexpr (SP == 1) {
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const float inv = wsum[u] > 0.f ? 1.f / wsum[u] : 0.f;
-      u16x8 packed;
+      for (int u = 0; u < R; ++u) {
+        const float inv = wsum[u] > 0.f ? 1.f / wsum[u] : 0.f;
+        u16x8 packed;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) packed[e] = live[u] ? f32_to_bf16(macc[u][e] * inv) : 0;
-      *reinterpret_cast<u16x8*>(olat + (wave * R + u) * kCombRowBytes + lane * 16) = packed;
+        for (int e = 0; e < 8; ++e) packed[e] = live[u] ? f32_to_bf16(macc[u][e] * inv) : 0;
+        *reinterpret_cast<u16x8*>(olat + (row_off + u) * kCombRowBytes + lane * 16) = packed;
+      }
+    } else {
+      // the SP partial sums of each row: through LDS (wavefront w's row u
+      // at w R + u), then wavefront w finishes block rows w, w + 4, ..
+      float* pp = reinterpret_cast<float*>(part);
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 4)
+          *reinterpret_cast<f32x4*>(pp + ((wave * R + u) * kLatent) + lane * 8 + e) =
+              f32x4{macc[u][e], macc[u][e + 1], macc[u][e + 2], macc[u][e + 3]};
+        if (lane == 0) psum[wave * R + u] = wsum[u];
+      }
+      __syncthreads();
+      for (int r = wave; r < RB; r += 4) {
+        const int w0 = (r / R) * SP;  // the wavefronts of row r's group
+        const int u = r % R;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float ws_all = 0.f;
+#pragma unroll
+        for (int k = 0; k < SP; ++k) {
+          ws_all += psum[(w0 + k) * R + u];
+#pragma unroll
+          for (int e = 0; e < 8; e += 4) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(pp + (((w0 + k) * R + u) * kLatent) +
+                                                            lane * 8 + e);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[e + c] += t[c];
+          }
+        }
+        const float inv = ws_all > 0.f ? 1.f / ws_all : 0.f;
+        const bool lv = row_base + r < total_rows;
+        u16x8 packed;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) packed[e] = lv ? f32_to_bf16(acc[e] * inv) : 0;
+        *reinterpret_cast<u16x8*>(olat + r * kCombRowBytes + lane * 16) = packed;
+      }
     }
+  }
+  if constexpr (RB < 16) {
+    // rows RB .. 15 of the 16-row product tile are zero
+    for (int u = RB + wave; u < 16; u += 4)
+      *reinterpret_cast<u16x8*>(olat + u * kCombRowBytes + lane * 16) = u16x8{};
   }
   __syncthreads();
 
-  // ---- projection: wave w computes d in [32w, 32w+32) for all 32 rows -------
-  constexpr int NT = kCombRows / 16;
+  // ---- projection: wave w computes d in [32w, 32w+32) for all rows --------
+  constexpr int NT = (RB + 15) / 16;
   f32x4 acc[2][NT];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -179,8 +235,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   // D^T[d][row]: lane holds d = 16mt + 4g + i of row n of tile nt
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int bi = row_base + nt * 16 + n;
-    if (bi >= total_rows) continue;
+    const int r = nt * 16 + n;
+    const int bi = row_base + r;
+    if (r >= RB || bi >= total_rows) continue;
     uint16_t* dst = out + ((int64_t)bi * heads + h) * kVdim + wave * 32;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -194,11 +251,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 
 hipError_t launch_combine(const uint16_t* o_part, const float* lse_part, PlanView plan,
                           const uint16_t* kv_b, int heads, int q_len, int batch, uint16_t* out,
-                          hipStream_t stream) {
+                          int cus, hipStream_t stream) {
   const int rows = batch * q_len;
-  dim3 grid(heads, (rows + kCombRows - 1) / kCombRows);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, o_part, lse_part, plan, kv_b,
-                     heads, q_len, batch, out);
+  // the largest row block that still gives every CU a workgroup: W_UV (128
+  // KB per head) is read once per block, so fewer blocks read less
+  if (heads * ((rows + 31) / 32) >= cus) {
+    hipLaunchKernelGGL((combine_kernel<32, 1>), dim3(heads, (rows + 31) / 32), dim3(256), 0,
+                       stream, o_part, lse_part, plan, kv_b, heads, q_len, batch, out);
+  } else if (heads * ((rows + 15) / 16) >= cus) {
+    hipLaunchKernelGGL((combine_kernel<16, 2>), dim3(heads, (rows + 15) / 16), dim3(256), 0,
+                       stream, o_part, lse_part, plan, kv_b, heads, q_len, batch, out);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<8, 4>), dim3(heads, (rows + 7) / 8), dim3(256), 0, stream,
+                       o_part, lse_part, plan, kv_b, heads, q_len, batch, out);
+  }
   return hipGetLastError();
 }
 

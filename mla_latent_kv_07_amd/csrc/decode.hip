@@ -893,20 +893,24 @@ __device__ __forceinline__ void mfma_o(f32x4& acc, const bf16x8& a, const bf16x8
 // scores (they pass through this statement).
 template <int NH>
 __device__ __forceinline__ void mfma_drain(f32x4 (&sacc)[NH][2]) {
-  static_assert(NH == 2, "four score tiles");
-  asm volatile("s_nop 7\n\ts_nop 3"
-               : "+v"(sacc[0][0]), "+v"(sacc[0][1]), "+v"(sacc[1][0]), "+v"(sacc[1][1]));
+  static_assert(NH == 1 || NH == 2, "two or four score tiles");
+  if constexpr (NH == 2)
+    asm volatile("s_nop 7\n\ts_nop 3"
+                 : "+v"(sacc[0][0]), "+v"(sacc[0][1]), "+v"(sacc[1][0]), "+v"(sacc[1][1]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 3" : "+v"(sacc[0][0]), "+v"(sacc[0][1]));
 }
 // The same for the output tiles before they are read (after the chunk loop):
 // the wait states first, then every tile passes through an (empty) statement
 // ordered after them.
-template <int NH>
-__device__ __forceinline__ void mfma_drain_o(f32x4 (&oacc)[NH][32]) {
+template <int NH, int FT>
+__device__ __forceinline__ void mfma_drain_o(f32x4 (&oacc)[NH][FT]) {
+  static_assert(FT % 8 == 0, "tiles pass through in eights");
   asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
   for (int h = 0; h < NH; ++h)
 #pragma unroll
-    for (int f = 0; f < 32; f += 8)
+    for (int f = 0; f < FT; f += 8)
       asm volatile(""
                    : "+a"(oacc[h][f]), "+a"(oacc[h][f + 1]), "+a"(oacc[h][f + 2]),
                      "+a"(oacc[h][f + 3]), "+a"(oacc[h][f + 4]), "+a"(oacc[h][f + 5]),
@@ -930,20 +934,33 @@ __device__ __forceinline__ void score_step(int ks, const bf16x8 (&kb)[2],
 }
 
 // Unit map of one fused interval: kFusedScore score k-steps spread over the
-// first kFusedSpan of the kFusedUnits slots, P.V feature tiles in the others.
+// first fused_span(FT) of its kFusedScore + FT units, the FT P.V feature tiles
+// in the others.
 constexpr int kFusedScore = 18;
-constexpr int kFusedPv = 32;
-constexpr int kFusedUnits = kFusedScore + kFusedPv;
-constexpr int kFusedSpan = 44;
-constexpr int kFusedAhead = 3;
+constexpr int kFusedAhead = 6;  // LDS reads issued six units ahead
+// The first fused_pre(FT) units are P.V units: they read only the chunk
+// whose probabilities are known, so their LDS reads are issued at the end of
+// the previous interval, before its barrier (their latency hides under it).
+constexpr int fused_pre(int ft) { return ft - 6 < kFusedAhead ? ft - 6 : kFusedAhead; }
+// Then the score k-steps: on every other unit of 36 (32 tiles), or on the
+// units that leave six after the last k-step (fewer tiles).
+constexpr int fused_span(int ft) { return ft == 32 ? 36 : kFusedScore + ft - fused_pre(ft) - 6; }
+// After unit fused_mid(FT) (the last score k-step) the scores are complete:
+// the softmax of the next chunk runs in pieces between the remaining units.
+constexpr int fused_mid(int ft) {
+  return fused_pre(ft) + (kFusedScore - 1) * fused_span(ft) / kFusedScore;
+}
+template <int FT>
 struct FusedMap {
-  int kind[kFusedUnits];  // 0: score k-step, 1: P.V feature tile
-  int idx[kFusedUnits];   // the k-step or the tile
-  int copy[kFusedUnits];  // copy instructions issued at this unit
+  static constexpr int kUnits = kFusedScore + FT;
+  static_assert(fused_mid(FT) + 6 <= kUnits, "softmax pieces fit after the last k-step");
+  int kind[kUnits];  // 0: score k-step, 1: P.V feature tile
+  int idx[kUnits];   // the k-step or the tile
+  int copy[kUnits];  // copy instructions issued at this unit
   constexpr FusedMap(int ncopies) : kind(), idx(), copy() {
     int s = 0, p = 0;
-    for (int u = 0; u < kFusedUnits; ++u) {
-      if (s < kFusedScore && u == s * kFusedSpan / kFusedScore) {
+    for (int u = 0; u < kUnits; ++u) {
+      if (s < kFusedScore && u == fused_pre(FT) + s * fused_span(FT) / kFusedScore) {
         kind[u] = 0;
         idx[u] = s++;
       } else {
@@ -953,7 +970,7 @@ struct FusedMap {
       copy[u] = 0;
     }
     // one copy per unit, from unit 1 on (every other unit while they last)
-    for (int c = 0; c < ncopies; ++c) copy[(1 + 2 * c) % kFusedUnits] += 1;
+    for (int c = 0; c < ncopies; ++c) copy[(1 + 2 * c) % kUnits] += 1;
   }
 };
 
@@ -966,12 +983,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Reads of fused unit v into rb: a score k-step's two K pieces from the
-// chunk at (be, bo), or a P.V feature tile of V^T from the chunk at pv.
-template <int V>
+// chunk at (be, bo), or a P.V feature tile of V^T from the chunk at pv (tile f
+// of the wavefront's slice at vbase[f & 3] + 128 (f >> 2); vbase holds the
+// slice's offset).
+template <int V, int FT>
 __device__ __forceinline__ void fused_reads(bf16x8 (&rb)[2], const MLA_LDS char* be,
                                             const MLA_LDS char* bo, const MLA_LDS char* pv,
                                             const int (&vbase)[4]) {
-  constexpr FusedMap m(0);
+  constexpr FusedMap<FT> m(0);
   constexpr int i = m.idx[V];
   if constexpr (m.kind[V] == 0) {
 #pragma unroll
@@ -991,43 +1010,83 @@ __device__ __forceinline__ void fused_reads(bf16x8 (&rb)[2], const MLA_LDS char*
 // chunk j+1 (slot `sc`, into sacc), the copies of `cc` issued along the way.
 // Every matrix instruction is an ordered asm statement, so the stream runs in
 // the order written: per unit its copies, the LDS reads of the unit
-// kFusedAhead later, then its MFMAs.
-template <int NH, int KPER, int WB, int ST>
+// kFusedAhead later, then its MFMAs; after the last score k-step, mid(unit)
+// runs between the units (the next chunk's softmax, see the kernel).
+// The LDS reads of the first fused_pre(FT) units (P.V tiles of the chunk at
+// pv), issued ahead of the interval.
+template <int FT>
+__device__ __forceinline__ void fused_prefetch(bf16x8 (&rb)[kFusedAhead + 1][2],
+                                               const MLA_LDS char* pv, const int (&vbase)[4]) {
+  static_for<0, fused_pre(FT)>([&](auto v_c) __attribute__((always_inline)) {
+    constexpr int v = decltype(v_c)::value;
+    fused_reads<v, FT>(rb[v % (kFusedAhead + 1)], nullptr, nullptr, pv, vbase);
+  });
+}
+
+// (rb: the read-ahead registers, the first fused_pre(FT) units' reads already
+// issued by fused_prefetch)
+template <int NH, int FT, int KPER, int WB, int ST, class Mid>
 __device__ __forceinline__ void fused_interval(const MLA_LDS char* pv, const int (&vbase)[4],
-                                               const bf16x8 (&pk)[NH], f32x4 (&oacc)[NH][32],
+                                               const bf16x8 (&pk)[NH], f32x4 (&oacc)[NH][FT],
                                                const MLA_LDS char* sc, int sbase_even,
                                                int sbase_odd, const bf16x8 (&qreg)[NH][18],
                                                f32x4 (&sacc)[NH][2], const ChunkCopy& cc,
-                                               const uint32_t* off, int wave) {
-  constexpr FusedMap m(KPER);
+                                               const uint32_t* off, int wave,
+                                               bf16x8 (&rb)[kFusedAhead + 1][2], Mid&& mid) {
+  using M = FusedMap<FT>;
+  constexpr M m(KPER);
+  constexpr int U = M::kUnits;
   const MLA_LDS char* be = sc + sbase_even;
   const MLA_LDS char* bo = sc + sbase_odd;
-  bf16x8 rb[kFusedAhead + 1][2];
-  static_for<0, kFusedAhead>([&](auto v_c) __attribute__((always_inline)) {
+  static_for<fused_pre(FT), kFusedAhead>([&](auto v_c) __attribute__((always_inline)) {
     constexpr int v = decltype(v_c)::value;
-    fused_reads<v>(rb[v % (kFusedAhead + 1)], be, bo, pv, vbase);
+    fused_reads<v, FT>(rb[v % (kFusedAhead + 1)], be, bo, pv, vbase);
   });
-  static_for<0, kFusedUnits>([&](auto u_c) __attribute__((always_inline)) {
+  static_for<0, U>([&](auto u_c) __attribute__((always_inline)) {
     constexpr int u = decltype(u_c)::value;
     constexpr int r = u % (kFusedAhead + 1);
     constexpr int i = m.idx[u];
     constexpr int c0 = [] {
-      constexpr FusedMap mm(KPER);
+      constexpr M mm(KPER);
       int c = 0;
       for (int k = 0; k < u; ++k) c += mm.copy[k];
       return c;
     }();
 #pragma unroll
     for (int c = 0; c < m.copy[u]; ++c) copy_piece<WB, ST>(cc, off, c0 + c, wave);
-    if constexpr (u + kFusedAhead < kFusedUnits)
-      fused_reads<u + kFusedAhead>(rb[(u + kFusedAhead) % (kFusedAhead + 1)], be, bo, pv, vbase);
+    if constexpr (u + kFusedAhead < U)
+      fused_reads<u + kFusedAhead, FT>(rb[(u + kFusedAhead) % (kFusedAhead + 1)], be, bo, pv,
+                                       vbase);
     if constexpr (m.kind[u] == 0) {
       score_step<NH>(i, rb[r], qreg, sacc);
     } else {
 #pragma unroll
       for (int h = 0; h < NH; ++h) mfma_o(oacc[h][i], rb[r][0], pk[h]);
     }
+    if constexpr (u >= fused_mid(FT)) {
+      // the next chunk's softmax in pieces between the remaining P.V units
+      __builtin_amdgcn_sched_barrier(0);
+      mid(u_c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   });
+}
+
+// One piece of the masked softmax of a chunk (see softmax_chunk): row group
+// H, positions 16T .. 16T+15 of this lane's four: p = 2^(s - ref) (0 past the
+// causal limit), summed into psum[H], rounded into pk[H][4T .. 4T+3].
+template <int NH, int H, int T>
+__device__ __forceinline__ void softmax_piece(const f32x4 (&sacc)[NH][2], bf16x8 (&pk)[NH],
+                                              const float (&m_ref)[NH], float (&psum)[NH],
+                                              const int (&lim)[NH]) {
+  const float m_use = m_ref[H] == -INFINITY ? 0.f : m_ref[H];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float sv = (16 * T + i > lim[H]) ? -INFINITY : sacc[H][T][i];
+    const float p = __builtin_amdgcn_exp2f(sv - m_use);
+    psum[H] = (T == 0 && i == 0) ? p : psum[H] + p;
+    pk[H][T * 4 + i] = (__bf16)p;
+  }
 }
 
 // Scores of one chunk alone (the first chunk of an item, and the restart
@@ -1056,9 +1115,9 @@ __device__ __forceinline__ void score_only(const MLA_LDS char* buf, int sbase_ev
 }
 
 // P.V of one chunk alone (the last chunk of an item, and the restart pass).
-template <int NH>
+template <int NH, int FT>
 __device__ __forceinline__ void pv_only(const MLA_LDS char* buf, const int (&vbase)[4],
-                                        const bf16x8 (&pk)[NH], f32x4 (&oacc)[NH][32]) {
+                                        const bf16x8 (&pk)[NH], f32x4 (&oacc)[NH][FT]) {
   constexpr int A = 3;
   bf16x8 vb[A + 1];
   auto vload = [&](int f, bf16x8& dst) {
@@ -1071,14 +1130,19 @@ __device__ __forceinline__ void pv_only(const MLA_LDS char* buf, const int (&vba
 #pragma unroll
   for (int f = 0; f < A; ++f) vload(f, vb[f]);
 #pragma unroll
-  for (int f = 0; f < 32; ++f) {
-    if (f + A < 32) vload(f + A, vb[(f + A) % (A + 1)]);
+  for (int f = 0; f < FT; ++f) {
+    if (f + A < FT) vload(f + A, vb[(f + A) % (A + 1)]);
 #pragma unroll
     for (int h = 0; h < NH; ++h) mfma_o(oacc[h][f], vb[f % (A + 1)], pk[h]);
   }
 }
 
-template <int NH>
+// FS = 1: four wavefronts of NH row groups each (4 NH 16 rows), every
+// wavefront accumulating all 512 features of its rows.  FS = 2 or 4: FS
+// wavefronts share the same NH row groups (each scores them, so each has the
+// probabilities) and take 32 / FS feature tiles each; the workgroup covers
+// (4 / FS) NH 16 rows.
+template <int NH, int FS>
 __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
                                                              const int32_t* __restrict__ block_table) {
   constexpr int NW = 4;
@@ -1120,7 +1184,10 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int gq = lane >> 4;
-  const int row0 = rg * NW * NH * 16 + wave * 16 * NH;  // first row of this wavefront
+  constexpr int FT = 32 / FS;                 // feature tiles of a wavefront
+  constexpr int kRowsWg = (NW / FS) * NH * 16;  // rows of the workgroup
+  const int fslice = wave % FS;               // this wavefront's feature slice
+  const int row0 = rg * kRowsWg + (wave / FS) * 16 * NH;  // first row of this wavefront
   int tmax[NH];
   int tmax_min = 0x7fffffff;
 #pragma unroll
@@ -1139,7 +1206,7 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
     const int y = (qq >> 1) ^ swz(row);
 #pragma unroll
     for (int f4 = 0; f4 < 4; ++f4) {
-      vbase[f4] = row * kEntryBytes + 16 * ((2 * f4) ^ y) + 8 * (qq & 1);
+      vbase[f4] = row * kEntryBytes + 16 * ((2 * f4) ^ y) + 8 * (qq & 1) + 32 * FT * fslice;
       asm volatile("" : "+v"(vbase[f4]));
     }
   }
@@ -1151,11 +1218,11 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qreg[h][ks] = qp[4 * ks];
   }
-  f32x4 oacc[NH][32];
+  f32x4 oacc[NH][FT];
 #pragma unroll
   for (int h = 0; h < NH; ++h)
 #pragma unroll
-    for (int f = 0; f < 32; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < FT; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref[NH], l_run[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
@@ -1173,10 +1240,40 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
   const char* cache = reinterpret_cast<const char*>(a.cache);
   uint32_t doff[kPer];
   dma_offsets<NW, kPer, false>(wave, lane, doff);
+  // The item's block ids in registers, lane L of btv[k] holding page
+  // p0 + 64 k + L's: a chunk's block is then a lane read, not a scalar load
+  // (whose wait, lgkmcnt(0), would also wait for every LDS read in flight).
+  // Items of more than 256 pages read the table with scalar loads.
+  constexpr int kBtRegs = 4;
+  const int npages = p1 - p0;
+  const bool bt_regs = npages <= 64 * kBtRegs;
+  int btv[kBtRegs];
+#pragma unroll
+  for (int k = 0; k < kBtRegs; ++k) {
+    btv[k] = (bt_regs && 64 * k + lane < npages) ? bt[p0 + 64 * k + lane] : 0;
+    // (kept in registers: an indexed form of these would be moved to LDS)
+    asm volatile("" : "+v"(btv[k]));
+  }
   auto chunk_copy = [&](auto slot_c, int j) -> ChunkCopy {
     const bool real = j < nchunks;
-    const int t = tok_begin + (real ? j : 0) * kChunk;
-    const int64_t blk = bt[t / kPage];
+    const int lp = real ? (j >> 1) : 0;  // page of the item (two chunks a page)
+    int64_t blk;
+    if (bt_regs) {
+      // one lane read per register, then a scalar select
+      int b = __builtin_amdgcn_readlane(btv[0], lp & 63);
+#pragma unroll
+      for (int k = 1; k < kBtRegs; ++k) {
+        const int bk = __builtin_amdgcn_readlane(btv[k], lp & 63);
+        b = (lp >> 6) == k ? bk : b;
+      }
+      blk = b;
+    } else {
+      // (the scalar load is waited for here, on this path only)
+      int b = bt[p0 + lp];
+      asm volatile("" : "+s"(b));
+      blk = b;
+    }
+    const int t = tok_begin + lp * kPage + (real ? (j & 1) * kChunk : 0);
     const int bytes = real ? min(tok_end - t, kChunk) * kEntryBytes : 0;
     const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kEntryBytes;
     return ChunkCopy{
@@ -1187,6 +1284,8 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
 #pragma unroll
     for (int i = 0; i < kPer; ++i) copy_piece<D::kWaveBase, D::kStride>(cc, doff, i, wave);
   };
+  // read-ahead registers of the fused intervals (see fused_prefetch)
+  bf16x8 rb[kFusedAhead + 1][2];
   auto chunk_limits = [&](int j, int (&lim)[NH]) {
     const int t0 = tok_begin + j * kChunk;
 #pragma unroll
@@ -1218,25 +1317,50 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
     mfma_drain<NH>(sacc);
     softmax(sacc, 0, T{});
   }
+  if (1 < nchunks) fused_prefetch<FT>(rb, ring(Slot<0>{}), vbase);
   // interval j: P.V of chunk j (slot j % 4) with the scores of chunk j+1
   // (slot (j+1) % 4); chunk j+3 goes into slot (j+3) % 4, chunk j-1's.
   auto interval = [&](auto s_c, int j) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value;
     // chunk j+1 has landed once at most chunk j+2's copies are pending; the
-    // barrier also tells that every wavefront is done with chunk j-1
+    // barrier also tells that every wavefront is done with chunk j-1.  (No
+    // LDS-read wait before it: every read of chunk j-1 has been consumed,
+    // and the reads in flight, this interval's prefetch, are of chunk j.)
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<kPer>());
-    ring_barrier();
+    asm volatile("s_barrier" ::: "memory");
     const ChunkCopy cc = chunk_copy(Slot<S + 3>{}, j + 3);
     if (j + 1 < nchunks) {
       f32x4 sacc[NH][2];
-      fused_interval<NH, kPer, D::kWaveBase, D::kStride>(ring(Slot<S>{}), vbase, pk, oacc,
-                                                         ring(Slot<S + 1>{}), sbase_even,
-                                                         sbase_odd, qreg, sacc, cc, doff, wave);
-      mfma_drain<NH>(sacc);
-      softmax(sacc, j + 1, F{});
+      bf16x8 pk_next[NH];
+      float psum[NH];
+      int lim[NH];
+      chunk_limits(j + 1, lim);
+      fused_interval<NH, FT, kPer, D::kWaveBase, D::kStride>(
+          ring(Slot<S>{}), vbase, pk, oacc, ring(Slot<S + 1>{}), sbase_even, sbase_odd, qreg,
+          sacc, cc, doff, wave, rb, [&](auto u_c) __attribute__((always_inline)) {
+            // after the last score unit: the wait states, then one piece per
+            // P.V unit (the mask is applied to every chunk: no branch splits
+            // the interval, and only chunks at the causal limit change)
+            constexpr int k = decltype(u_c)::value - fused_mid(FT);
+            if constexpr (k == 0) mfma_drain<NH>(sacc);
+            if constexpr (k >= 1 && k <= 2 * NH)
+              softmax_piece<NH, (k - 1) / 2, (k - 1) % 2>(sacc, pk_next, m_ref, psum, lim);
+            if constexpr (k == 2 * NH + 1) {
+#pragma unroll
+              for (int h = 0; h < NH; ++h) {
+                l_run[h] += psum[h];
+                // every p <= psum: psum <= 2^16 bounds them all (NaN/inf fail too)
+                need_restart |= !(psum[h] <= kSlackPow);
+              }
+            }
+          });
+#pragma unroll
+      for (int h = 0; h < NH; ++h) pk[h] = pk_next[h];
+      // the next interval's first P.V reads (chunk j+1), before its barrier
+      if (j + 2 < nchunks) fused_prefetch<FT>(rb, ring(Slot<S + 1>{}), vbase);
     } else if (j < nchunks) {
       issue_all(cc);
-      pv_only<NH>(ring(Slot<S>{}), vbase, pk, oacc);
+      pv_only<NH, FT>(ring(Slot<S>{}), vbase, pk, oacc);
     } else {
       issue_all(cc);
     }
@@ -1281,22 +1405,22 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
       l_run[h] = 0.f;
     }
     // (the wait states before the accumulators are overwritten)
-    mfma_drain_o<NH>(oacc);
+    mfma_drain_o<NH, FT>(oacc);
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int f = 0; f < 32; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int f = 0; f < FT; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < nchunks; ++j) {
       const MLA_LDS char* buf = fetch(j);
       f32x4 sacc[NH][2];
       score_only<NH>(buf, sbase_even, sbase_odd, qreg, sacc);
       mfma_drain<NH>(sacc);
       softmax(sacc, j, F{});
-      pv_only<NH>(buf, vbase, pk, oacc);
+      pv_only<NH, FT>(buf, vbase, pk, oacc);
       __syncthreads();
     }
   }
-  mfma_drain_o<NH>(oacc);
+  mfma_drain_o<NH, FT>(oacc);
 
   // ---- finalise: each wavefront normalises its own rows --------------------
 #pragma unroll
@@ -1305,12 +1429,13 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     const float lse = l > 0.f ? m_ref[h] + __builtin_amdgcn_logf(l) : -INFINITY;
-    if (gq == 0) a.lse_part[(int64_t)item * a.rows_per_seq + row0 + 16 * h + n] = lse;
+    // (the FS wavefronts of a row group hold the same sums)
+    if (gq == 0 && fslice == 0) a.lse_part[(int64_t)item * a.rows_per_seq + row0 + 16 * h + n] = lse;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t orow = (int64_t)item * a.rows_per_seq + row0 + 16 * h + n;
-    uint16_t* op = a.o_part + orow * kLatent + 4 * gq;
+    uint16_t* op = a.o_part + orow * kLatent + 16 * FT * fslice + 4 * gq;
 #pragma unroll
-    for (int f = 0; f < 32; ++f) {
+    for (int f = 0; f < FT; ++f) {
       u16x4 v;
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(oacc[h][f][i] * inv);
@@ -1324,21 +1449,27 @@ DecodeConfig decode_config(int rows_per_seq) {
   DecodeConfig c;
   c.chunk = kChunk;
   c.nbuf = 4;
+  // rows per workgroup 128, 64, 32 or 16: the pipelined kernel with four
+  // wavefronts of their own rows (feature split 1), or pairs / quartets of
+  // wavefronts sharing rows (split 2 / 4).  `waves` and `heads_per_wave`
+  // describe the four-stage kernel with the same rows per workgroup, which
+  // serves the FP8 cache at fewer than 128 rows.
   if (groups % 8 == 0) {
-    // the pipelined kernel: four wavefronts of two row groups each, every
-    // wavefront accumulating all 512 features of its own rows
     c.waves = 4;
     c.heads_per_wave = 2;
     c.pipe = 1;
   } else if (groups % 4 == 0) {
     c.waves = 2;
     c.heads_per_wave = 2;
+    c.pipe = 2;
   } else if (groups % 2 == 0) {
     c.waves = 1;
     c.heads_per_wave = 2;
+    c.pipe = 3;
   } else {
     c.waves = 1;
     c.heads_per_wave = 1;
+    c.pipe = 4;
   }
   if (c.waves == 1) c.nbuf = 3;
   c.lds_bytes = c.nbuf * kBufBytes + c.waves * c.heads_per_wave * (1024 + 64);
@@ -1379,11 +1510,27 @@ hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_ab
   args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
-  if (cfg.pipe) {
+  if (cfg.pipe && !(fp8 && cfg.pipe != 1)) {
     // FP8 rows: the eight-wavefront kernel, same 128 rows per workgroup
     if (fp8) return launch_t<8, 1>(grid, fp8, args, block_table, stream);
-    hipLaunchKernelGGL((decode_pipe_kernel<2>), dim3(grid), dim3(256), 0, stream, args,
-                       block_table);
+    switch (cfg.pipe) {
+      case 1:
+        hipLaunchKernelGGL((decode_pipe_kernel<2, 1>), dim3(grid), dim3(256), 0, stream, args,
+                           block_table);
+        break;
+      case 2:
+        hipLaunchKernelGGL((decode_pipe_kernel<2, 2>), dim3(grid), dim3(256), 0, stream, args,
+                           block_table);
+        break;
+      case 3:
+        hipLaunchKernelGGL((decode_pipe_kernel<2, 4>), dim3(grid), dim3(256), 0, stream, args,
+                           block_table);
+        break;
+      default:
+        hipLaunchKernelGGL((decode_pipe_kernel<1, 4>), dim3(grid), dim3(256), 0, stream, args,
+                           block_table);
+        break;
+    }
     return hipGetLastError();
   }
   if (cfg.waves == 2) return launch_t<2, 2>(grid, fp8, args, block_table, stream);

@@ -363,7 +363,7 @@ int decode_any(bool fp8, const InsertArgs* ins, const mla_dims* dims, const void
   prof_mark(pc, 2, s);
   if (e == hipSuccess)
     e = launch_combine(o_part, lse_part, plan, static_cast<const uint16_t*>(kv_b), heads, q_len,
-                       batch, static_cast<uint16_t*>(out), s);
+                       batch, static_cast<uint16_t*>(out), device_cus(), s);
   prof_mark(pc, 3, s);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

@@ -94,7 +94,7 @@ struct DecodeConfig {
   int nbuf;     // LDS ring depth (chunks)
   int lds_bytes;
   int wgs_per_cu;
-  int pipe = 0;  // 1: the pipelined kernel (four wavefronts owning their rows' outputs)
+  int pipe = 0;  // pipelined kernel variant: 1..4 = 128, 64, 32, 16 rows per workgroup
 };
 DecodeConfig decode_config(int rows_per_seq);
 
@@ -130,8 +130,9 @@ hipError_t launch_gather(bool fp8, const void* cache, const int32_t* block_table
                          const int32_t* kept, int top_k, const int32_t* counts, int batch,
                          int kpages, void* dense, int32_t* dense_bt, hipStream_t stream);
 
+// cus: compute units of the device (sizes the row blocks)
 hipError_t launch_combine(const uint16_t* o_part, const float* lse_part, PlanView plan,
                           const uint16_t* kv_b, int heads, int q_len, int batch, uint16_t* out,
-                          hipStream_t stream);
+                          int cus, hipStream_t stream);
 
 }  // namespace mla

@@ -209,6 +209,22 @@ def test_decode_split_invariance():
         assert np.max(np.abs(outs[h] - outs[0])) <= 2e-2
 
 
+def test_decode_one_long_sequence_many_splits():
+    """One 32768-position sequence: the automatic plan cuts it into far more
+    than 64 items (the merge's lane-parallel weights then take several blocks
+    of 64 splits, split over the merge's wavefronts), q_len 1 and 2."""
+    torch = _torch()
+    for q_len in (1, 2):
+        say(f"[decode] one sequence of 32768, q_len {q_len}")
+        d = wl.make_inputs(1, q_len, 128, [32768], permute=True, seed=47 + q_len)
+        cache = ref_cache(d)
+        got = run_decode(d, dev(cache, torch), torch)
+        ref = decode_expanded(d["q"], d["kv_b"], cache, d["block_table"], d["seq_lens"], q_len)
+        mx, rr = errors(got, ref)
+        say(f"   max-abs {mx:.3e} rel-rms {rr:.3e}")
+        assert mx <= MAX_ABS and rr <= REL_RMS
+
+
 def test_decode_ignores_slots_beyond_length():
     """Slots at positions >= seq_len hold NaN sentinels (and random pages hold
     other sequences' data); rewriting them must not change the output."""
