@@ -55,7 +55,8 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = 3,  /* dimensions this build does not implement */
   MLA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
   MLA_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
-  MLA_ERR_BOUNDS = 6        /* debug checks: a block id or length breaks the contract */
+  MLA_ERR_BOUNDS = 6,       /* debug checks: a block id or length breaks the contract */
+  MLA_ERR_SCRATCH = 7       /* mla_decode_noalloc: the call needs more than its scratch */
 } mla_status;
 
 /* Model dimensions ([V3-src] MLA: kv_lora_rank, qk_rope_head_dim,
@@ -138,6 +139,30 @@ int mla_decode(const mla_dims* dims, const void* q, const void* kv_b, const void
                const int32_t* seq_lens, int32_t batch, int32_t q_len, int32_t max_seq_len,
                float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
                int32_t num_splits_hint, void* stream);
+
+/*
+ * mla_decode_noalloc — mla_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, allocation-free serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments as mla_decode minus the
+ * workspace, same kernels and output.  The workspace is a file-scope device
+ * array of the library (mla_noalloc_scratch_bytes() = 128 MiB), which every
+ * GPU the library runs on holds from the library's load until the process
+ * ends; its address on the current device is looked up once per device.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  Every call on one GPU uses that GPU's one array: calls that
+ * overlap on a GPU (other streams, other threads) race and must be ordered
+ * by the caller; nothing in the array needs to start at zero.  When the
+ * automatic split plan's worst case does not fit, the planner is limited to
+ * fewer work items (at least one per sequence); a call that does not fit
+ * even then (or with num_splits_hint > 0, whose item count is fixed) returns
+ * MLA_ERR_SCRATCH with nothing enqueued.
+ */
+size_t mla_noalloc_scratch_bytes(void);
+int mla_decode_noalloc(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+                       int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                       const int32_t* seq_lens, int32_t batch, int32_t q_len,
+                       int32_t max_seq_len, float softmax_scale, void* out,
+                       int32_t num_splits_hint, void* stream);
 
 /*
  * FP8 latent cache ("DeepSeek-V3.2-Exp unboxing", 初步研读: the deployed KV

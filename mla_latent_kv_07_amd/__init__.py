@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     cache_insert,
     debug_checks,
     decode,
+    decode_noalloc,
     decode_step,
     decode_workspace_bytes,
     dsa_decode,
@@ -18,6 +19,7 @@ from ._lib import (  # noqa: F401
     dsa_workspace_bytes,
     lib_path,
     load,
+    noalloc_scratch_bytes,
     prefill,
     prefill_workspace_bytes,
     profile_collect,

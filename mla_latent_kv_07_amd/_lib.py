@@ -89,6 +89,10 @@ def load() -> ctypes.CDLL:
     lib.mla_abi_version.restype = ctypes.c_int
     lib.mla_debug_checks.argtypes = [I32]
     lib.mla_debug_checks.restype = ctypes.c_int
+    lib.mla_decode_noalloc.argtypes = [DP, P, P, P, I32, P, I32, P, I32, I32, I32, F, P, I32, P]
+    lib.mla_decode_noalloc.restype = ctypes.c_int
+    lib.mla_noalloc_scratch_bytes.argtypes = []
+    lib.mla_noalloc_scratch_bytes.restype = SZ
     _lib = lib
     return lib
 
@@ -338,6 +342,40 @@ def dsa_workspace_bytes(heads: int, batch: int, max_seq_len: int, top_k: int,
     d = dims(heads)
     return int(load().mla_dsa_workspace_bytes(ctypes.byref(d), batch, max_seq_len, top_k,
                                               num_splits_hint))
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the device scratch mla_decode_noalloc works in."""
+    return int(load().mla_noalloc_scratch_bytes())
+
+
+def decode_noalloc(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, *,
+                   softmax_scale: float | None = None, out=None, num_splits_hint: int = 0,
+                   stream=None):
+    """mla_decode_noalloc: mla_decode (bf16 cache) working in the library's
+    own device scratch instead of a caller workspace; ``out`` must be given
+    by a caller that cannot allocate."""
+    import torch
+    bsz, q_len, heads = q.shape[0], q.shape[1], q.shape[2]
+    dev = cache.device
+    _check(q, "q", torch.bfloat16, (bsz, q_len, heads, NOPE + ROPE), dev)
+    _check(kv_b, "kv_b", torch.bfloat16, (heads * (NOPE + VDIM), LATENT), dev)
+    _check_cache(cache, False, dev)
+    _check(block_table, "block_table", torch.int32, None, dev)
+    _check(seq_lens, "seq_lens", torch.int32, (bsz,), dev)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(NOPE + ROPE)
+    if out is None:
+        out = torch.empty((bsz, q_len, heads, VDIM), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (bsz, q_len, heads, VDIM), dev)
+    d = dims(heads)
+    st = load().mla_decode_noalloc(ctypes.byref(d), _ptr(q), _ptr(kv_b), _ptr(cache),
+                                   cache.shape[0], _ptr(block_table), block_table.shape[1],
+                                   _ptr(seq_lens), bsz, q_len, max_seq_len, softmax_scale,
+                                   _ptr(out), num_splits_hint, _stream(stream))
+    if st != 0:
+        raise MLAError(st, "mla_decode_noalloc")
+    return out
 
 
 def dsa_decode(q, kv_b, cache, block_table, seq_lens, max_seq_len: int, index_q, index_w,

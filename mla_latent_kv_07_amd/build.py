@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["insert.hip", "qabsorb.hip", "decode.hip", "combine.hip", "prefill.hip", "dsa.hip", "mla_api.cpp"]
+SOURCES = ["insert.hip", "qabsorb.hip", "decode.hip", "combine.hip", "prefill.hip", "dsa.hip",
+           "scratch.hip", "mla_api.cpp"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 

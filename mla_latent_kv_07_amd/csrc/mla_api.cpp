@@ -114,7 +114,9 @@ struct Layout {
 };
 
 // Workspace layout for one decode call (pure function of the sizes).
-Layout make_layout(int heads, int batch, int q_len, int hint) {
+// item_cap > 0 bounds the number of work items the planner may choose (the
+// no-allocation entry point sizes it to its scratch).
+Layout make_layout(int heads, int batch, int q_len, int hint, int item_cap = 0) {
   Layout L;
   const int rows = heads * q_len;
   L.cfg = decode_config(rows);
@@ -122,6 +124,7 @@ Layout make_layout(int heads, int batch, int q_len, int hint) {
   L.slots = device_cus() * L.cfg.wgs_per_cu / row_groups;
   if (L.slots < 1) L.slots = 1;
   L.max_items = hint > 0 ? batch * hint : batch + 4 * L.slots;
+  if (item_cap > 0 && item_cap < L.max_items) L.max_items = item_cap;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -227,6 +230,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_WORKSPACE: return "workspace missing or too small";
     case MLA_ERR_HIP: return "HIP runtime error at kernel launch";
     case MLA_ERR_BOUNDS: return "block table or sequence lengths break the contract (debug checks)";
+    case MLA_ERR_SCRATCH: return "the call needs more than the no-allocation scratch (mla_noalloc_scratch_bytes)";
     default: return "unknown status";
   }
 }
@@ -301,7 +305,8 @@ int decode_any(bool fp8, const InsertArgs* ins, const mla_dims* dims, const void
                const void* kv_b, const void* cache, int32_t num_blocks,
                const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
                int32_t batch, int32_t q_len, int32_t max_seq_len, float softmax_scale, void* out,
-               void* workspace, size_t workspace_bytes, int32_t num_splits_hint, void* stream) {
+               void* workspace, size_t workspace_bytes, int32_t num_splits_hint, void* stream,
+               int item_cap = 0) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (batch < 0 || batch > kMaxBatch || q_len < 1 || q_len > kMaxQLen || max_seq_len < q_len ||
@@ -315,7 +320,7 @@ int decode_any(bool fp8, const InsertArgs* ins, const mla_dims* dims, const void
   if (!q || !kv_b || !cache || !block_table || !seq_lens || !out) return MLA_ERR_NULL;
   if (!workspace) return MLA_ERR_WORKSPACE;
   const int heads = dims->heads;
-  const Layout L = make_layout(heads, batch, q_len, num_splits_hint);
+  const Layout L = make_layout(heads, batch, q_len, num_splits_hint, item_cap);
   if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
   if (debug_checks()) {
     st = check_all_pages(block_table, bt_stride, seq_lens, batch, q_len, max_seq_len, num_blocks,
@@ -388,6 +393,42 @@ int mla_decode_fp8(const mla_dims* dims, const void* q, const void* kv_b, const 
   return decode_any(true, nullptr, dims, q, kv_b, cache, num_blocks, block_table, bt_stride,
                     seq_lens, batch, q_len, max_seq_len, softmax_scale, out, workspace,
                     workspace_bytes, num_splits_hint, stream);
+}
+
+size_t mla_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int mla_decode_noalloc(const mla_dims* dims, const void* q, const void* kv_b, const void* cache,
+                       int32_t num_blocks, const int32_t* block_table, int32_t bt_stride,
+                       const int32_t* seq_lens, int32_t batch, int32_t q_len,
+                       int32_t max_seq_len, float softmax_scale, void* out,
+                       int32_t num_splits_hint, void* stream) {
+  int st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || batch > kMaxBatch || q_len < 1 || q_len > kMaxQLen || max_seq_len < q_len ||
+      max_seq_len > kMaxSeqLen || num_splits_hint < 0 || num_splits_hint > kMaxHint)
+    return MLA_ERR_SHAPE;
+  if (batch == 0) return decode_any(false, nullptr, dims, q, kv_b, cache, num_blocks, block_table,
+                                    bt_stride, seq_lens, batch, q_len, max_seq_len, softmax_scale,
+                                    out, nullptr, 0, num_splits_hint, stream);
+  // the workspace of mla_decode, with the item list capped so that it fits
+  // the scratch: its size is linear in the item count
+  const int heads = dims->heads;
+  Layout L = make_layout(heads, batch, q_len, num_splits_hint);
+  int cap = 0;
+  if (L.total > kScratchBytes) {
+    if (num_splits_hint > 0) return MLA_ERR_SCRATCH;  // the hint fixes the item count
+    const Layout one = make_layout(heads, batch, q_len, 0, batch);
+    const Layout two = make_layout(heads, batch, q_len, 0, batch + 1);
+    if (one.total > kScratchBytes) return MLA_ERR_SCRATCH;
+    const size_t per_item = two.total > one.total ? two.total - one.total : 1;
+    cap = batch + (int)((kScratchBytes - one.total) / per_item);
+    while (cap > batch && make_layout(heads, batch, q_len, 0, cap).total > kScratchBytes) --cap;
+  }
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess || ws == nullptr) return MLA_ERR_HIP;
+  return decode_any(false, nullptr, dims, q, kv_b, cache, num_blocks, block_table, bt_stride,
+                    seq_lens, batch, q_len, max_seq_len, softmax_scale, out, ws, kScratchBytes,
+                    num_splits_hint, stream, cap);
 }
 
 namespace {

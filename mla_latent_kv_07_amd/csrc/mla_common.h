@@ -130,6 +130,11 @@ hipError_t launch_gather(bool fp8, const void* cache, const int32_t* block_table
                          const int32_t* kept, int top_k, const int32_t* counts, int batch,
                          int kpages, void* dense, int32_t* dense_bt, hipStream_t stream);
 
+// The no-allocation entry point's device scratch (scratch.hip): its size and
+// the address of the current device's copy.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+hipError_t scratch_address(void** out);
+
 // cus: compute units of the device (sizes the row blocks)
 hipError_t launch_combine(const uint16_t* o_part, const float* lse_part, PlanView plan,
                           const uint16_t* kv_b, int heads, int q_len, int batch, uint16_t* out,

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert lib.mla_status_string(s) and lib.mla_status_string(s) != b"unknown status"
     assert lib.mla_status_string(99) == b"unknown status"
 
