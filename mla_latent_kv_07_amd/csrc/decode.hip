@@ -1404,8 +1404,13 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
       m_ref[h] = m_exact[h];
       l_run[h] = 0.f;
     }
-    // (the wait states before the accumulators are overwritten)
-    mfma_drain_o<NH, FT>(oacc);
+    // Zeroed with no statement that reads the old tiles, so they are dead on
+    // this path (passing them through mfma_drain_o first kept them alive
+    // across the exact-max pass, and the compiler spilled them on every
+    // item).  The wait states the drain provided are not needed here: the
+    // last matrix instruction that wrote them is a whole pass (and its
+    // barriers) behind, and the first that reads them a fetch and a softmax
+    // ahead.
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll

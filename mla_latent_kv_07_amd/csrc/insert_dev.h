@@ -12,6 +12,8 @@
 // rotation run in double and round once to bf16.
 #pragma once
 
+#include <cmath>
+
 #include "mla_common.h"
 
 namespace mla {
@@ -26,18 +28,27 @@ struct InsertArgs {
   const int32_t* seq_lens;    // after the insert
   int q_len;
   void* cache;                // bf16 [.., 64, 576] or FP8 rows [.., 64, 656]
+  double freq[kRope / 2];     // base^(-2j/64), set on the host by with_rope_freq
 };
+
+// The arguments with the rotary frequencies filled in, computed once on the
+// host in double (the same expression the angle needs, so the kernels spend no
+// pow per lane).
+inline InsertArgs with_rope_freq(InsertArgs a) {
+  for (int j = 0; j < kRope / 2; ++j) a.freq[j] = std::pow(a.rope_base, -2.0 * j / (double)kRope);
+  return a;
+}
 
 // RoPE of one interleaved pair (re, im) = elements (2j, 2j+1) of a 64-wide
 // rotary part at position pos ("深度解读DeepSeek：源码解读 DeepSeek-V3",
 // section MLA, apply_rotary_emb with the complex freqs_cis of the Transformer
 // constructor): angle pos * base^(-2j/64), rotation in double, each result
 // rounded once to bf16.  Returns the rotated pair packed as (re | im << 16).
-// (rope_angle: the cosine and sine of pair j's angle; rotate_pair: the
-// rotation of one packed pair by them.)
-__device__ __forceinline__ void rope_angle(int pos, int j, double base, double& c, double& s) {
+// (rope_angle: the cosine and sine of pair j's angle, freq = base^(-2j/64)
+// from InsertArgs::freq; rotate_pair: the rotation of one packed pair by
+// them.)
+__device__ __forceinline__ void rope_angle(int pos, double freq, double& c, double& s) {
 #pragma clang fp contract(off)
-  const double freq = pow(base, -2.0 * (double)j / (double)kRope);
   const double ang = (double)pos * freq;
   sincos(ang, &s, &c);
 }
@@ -51,11 +62,6 @@ __device__ __forceinline__ uint32_t rotate_pair(uint32_t pair, double c, double 
   return (uint32_t)o_re | ((uint32_t)o_im << 16);
 }
 
-__device__ __forceinline__ uint32_t rope_pair(uint32_t pair, int pos, int j, double base) {
-  double c, s;
-  rope_angle(pos, j, base, c, s);
-  return rotate_pair(pair, c, s);
-}
 
 // The RMSNorm of the token's latent, 8 consecutive values per lane, as the
 // bf16 cache values (widened to float, exactly).
@@ -81,12 +87,18 @@ __device__ __forceinline__ void rmsnorm_lane(const InsertArgs& a, const uint16_t
   }
 }
 
-// Insert token `token` (= b * q_len + i) into the bf16 cache; the calling
-// wavefront's 64 lanes do it together.
-__device__ __forceinline__ void insert_token_bf16(const InsertArgs& a, int token, int lane) {
+// Position of token `token` (= b * q_len + i) in its sequence.
+__device__ __forceinline__ int token_pos(const InsertArgs& a, int token) {
   const int b = token / a.q_len;
-  const int i = token - b * a.q_len;
-  const int pos = a.seq_lens[b] - a.q_len + i;
+  return a.seq_lens[b] - a.q_len + (token - b * a.q_len);
+}
+
+// Insert token `token` (= b * q_len + i, at position pos) into the bf16
+// cache; the calling wavefront's 64 lanes do it together.  (c, s): the
+// rotation of pair lane % 32 at pos (rope_angle).
+__device__ __forceinline__ void insert_token_bf16(const InsertArgs& a, int token, int lane,
+                                                  int pos, double c, double s) {
+  const int b = token / a.q_len;
   const int64_t blk = a.block_table[(int64_t)b * a.bt_stride + pos / kPage];
   uint16_t* dst = static_cast<uint16_t*>(a.cache) + (blk * kPage + pos % kPage) * (int64_t)kEntry;
   const uint16_t* src = a.kv_a + (int64_t)token * kEntry;
@@ -99,8 +111,7 @@ __device__ __forceinline__ void insert_token_bf16(const InsertArgs& a, int token
   // k_pe: lane j < 32 rotates pair (2j, 2j+1)
   if (lane < kRope / 2) {
     const uint32_t pair = *reinterpret_cast<const uint32_t*>(src + kLatent + 2 * lane);
-    *reinterpret_cast<uint32_t*>(dst + kLatent + 2 * lane) =
-        rope_pair(pair, pos, lane, a.rope_base);
+    *reinterpret_cast<uint32_t*>(dst + kLatent + 2 * lane) = rotate_pair(pair, c, s);
   }
 }
 
@@ -112,10 +123,9 @@ __device__ __forceinline__ void insert_token_bf16(const InsertArgs& a, int token
 // value), e in [-126, 127], e = 0 for an all-zero row; codes round to nearest
 // even (the gfx950 conversion, which only overflows above 464, a value the
 // scale rules out).  Row: codes, rope (bf16), scale byte e + 127, zeros.
-__device__ __forceinline__ void insert_token_fp8(const InsertArgs& a, int token, int lane) {
+__device__ __forceinline__ void insert_token_fp8(const InsertArgs& a, int token, int lane,
+                                                 int pos, double c, double s) {
   const int b = token / a.q_len;
-  const int i = token - b * a.q_len;
-  const int pos = a.seq_lens[b] - a.q_len + i;
   const int64_t blk = a.block_table[(int64_t)b * a.bt_stride + pos / kPage];
   uint8_t* dst =
       static_cast<uint8_t*>(a.cache) + (blk * kPage + pos % kPage) * (int64_t)kFp8EntryBytes;
@@ -146,8 +156,7 @@ __device__ __forceinline__ void insert_token_fp8(const InsertArgs& a, int token,
   // k_pe: lane j < 32 rotates pair (2j, 2j+1)
   if (lane < kRope / 2) {
     const uint32_t pair = *reinterpret_cast<const uint32_t*>(src + kLatent + 2 * lane);
-    *reinterpret_cast<uint32_t*>(dst + kFp8RopeOff + 4 * lane) =
-        rope_pair(pair, pos, lane, a.rope_base);
+    *reinterpret_cast<uint32_t*>(dst + kFp8RopeOff + 4 * lane) = rotate_pair(pair, c, s);
   }
   // scale byte and zero padding: the row's last 16 bytes
   if (lane == 0)

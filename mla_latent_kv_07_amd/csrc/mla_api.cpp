@@ -441,9 +441,9 @@ int step_any(bool fp8, const mla_dims* dims, const void* q, const void* kv_a, co
   if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(rope_base) || rope_base <= 0.f)
     return MLA_ERR_SHAPE;
   if (batch > 0 && (!kv_a || !rms_w)) return MLA_ERR_NULL;
-  const InsertArgs ins{static_cast<const uint16_t*>(kv_a), static_cast<const uint16_t*>(rms_w),
-                       (double)eps, (double)rope_base, block_table, bt_stride, seq_lens, q_len,
-                       cache};
+  const InsertArgs ins = with_rope_freq(
+      InsertArgs{static_cast<const uint16_t*>(kv_a), static_cast<const uint16_t*>(rms_w),
+                 (double)eps, (double)rope_base, block_table, bt_stride, seq_lens, q_len, cache});
   return decode_any(fp8, &ins, dims, q, kv_b, cache, num_blocks, block_table, bt_stride,
                     seq_lens, batch, q_len, max_seq_len, softmax_scale, out, workspace,
                     workspace_bytes, num_splits_hint, stream);

@@ -40,7 +40,7 @@ static_assert(kPlanThreads == 256, "the plan runs on one 256-thread workgroup");
 // Then 4H blocks: absorption of head k/4, latent columns (k%4)*128 .. +128.
 // q_abs's rope part of heads h0 .. h0 + 2 kQpeBatch - 1 (those below `heads`)
 // of query row `token`: q_pe rotated at the token's position (each head's 32
-// pairs by the 32 angles of that position, as rope_pair), times q_scale,
+// pairs rotated by the 32 angles of that position, see rope_angle), times q_scale,
 // rounded to bf16.  Lane L handles pair L % 32 of heads h0 + L / 32 + 2u.
 // The pairs are loaded first (load_query_pe), so their latency is paid once.
 constexpr int kQpeBatch = 16;
@@ -61,14 +61,9 @@ __device__ __forceinline__ void load_query_pe(const uint16_t* __restrict__ q, in
 }
 
 __device__ __forceinline__ void rotate_query_pe(const QueryPe& qp, int heads, float q_scale,
-                                                uint16_t* __restrict__ q_abs,
-                                                const InsertArgs& ia, int token, int lane,
-                                                int h0) {
-  const int b = token / ia.q_len;
-  const int pos = ia.seq_lens[b] - ia.q_len + (token - b * ia.q_len);
+                                                uint16_t* __restrict__ q_abs, int token, int lane,
+                                                int h0, double c, double s) {
   const int j = lane & 31;
-  double c, s;
-  rope_angle(pos, j, ia.rope_base, c, s);
 #pragma unroll
   for (int u = 0; u < kQpeBatch; ++u) {
     const int h = h0 + (lane >> 5) + 2 * u;
@@ -102,13 +97,18 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
     const int h0 = wave * 2 * kQpeBatch;
     QueryPe qp;
     if (h0 < heads) load_query_pe(q, heads, token, lane, h0, qp);
+    // the token's 32 angles, once: the same rotation serves its k_pe (the
+    // insert) and its q_pe
+    const int pos = token_pos(ia, token);
+    double c, s;
+    rope_angle(pos, ia.freq[lane & 31], c, s);
     if (wave == 0) {
       if (MODE == 1)
-        insert_token_bf16(ia, token, lane);
+        insert_token_bf16(ia, token, lane, pos, c, s);
       else
-        insert_token_fp8(ia, token, lane);
+        insert_token_fp8(ia, token, lane, pos, c, s);
     }
-    if (h0 < heads) rotate_query_pe(qp, heads, q_scale, q_abs, ia, token, lane, h0);
+    if (h0 < heads) rotate_query_pe(qp, heads, q_scale, q_abs, token, lane, h0, c, s);
     return;
   }
   MLA_LDS char* w_lds = (MLA_LDS char*)smem;
