@@ -917,6 +917,18 @@ __device__ __forceinline__ void mfma_drain_o(f32x4 (&oacc)[NH][FT]) {
                      "+a"(oacc[h][f + 6]), "+a"(oacc[h][f + 7]));
 }
 
+// The probabilities pk as the B operand of the P.V MFMAs that follow in the
+// same block (the restart pass): two wait states after the vector
+// instructions that produced them, which the compiler may otherwise place
+// right before the first MFMA.
+template <int NH>
+__device__ __forceinline__ void pin_pk(bf16x8 (&pk)[NH]) {
+  if constexpr (NH == 2)
+    asm volatile("s_nop 1" : "+v"(pk[0]), "+v"(pk[1]));
+  else
+    asm volatile("s_nop 1" : "+v"(pk[0]));
+}
+
 // Score k-step ks of the chunk at (be, bo) (see score_chunk) for NH row
 // groups, the two 16-position tiles' K pieces already in kb.
 template <int NH>
@@ -1421,6 +1433,7 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
       score_only<NH>(buf, sbase_even, sbase_odd, qreg, sacc);
       mfma_drain<NH>(sacc);
       softmax(sacc, j, F{});
+      pin_pk<NH>(pk);
       pv_only<NH, FT>(buf, vbase, pk, oacc);
       __syncthreads();
     }
@@ -1449,6 +1462,881 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined decode over the FP8 cache: the kernel above with each chunk kept
+// in LDS as its FP8 rows (656 bytes: 512 E4M3 codes, the 64 bf16 RoPE values,
+// the scale byte and zero padding).  The ring slot of a chunk is 21 KB
+// instead of 36.
+//
+// Scores on the FP8 matrix cores.  The latent part of S^T = K Q^T takes the
+// codes as they are, as the A operand of the block-scaled MFMA 16x16x128
+// (E4M3 x E4M3, fp32 accumulation; two 16-byte LDS reads give a lane its 32
+// codes).  The absorbed query (bf16) is carried as two E4M3 terms per value:
+// with S = the row's power-of-two scale (largest with max |q| S <= 448),
+// hi = q S rounded to E4M3 and lo = (q S - hi) 16 rounded to E4M3.  A bf16
+// value has eight significant bits, hi keeps the top four and the remainder
+// needs at most four, so hi + lo / 16 is q S exactly (unless lo falls below
+// the E4M3 normal range: parts below 2^-6 of the row's largest value).  Each
+// k-step runs the hi MFMA with unit scales and the lo MFMA with a B scale of
+// 2^-4 into the same accumulator, so the latent scores cost two FP8 MFMAs per
+// 128 dimensions (the matrix time of four bf16 16x16x32 k-steps).  After the
+// last latent k-step each score is multiplied by its token's scale times
+// 1 / S, and the two bf16 RoPE k-steps add the RoPE part.
+// P.V keeps the bf16 MFMA: its operand V^T comes from the codes through the
+// transposing byte read (ds_read_b64_tr_b8, one per 16 features x 32
+// positions) and four conversions to bf16, and the weights are p times the
+// token's scale (bf16(p 2^e) = bf16(p) 2^e), so the codes need no scale.
+//
+// Position order.  Score tile t, row 4g + i (g = 0..3, i = 0..3) is chunk
+// position 8g + 4t + i.  A lane's four scores of tile t are then positions
+// 8gq + 4t + i, its eight scores of the chunk positions 8gq .. 8gq+7: exactly
+// the eight positions its P.V operand holds (P.V index k = chunk position).
+// The transposing read supplies them from eight rows: lane L addresses row
+// L >> 1, half L & 1 of a 16-byte feature group, and receives feature L & 15
+// of rows 8 (L >> 4) .. 8 (L >> 4) + 7.
+// Latent dimensions.  In k-step k (0..3) lane (n, gq = 2 g1 + g0) holds the
+// codes of the 16-byte units 8k + 4 g0 + g1 and 8k + 4 g0 + g1 + 2 of its row
+// (32 dimensions), the query terms of the same dimensions in the same byte
+// order (the contraction is a sum over dimensions: any order both operands
+// share gives the same products).  RoPE k-step 16 + r reads unit 32 + 4 g0 +
+// 2 r + g1 (bf16).  Rows are 656 bytes apart, i.e. 144 bytes (nine 16-byte
+// units) apart modulo the 256-byte bank window; with this order every read
+// pattern of the kernel is free of bank conflicts (each lane's banks
+// enumerated).
+// Scales.  The chunk's 32 scale bytes come with the chunk: one 4-byte-per-
+// lane copy puts their dwords in a 128-byte array after the rows.
+// Hazards.  The P.V operands are converted by vector instructions and feed
+// asm MFMAs, which the compiler does not see as matrix instructions: each is
+// produced one unit before its MFMAs and pinned there (an ordered empty asm
+// statement), so the previous unit's MFMAs stand between them (two wait
+// states are required; with one row group per wavefront the pin adds an
+// s_nop).  Vector instructions read FP8 MFMA results only after 16 wait
+// states (mfma_drain_f8).
+
+constexpr int kF8ChunkBytes = kChunk * kFp8EntryBytes;  // 20992
+constexpr int kF8Whole = 20;                            // whole 1 KB copies of a chunk
+constexpr int kF8Tail = kF8Whole * 1024;                // 20480: the last 512 bytes after it
+constexpr int kF8ScaleLds = kF8ChunkBytes;              // 32 scale dwords after the rows
+constexpr int kF8SlotBytes = kF8ScaleLds + 512;         // 21504
+constexpr int kF8Per = 6;                               // copy instructions per wavefront
+constexpr int kF8Ahead = 5;                             // LDS reads issued five units ahead
+constexpr int kE8m0One = 127;                           // MFMA block scale 2^0
+constexpr int kE8m0Lo = 127 - 4;                        // 2^-4: the lo query term
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x2_gnu_t __attribute__((vector_size(8)));
+
+// ds_read_b64_tr_b8 at p (see the position order for the lane layout).
+__device__ __forceinline__ u32x2_t ds_read_tr8(const MLA_LDS char* p) {
+  const i32x2_gnu_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2_gnu_t*)p);
+  return u32x2_t{(uint32_t)r[0], (uint32_t)r[1]};
+}
+
+// Source offsets of a wavefront's copies of one chunk (four wavefronts).
+// Copies 0..4: 1 KB each, copy i of wavefront w fills chunk bytes
+// 1024 (4i + w) ..; copy 5 moves 4 bytes per lane: the chunk's last 512 bytes
+// (wavefronts 0 and 1), the scale dwords of the 32 rows (wavefront 2, lanes
+// 0..31), nothing (wavefront 3).  Its LDS destination is kF8Tail + 256 w: the
+// tail lands in place and the scales at kF8ScaleLds.
+__device__ __forceinline__ void dma_offsets_f8(int wave, int lane, uint32_t (&off)[kF8Per]) {
+#pragma unroll
+  for (int i = 0; i < kF8Per - 1; ++i) off[i] = (uint32_t)(1024 * (4 * i + wave) + 16 * lane);
+  uint32_t o5 = 0x80000000u;  // beyond any range: no memory access, zeros to LDS
+  if (wave < 2) o5 = (uint32_t)(kF8Tail + 256 * wave + 4 * lane);
+  if (wave == 2 && lane < kChunk) o5 = (uint32_t)(lane * kFp8EntryBytes + kFp8ScaleOff);
+  off[kF8Per - 1] = o5;
+}
+
+// Copy instruction I (0..5) of the wavefront's share of an FP8 chunk.
+template <int I>
+__device__ __forceinline__ void copy_piece_f8(const ChunkCopy& c, const uint32_t* off, int wave) {
+  if constexpr (I < kF8Per - 1)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, c.dst + wave * 1024 + I * 4096, 16, off[I], 0,
+                                             0, kCopyPolicy);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, c.dst + kF8Tail + 256 * wave, 4, off[I], 0, 0,
+                                             kCopyPolicy);
+}
+
+// Eight E4M3 codes (two dwords, code k in byte k) as eight bf16 values.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t d0, uint32_t d1) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// A token's scale 2^(s - 127) from its scale dword (s in the low byte).
+__device__ __forceinline__ float f8_scale(uint32_t dw) { return __uint_as_float((dw & 0xffu) << 23); }
+
+// The block-scaled FP8 MFMA (both operands E4M3; sa, sb: E8M0 scales, the same
+// in every lane).  _0: with a zero accumulator.
+__device__ __forceinline__ void mfma_f8_0(f32x4& acc, const u32x8_t& a, const u32x8_t& b, int sa,
+                                          int sb) {
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
+               : "=&v"(acc)
+               : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+__device__ __forceinline__ void mfma_f8(f32x4& acc, const u32x8_t& a, const u32x8_t& b, int sa,
+                                        int sb) {
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+v"(acc)
+               : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+// 16 wait states after the last FP8 score MFMA, ordered before every read of
+// the scores.
+template <int NH>
+__device__ __forceinline__ void mfma_drain_f8(f32x4 (&sacc)[NH][2]) {
+  static_assert(NH == 1 || NH == 2, "two or four score tiles");
+  if constexpr (NH == 2)
+    asm volatile("s_nop 7\n\ts_nop 7"
+                 : "+v"(sacc[0][0]), "+v"(sacc[0][1]), "+v"(sacc[1][0]), "+v"(sacc[1][1]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sacc[0][0]), "+v"(sacc[0][1]));
+}
+
+// Per-lane LDS offsets inside a slot (see the position order above).
+struct F8Lane {
+  int k;  // score reads: row 8 (n >> 2) + (n & 3), unit 4 g0 + g1
+  int v;  // transposing reads: row lane >> 1, half lane & 1, the wavefront's feature slice
+  int s;  // scale reads: dwords 8 gq .. 8 gq + 7
+};
+
+// Offset (relative to F8Lane::k) of the first of latent k-step k's two reads
+// of tile t (the second is 32 bytes further), and of RoPE k-step 16 + r.
+constexpr int f8_kread(int k, int t) { return 4 * kFp8EntryBytes * t + 128 * k; }
+constexpr int f8_rread(int r, int t) { return 4 * kFp8EntryBytes * t + kFp8RopeOff + 32 * r; }
+
+// The query of a wavefront's NH row groups in the operand forms above.
+template <int NH>
+struct F8Query {
+  u32x8_t hi[NH][4];   // latent k-steps: q S as E4M3
+  u32x8_t lo[NH][4];   // (q S - hi) 16 as E4M3
+  bf16x8 rope[NH][2];  // RoPE k-steps (bf16, as given)
+  float inv_s[NH];     // 1 / S of the lane's row
+};
+
+// Split one row group's absorbed query (q: the lane's bf16 row of 576) into
+// the operand forms: the lane's 128 latent values (units 8k + 4 g0 + g1 and
+// + 2 for k = 0..3), the row scale S from the four lanes of the row.  Two
+// passes over the values (the second reads them again from cache) keep the
+// prologue's registers to those of the result.
+template <int NH>
+__device__ __forceinline__ void f8_split_query(const uint16_t* q, int g0, int g1, int h,
+                                               F8Query<NH>& fq) {
+  auto load = [&](int k, int j) -> u16x8 {  // 8 values: unit 8k + 4 g0 + g1 + 2 (j >> 1), half j & 1
+    return *reinterpret_cast<const u16x8*>(q + 16 * (8 * k + 4 * g0 + g1 + 2 * (j >> 1)) +
+                                           8 * (j & 1));
+  };
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u16x8 v = load(k, j);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)v[e] << 16)));
+    }
+  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  // S: the power of two at or below 448 / amax, kept within [2^-64, 2^64]
+  // (an all-zero row gives 2^64 and zero codes)
+  const float t = fminf(fmaxf(448.f / amax, 0x1p-64f), 0x1p64f);
+  const float s = __uint_as_float(__float_as_uint(t) & 0xff800000u);
+  fq.inv_s[h] = 1.f / s;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u16x8 v = load(k, j);
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {  // dword 2j + w of the operand: values 4w .. 4w+3 of v
+        uint32_t hw = 0, lw = 0;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const float a = __uint_as_float((uint32_t)v[4 * w + 2 * p] << 16) * s;
+          const float b = __uint_as_float((uint32_t)v[4 * w + 2 * p + 1] << 16) * s;
+          const int hc = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+          const f32x2_t hv = __builtin_amdgcn_cvt_pk_f32_fp8(hc, false);
+          const int lc =
+              __builtin_amdgcn_cvt_pk_fp8_f32((a - hv[0]) * 16.f, (b - hv[1]) * 16.f, 0, false);
+          hw |= ((uint32_t)hc & 0xffffu) << (16 * p);
+          lw |= ((uint32_t)lc & 0xffffu) << (16 * p);
+        }
+        fq.hi[h][k][2 * j + w] = hw;
+        fq.lo[h][k][2 * j + w] = lw;
+      }
+    }
+  // (each term computed before this point; the kernel adds the wait states
+  // before the first MFMA reads them)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(fq.hi[h][k]), "+v"(fq.lo[h][k]));
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    fq.rope[h][r] = *reinterpret_cast<const bf16x8*>(q + kLatent + 32 * g0 + 16 * r + 8 * g1);
+}
+
+// Unit map of one FP8 interval: LU latent score units (per k-step: one per
+// tile with two row groups, both tiles in one with one, so that the hi and lo
+// MFMAs of an accumulator are never adjacent), two RoPE units, FT P.V feature
+// tiles; the score units spread over the interval as in FusedMap.
+template <int NH>
+constexpr int f8_lat_units() { return NH == 2 ? 8 : 4; }
+template <int NH>
+constexpr int f8_score_units() { return f8_lat_units<NH>() + 2; }
+constexpr int f8_pre(int ft) { return ft - 6 < kF8Ahead ? ft - 6 : kF8Ahead; }
+template <int NH, int FT>
+constexpr int f8_span() { return f8_score_units<NH>() + FT - f8_pre(FT) - 6; }
+template <int NH, int FT>
+constexpr int f8_mid() {
+  return f8_pre(FT) + (f8_score_units<NH>() - 1) * f8_span<NH, FT>() / f8_score_units<NH>();
+}
+template <int NH, int FT>
+struct F8Map {
+  static constexpr int kScore = f8_score_units<NH>();
+  static constexpr int kUnits = kScore + FT;
+  static_assert(f8_mid<NH, FT>() + 6 <= kUnits, "softmax pieces fit after the last k-step");
+  static_assert(kUnits >= 2 * kF8Per, "the copies fit in the interval");
+  int kind[kUnits];  // 0: latent score unit, 1: P.V feature tile, 2: RoPE k-step
+  int idx[kUnits];   // latent unit, tile or RoPE k-step
+  int copy[kUnits];  // copy instructions issued at this unit
+  constexpr F8Map() : kind(), idx(), copy() {
+    int s = 0, p = 0;
+    for (int u = 0; u < kUnits; ++u) {
+      if (s < kScore && u == f8_pre(FT) + s * f8_span<NH, FT>() / kScore) {
+        kind[u] = s < f8_lat_units<NH>() ? 0 : 2;
+        idx[u] = s < f8_lat_units<NH>() ? s : s - f8_lat_units<NH>();
+        ++s;
+      } else {
+        kind[u] = 1;
+        idx[u] = p++;
+      }
+      copy[u] = 0;
+    }
+    for (int c = 0; c < kF8Per; ++c) copy[1 + 2 * c] += 1;
+  }
+};
+
+// LDS data of one interval's units (indexed by compile-time unit indices
+// only, so every element is a register of its own, live from its read to its
+// use): latent codes per k-step and tile, RoPE operands, V^T codes, the
+// chunk's scale dwords.
+template <int FT>
+struct F8Raw {
+  u32x8_t k[4][2];
+  bf16x8 r[2][2];
+  u32x2_t v[FT];
+  u32x4_t s[2];
+};
+
+// The latent k-steps and tiles of latent unit i (one tile with two row groups,
+// both tiles with one).
+template <int NH>
+constexpr int f8_lat_k(int i) { return NH == 2 ? i >> 1 : i; }
+template <int NH>
+constexpr int f8_lat_t0(int i) { return NH == 2 ? (i & 1) : 0; }
+template <int NH>
+constexpr int f8_lat_nt() { return NH == 2 ? 1 : 2; }
+
+template <int NH>
+__device__ __forceinline__ void f8_read_lat(u32x8_t& dst, const MLA_LDS char* p) {
+  const u32x4_t a = *reinterpret_cast<const MLA_LDS u32x4_t*>(p);
+  const u32x4_t b = *reinterpret_cast<const MLA_LDS u32x4_t*>(p + 32);
+  dst = u32x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+template <int NH, int FT, int V>
+__device__ __forceinline__ void f8_reads(F8Raw<FT>& x, const MLA_LDS char* sc,
+                                         const MLA_LDS char* pv, const F8Lane& ln) {
+  constexpr F8Map<NH, FT> m;
+  constexpr int i = m.idx[V];
+  if constexpr (m.kind[V] == 0) {
+    constexpr int k = f8_lat_k<NH>(i);
+#pragma unroll
+    for (int t = f8_lat_t0<NH>(i); t < f8_lat_t0<NH>(i) + f8_lat_nt<NH>(); ++t)
+      f8_read_lat<NH>(x.k[k][t], sc + ln.k + f8_kread(k, t));
+    if constexpr (i == f8_lat_units<NH>() - 1) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        x.s[t] = *reinterpret_cast<const MLA_LDS u32x4_t*>(sc + kF8ScaleLds + ln.s + 16 * t);
+    }
+  } else if constexpr (m.kind[V] == 2) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      x.r[i][t] = *reinterpret_cast<const MLA_LDS bf16x8*>(sc + ln.k + f8_rread(i, t));
+  } else {
+    x.v[i] = ds_read_tr8(pv + ln.v + 16 * i);
+  }
+}
+
+// Two wait states with the operands of the MFMAs that follow in registers
+// (inputs of this statement).  Where the output tiles leave accumulation
+// registers free, the register allocator may keep an operand there and copy
+// it back right before its asm MFMA; the copy, a vector instruction, then
+// lands before these wait states.
+// (plain overloads: the host pass rejects templates around these asm operands)
+__device__ __forceinline__ void mfma_guard(const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1" ::"v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_guard(const bf16x8& a, const bf16x8& b, const bf16x8& c) {
+  asm volatile("s_nop 1" ::"v"(a), "v"(b), "v"(c));
+}
+__device__ __forceinline__ void mfma_guard(const bf16x8& a, const bf16x8& b, const bf16x8& c,
+                                           const bf16x8& d) {
+  asm volatile("s_nop 1" ::"v"(a), "v"(b), "v"(c), "v"(d));
+}
+__device__ __forceinline__ void mfma_guard(const u32x8_t& a, const u32x8_t& b, const u32x8_t& c,
+                                           const u32x8_t& d) {
+  asm volatile("s_nop 1" ::"v"(a), "v"(b), "v"(c), "v"(d));
+}
+__device__ __forceinline__ void mfma_guard(const u32x8_t& a, const u32x8_t& b, const u32x8_t& c,
+                                           const u32x8_t& d, const u32x8_t& e, const u32x8_t& f) {
+  asm volatile("s_nop 1" ::"v"(a), "v"(b), "v"(c), "v"(d), "v"(e), "v"(f));
+}
+
+// The latent MFMAs of k-step k, tiles T0 .. T0 + NT - 1: every hi product
+// before any lo product, so two MFMAs on one accumulator are never adjacent.
+template <int NH, int K, int T0, int NT, bool GUARD>
+__device__ __forceinline__ void f8_lat_mfma(f32x4 (&sacc)[NH][2], const u32x8_t (&a)[2],
+                                            const F8Query<NH>& fq, int e_one, int e_lo) {
+  if constexpr (GUARD) {
+    if constexpr (NH == 2)
+      mfma_guard(a[T0], a[T0 + NT - 1], fq.hi[0][K], fq.hi[1][K], fq.lo[0][K], fq.lo[1][K]);
+    else
+      mfma_guard(a[T0], a[T0 + NT - 1], fq.hi[0][K], fq.lo[0][K]);
+  }
+#pragma unroll
+  for (int t = T0; t < T0 + NT; ++t)
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      if constexpr (K == 0)
+        mfma_f8_0(sacc[h][t], a[t], fq.hi[h][K], e_one, e_one);
+      else
+        mfma_f8(sacc[h][t], a[t], fq.hi[h][K], e_one, e_one);
+    }
+#pragma unroll
+  for (int t = T0; t < T0 + NT; ++t)
+#pragma unroll
+    for (int h = 0; h < NH; ++h) mfma_f8(sacc[h][t], a[t], fq.lo[h][K], e_one, e_lo);
+}
+
+// The latent scores times token scale / S (before the RoPE k-steps add their
+// part): the wait states after the FP8 MFMAs, the products, two wait states
+// before the next MFMA reads them.  scl receives the chunk's token scales.
+template <int NH>
+__device__ __forceinline__ void f8_scale_scores(f32x4 (&sacc)[NH][2], const u32x4_t (&s)[2],
+                                                const float (&inv_s)[NH], float (&scl)[8]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) scl[4 * t + i] = f8_scale(s[t][i]);
+  mfma_drain_f8<NH>(sacc);
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc[h][t][i] *= scl[4 * t + i] * inv_s[h];
+  if constexpr (NH == 2)
+    asm volatile("s_nop 1"
+                 : "+v"(sacc[0][0]), "+v"(sacc[0][1]), "+v"(sacc[1][0]), "+v"(sacc[1][1]));
+  else
+    asm volatile("s_nop 1" : "+v"(sacc[0][0]), "+v"(sacc[0][1]));
+}
+
+// The V^T reads of the first f8_pre(FT) units (P.V tiles of the chunk at
+// pv), issued ahead of the interval.
+template <int FT>
+__device__ __forceinline__ void f8_prefetch(u32x2_t (&vpre)[f8_pre(FT)], const MLA_LDS char* pv,
+                                            const F8Lane& ln) {
+#pragma unroll
+  for (int f = 0; f < f8_pre(FT); ++f) vpre[f] = ds_read_tr8(pv + ln.v + 16 * f);
+}
+
+// P.V of chunk j (slot pv, weights pk) fused with the scores of chunk j+1
+// (slot sc, into sacc; its scales into scl), the copies of cc along the way:
+// per unit its copies, the reads of the unit kF8Ahead later, the conversion
+// of the next unit's V^T operand, then its MFMAs; after the last score unit,
+// mid(unit) between the units.
+template <int NH, int FT, bool GUARD, class Mid>
+__device__ __forceinline__ void fused_interval_f8(const MLA_LDS char* pv, const bf16x8 (&pk)[NH],
+                                                  f32x4 (&oacc)[NH][FT], const MLA_LDS char* sc,
+                                                  const F8Lane& ln, const F8Query<NH>& fq,
+                                                  int e_one, int e_lo, f32x4 (&sacc)[NH][2],
+                                                  float (&scl)[8], const ChunkCopy& cc,
+                                                  const uint32_t* off, int wave,
+                                                  const u32x2_t (&vpre)[f8_pre(FT)], Mid&& mid) {
+  using M = F8Map<NH, FT>;
+  constexpr M m;
+  constexpr int U = M::kUnits;
+  static_assert(f8_pre(FT) <= kF8Ahead, "the prefetched units precede the read-ahead window");
+  F8Raw<FT> x;
+#pragma unroll
+  for (int f = 0; f < f8_pre(FT); ++f) x.v[f] = vpre[f];
+  static_for<f8_pre(FT), kF8Ahead>([&](auto v_c) __attribute__((always_inline)) {
+    f8_reads<NH, FT, decltype(v_c)::value>(x, sc, pv, ln);
+  });
+  bf16x8 cv[U];
+  cv[0] = fp8x8_to_bf16(x.v[0][0], x.v[0][1]);
+  asm volatile("s_nop 1" : "+v"(cv[0]));
+  static_for<0, U>([&](auto u_c) __attribute__((always_inline)) {
+    constexpr int u = decltype(u_c)::value;
+    constexpr int i = m.idx[u];
+    constexpr int c0 = [] {
+      constexpr M mm;
+      int c = 0;
+      for (int k = 0; k < u; ++k) c += mm.copy[k];
+      return c;
+    }();
+    static_for<0, m.copy[u]>([&](auto c_c) __attribute__((always_inline)) {
+      copy_piece_f8<c0 + decltype(c_c)::value>(cc, off, wave);
+    });
+    if constexpr (u + kF8Ahead < U) f8_reads<NH, FT, u + kF8Ahead>(x, sc, pv, ln);
+    if constexpr (u + 1 < U && m.kind[u + 1] == 1) {
+      constexpr int f = m.idx[u + 1];
+      cv[u + 1] = fp8x8_to_bf16(x.v[f][0], x.v[f][1]);
+      if constexpr (NH == 1) asm volatile("s_nop 1" : "+v"(cv[u + 1]));
+      else asm volatile("" : "+v"(cv[u + 1]));
+    }
+    if constexpr (m.kind[u] == 0) {
+      f8_lat_mfma<NH, f8_lat_k<NH>(i), f8_lat_t0<NH>(i), f8_lat_nt<NH>(), GUARD>(
+          sacc, x.k[f8_lat_k<NH>(i)], fq, e_one, e_lo);
+    } else if constexpr (m.kind[u] == 2) {
+      if constexpr (i == 0) f8_scale_scores<NH>(sacc, x.s, fq.inv_s, scl);
+      if constexpr (GUARD) {
+        if constexpr (NH == 2)
+          mfma_guard(x.r[i][0], x.r[i][1], fq.rope[0][i], fq.rope[1][i]);
+        else
+          mfma_guard(x.r[i][0], x.r[i][1], fq.rope[0][i]);
+      }
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) mfma_sc(sacc[h][t], x.r[i][t], fq.rope[h][i]);
+    } else {
+      if constexpr (GUARD) {
+        if constexpr (NH == 2)
+          mfma_guard(cv[u], pk[0], pk[1]);
+        else
+          mfma_guard(cv[u], pk[0]);
+      }
+#pragma unroll
+      for (int h = 0; h < NH; ++h) mfma_o(oacc[h][i], cv[u], pk[h]);
+    }
+    if constexpr (u >= f8_mid<NH, FT>()) {
+      __builtin_amdgcn_sched_barrier(0);
+      mid(u_c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  });
+}
+
+// One piece of the FP8 chunk's masked softmax: row group H, tile T of the
+// lane's positions (8 gq + 4T + i): p = 2^(s - ref) (0 past the causal limit:
+// lim = the last visible position - 8 gq), summed into psum[H], and p times
+// the token scale rounded into pk[H][4T + i].
+template <int NH, int H, int T>
+__device__ __forceinline__ void softmax_piece_f8(const f32x4 (&sacc)[NH][2], bf16x8 (&pk)[NH],
+                                                 const float (&m_ref)[NH], float (&psum)[NH],
+                                                 const int (&lim)[NH], const float (&scl)[8]) {
+  const float m_use = m_ref[H] == -INFINITY ? 0.f : m_ref[H];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float sv = (4 * T + i > lim[H]) ? -INFINITY : sacc[H][T][i];
+    const float p = __builtin_amdgcn_exp2f(sv - m_use);
+    psum[H] = (T == 0 && i == 0) ? p : psum[H] + p;
+    pk[H][T * 4 + i] = (__bf16)(p * scl[4 * T + i]);
+  }
+}
+
+// Softmax of a whole FP8 chunk (the first chunk of an item, and the restart
+// pass): as softmax_chunk with the FP8 position order and weights.
+template <int NH, bool FIRST>
+__device__ __forceinline__ bool softmax_chunk_f8(const f32x4 (&sacc)[NH][2], bf16x8 (&pk)[NH],
+                                                 float (&m_ref)[NH], float (&l_run)[NH],
+                                                 const int (&lim)[NH], const float (&scl)[8]) {
+  bool restart = false;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    float sv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sv[k] = (k > lim[h]) ? -INFINITY : sacc[h][k >> 2][k & 3];
+    if (FIRST) {
+      float mloc = sv[0];
+#pragma unroll
+      for (int k = 1; k < 8; ++k) mloc = fmaxf(mloc, sv[k]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      m_ref[h] = mloc;
+    }
+    const float m_use = m_ref[h] == -INFINITY ? 0.f : m_ref[h];
+    float psum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float p = __builtin_amdgcn_exp2f(sv[k] - m_use);
+      psum += p;
+      pk[h][k] = (__bf16)(p * scl[k]);
+    }
+    l_run[h] += psum;
+    if (!FIRST) restart |= !(psum <= kSlackPow);
+  }
+  return restart;
+}
+
+// Row max of an FP8 chunk's scores (the first pass of a restart).
+template <int NH>
+__device__ __forceinline__ void max_chunk_f8(const f32x4 (&sacc)[NH][2], float (&m)[NH],
+                                             const int (&lim)[NH]) {
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mloc = fmaxf(mloc, (k > lim[h]) ? -INFINITY : sacc[h][k >> 2][k & 3]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    m[h] = fmaxf(m[h], mloc);
+  }
+}
+
+// Scores of one FP8 chunk alone (the first chunk of an item, the restart
+// passes), scaled, with the chunk's scales in scl.
+template <int NH>
+__device__ __forceinline__ void score_only_f8(const MLA_LDS char* buf, const F8Lane& ln,
+                                              const F8Query<NH>& fq, int e_one, int e_lo,
+                                              f32x4 (&sacc)[NH][2], float (&scl)[8]) {
+  u32x8_t kr[4][2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) f8_read_lat<NH>(kr[k][t], buf + ln.k + f8_kread(k, t));
+  static_for<0, 4>([&](auto k_c) __attribute__((always_inline)) {
+    constexpr int k = decltype(k_c)::value;
+    if constexpr (k + 2 < 4) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) f8_read_lat<NH>(kr[k + 2][t], buf + ln.k + f8_kread(k + 2, t));
+    }
+    f8_lat_mfma<NH, k, 0, 2, true>(sacc, kr[k], fq, e_one, e_lo);
+  });
+  u32x4_t s[2];
+  bf16x8 rr[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    s[t] = *reinterpret_cast<const MLA_LDS u32x4_t*>(buf + kF8ScaleLds + ln.s + 16 * t);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      rr[r][t] = *reinterpret_cast<const MLA_LDS bf16x8*>(buf + ln.k + f8_rread(r, t));
+  }
+  f8_scale_scores<NH>(sacc, s, fq.inv_s, scl);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if constexpr (NH == 2)
+      mfma_guard(rr[r][0], rr[r][1], fq.rope[0][r], fq.rope[1][r]);
+    else
+      mfma_guard(rr[r][0], rr[r][1], fq.rope[0][r]);
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) mfma_sc(sacc[h][t], rr[r][t], fq.rope[h][r]);
+  }
+}
+
+// P.V of one FP8 chunk alone (the last chunk of an item, the restart pass).
+template <int NH, int FT>
+__device__ __forceinline__ void pv_only_f8(const MLA_LDS char* buf, const F8Lane& ln,
+                                           const bf16x8 (&pk)[NH], f32x4 (&oacc)[NH][FT]) {
+  constexpr int A = 4;
+  u32x2_t vr[FT];
+#pragma unroll
+  for (int f = 0; f < A; ++f) vr[f] = ds_read_tr8(buf + ln.v + 16 * f);
+#pragma unroll
+  for (int f = 0; f < FT; ++f) {
+    if (f + A < FT) vr[f + A] = ds_read_tr8(buf + ln.v + 16 * (f + A));
+    const bf16x8 c = fp8x8_to_bf16(vr[f][0], vr[f][1]);
+    if constexpr (NH == 2)
+      mfma_guard(c, pk[0], pk[1]);
+    else
+      mfma_guard(c, pk[0]);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) mfma_o(oacc[h][f], c, pk[h]);
+  }
+}
+
+// The pipelined kernel over FP8 rows (NH, FS as decode_pipe_kernel).
+template <int NH, int FS>
+__global__ __launch_bounds__(256, 1) void decode_pipe_f8_kernel(
+    DecodeArgs a, const int32_t* __restrict__ block_table) {
+  constexpr int NW = 4;
+  constexpr int NS = 4;
+  static_assert(kF8Per * NW * 1024 >= kF8ChunkBytes, "the copies cover the chunk");
+  static_assert(kF8Tail + 512 == kF8ChunkBytes, "two 256-byte tail copies finish it");
+  static_assert(NS * kF8SlotBytes <= 160 * 1024, "the ring fits in LDS");
+  __shared__ __attribute__((aligned(1024))) char ring0[kF8SlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring1[kF8SlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring2[kF8SlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring3[kF8SlotBytes];
+  auto ring = [&](auto slot_c) -> MLA_LDS char* {
+    constexpr int S = decltype(slot_c)::value % NS;
+    if constexpr (S == 0) return (MLA_LDS char*)ring0;
+    else if constexpr (S == 1) return (MLA_LDS char*)ring1;
+    else if constexpr (S == 2) return (MLA_LDS char*)ring2;
+    else return (MLA_LDS char*)ring3;
+  };
+
+  const int gid = blockIdx.x;
+  const int xcd = gid & 7;
+  const int gslot = gid >> 3;
+  const int n_items = a.plan.header[0];
+  const int per_xcd = (n_items + 7) >> 3;
+  const int local = gslot / a.row_groups;
+  const int rg = gslot - local * a.row_groups;
+  const int item = xcd * per_xcd + local;
+  if (local >= per_xcd || item >= n_items) return;
+
+  const int b = a.plan.item_b[item];
+  const int p0 = a.plan.item_p0[item];
+  const int p1 = a.plan.item_p1[item];
+  const int len = a.seq_lens[b];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int gq = lane >> 4;
+  const int g0 = gq & 1;
+  const int g1 = gq >> 1;
+  constexpr int FT = 32 / FS;
+  constexpr int kRowsWg = (NW / FS) * NH * 16;
+  // output tiles short of the 256 accumulation registers: guard the MFMAs
+  constexpr bool kGuard = NH * FT * 4 < 256;
+  const int fslice = wave % FS;
+  const int row0 = rg * kRowsWg + (wave / FS) * 16 * NH;
+  int tmax[NH];
+  int tmax_min = 0x7fffffff;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    tmax[h] = len - a.q_len + (row0 + 16 * h) / a.heads;
+    tmax_min = min(tmax_min, tmax[h]);
+  }
+  F8Lane ln;
+  ln.k = kFp8EntryBytes * (8 * (n >> 2) + (n & 3)) + 16 * (4 * g0 + g1);
+  ln.v = kFp8EntryBytes * (lane >> 1) + 8 * (lane & 1) + 16 * FT * fslice;
+  ln.s = 32 * gq;
+  asm volatile("" : "+v"(ln.k), "+v"(ln.v), "+v"(ln.s));
+  // the absorbed query as FP8 terms (latent) and bf16 (RoPE); the MFMA block
+  // scales in registers; then two wait states before any MFMA reads them
+  int e_one = kE8m0One, e_lo = kE8m0Lo;
+  asm volatile("" : "+v"(e_one), "+v"(e_lo));
+  F8Query<NH> fq;
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+    f8_split_query<NH>(a.q_abs + ((int64_t)b * a.rows_per_seq + row0 + 16 * h + n) * kEntry, g0,
+                       g1, h, fq);
+  asm volatile("s_nop 1" ::: "memory");
+  f32x4 oacc[NH][FT];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int f = 0; f < FT; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[NH], l_run[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    m_ref[h] = -INFINITY;
+    l_run[h] = 0.f;
+  }
+  int* flag = a.restart_flag + blockIdx.x;
+  if (threadIdx.x == 0) __atomic_store_n(flag, 0, __ATOMIC_RELAXED);
+
+  const int tok_begin = p0 * kPage;
+  const int tok_end = min(p1 * kPage, len);
+  const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
+  const int jm = (tmax_min - tok_begin + 1) / kChunk;
+  const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
+  const char* cache = reinterpret_cast<const char*>(a.cache);
+  uint32_t doff[kF8Per];
+  dma_offsets_f8(wave, lane, doff);
+  constexpr int kBtRegs = 4;
+  const int npages = p1 - p0;
+  const bool bt_regs = npages <= 64 * kBtRegs;
+  int btv[kBtRegs];
+#pragma unroll
+  for (int k = 0; k < kBtRegs; ++k) {
+    btv[k] = (bt_regs && 64 * k + lane < npages) ? bt[p0 + 64 * k + lane] : 0;
+    asm volatile("" : "+v"(btv[k]));
+  }
+  auto chunk_copy = [&](auto slot_c, int j) -> ChunkCopy {
+    const bool real = j < nchunks;
+    const int lp = real ? (j >> 1) : 0;
+    int64_t blk;
+    if (bt_regs) {
+      int bb = __builtin_amdgcn_readlane(btv[0], lp & 63);
+#pragma unroll
+      for (int k = 1; k < kBtRegs; ++k) {
+        const int bk = __builtin_amdgcn_readlane(btv[k], lp & 63);
+        bb = (lp >> 6) == k ? bk : bb;
+      }
+      blk = bb;
+    } else {
+      int bb = bt[p0 + lp];
+      asm volatile("" : "+s"(bb));
+      blk = bb;
+    }
+    const int t = tok_begin + lp * kPage + (real ? (j & 1) * kChunk : 0);
+    const int bytes = real ? min(tok_end - t, kChunk) * kFp8EntryBytes : 0;
+    const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kFp8EntryBytes;
+    return ChunkCopy{
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, bytes, kRsrcWord3),
+        ring(slot_c)};
+  };
+  auto issue_all = [&](const ChunkCopy& cc) {
+    static_for<0, kF8Per>([&](auto i_c) __attribute__((always_inline)) {
+      copy_piece_f8<decltype(i_c)::value>(cc, doff, wave);
+    });
+  };
+  auto chunk_limits = [&](int j, int (&lim)[NH]) {
+    const int t0 = tok_begin + j * kChunk;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) lim[h] = tmax[h] - t0 - 8 * gq;
+  };
+  bool need_restart = false;
+  bf16x8 pk[NH];
+  u32x2_t vpre[f8_pre(FT)];
+
+  issue_all(chunk_copy(Slot<0>{}, 0));
+  issue_all(chunk_copy(Slot<1>{}, 1));
+  issue_all(chunk_copy(Slot<2>{}, 2));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * kF8Per>());
+  ring_barrier();
+  {
+    f32x4 sacc[NH][2];
+    float scl[8];
+    int lim[NH];
+    chunk_limits(0, lim);
+    score_only_f8<NH>(ring(Slot<0>{}), ln, fq, e_one, e_lo, sacc, scl);
+    mfma_drain<NH>(sacc);
+    softmax_chunk_f8<NH, true>(sacc, pk, m_ref, l_run, lim, scl);
+  }
+  if (1 < nchunks) f8_prefetch<FT>(vpre, ring(Slot<0>{}), ln);
+  auto interval = [&](auto s_c, int j) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_c)::value;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<kF8Per>());
+    asm volatile("s_barrier" ::: "memory");
+    const ChunkCopy cc = chunk_copy(Slot<S + 3>{}, j + 3);
+    if (j + 1 < nchunks) {
+      f32x4 sacc[NH][2];
+      float scl[8];
+      bf16x8 pk_next[NH];
+      float psum[NH];
+      int lim[NH];
+      chunk_limits(j + 1, lim);
+      fused_interval_f8<NH, FT, kGuard>(
+          ring(Slot<S>{}), pk, oacc, ring(Slot<S + 1>{}), ln, fq, e_one, e_lo, sacc, scl, cc, doff,
+          wave, vpre, [&](auto u_c) __attribute__((always_inline)) {
+            constexpr int k = decltype(u_c)::value - f8_mid<NH, FT>();
+            if constexpr (k == 0) mfma_drain<NH>(sacc);
+            if constexpr (k >= 1 && k <= 2 * NH)
+              softmax_piece_f8<NH, (k - 1) / 2, (k - 1) % 2>(sacc, pk_next, m_ref, psum, lim, scl);
+            if constexpr (k == 2 * NH + 1) {
+#pragma unroll
+              for (int h = 0; h < NH; ++h) {
+                l_run[h] += psum[h];
+                need_restart |= !(psum[h] <= kSlackPow);
+              }
+            }
+          });
+#pragma unroll
+      for (int h = 0; h < NH; ++h) pk[h] = pk_next[h];
+      if (j + 2 < nchunks) f8_prefetch<FT>(vpre, ring(Slot<S + 1>{}), ln);
+    } else if (j < nchunks) {
+      issue_all(cc);
+      pv_only_f8<NH, FT>(ring(Slot<S>{}), ln, pk, oacc);
+    } else {
+      issue_all(cc);
+    }
+  };
+  for (int j = 0; j < nchunks; j += 4) {
+    interval(Slot<0>{}, j);
+    interval(Slot<1>{}, j + 1);
+    interval(Slot<2>{}, j + 2);
+    interval(Slot<3>{}, j + 3);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+  __syncthreads();
+  if (__builtin_amdgcn_ballot_w64(need_restart) != 0 && lane == 0)
+    __atomic_store_n(flag, 1, __ATOMIC_RELAXED);
+  __syncthreads();
+  const bool restart = __atomic_load_n(flag, __ATOMIC_RELAXED) != 0;
+
+  // ---- restart (rare): exact row max, then a pass with it as the reference --
+  if (restart) {
+    auto fetch = [&](int j) -> const MLA_LDS char* {
+      issue_all(chunk_copy(Slot<0>{}, j));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+      __syncthreads();
+      return ring(Slot<0>{});
+    };
+    float m_exact[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) m_exact[h] = -INFINITY;
+    for (int j = 0; j < nchunks; ++j) {
+      const MLA_LDS char* buf = fetch(j);
+      int lim[NH];
+      chunk_limits(j, lim);
+      f32x4 sacc[NH][2];
+      float scl[8];
+      score_only_f8<NH>(buf, ln, fq, e_one, e_lo, sacc, scl);
+      mfma_drain<NH>(sacc);
+      max_chunk_f8<NH>(sacc, m_exact, lim);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      m_ref[h] = m_exact[h];
+      l_run[h] = 0.f;
+    }
+    // (zeroed without reading the old tiles: see decode_pipe_kernel)
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int f = 0; f < FT; ++f) oacc[h][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < nchunks; ++j) {
+      const MLA_LDS char* buf = fetch(j);
+      int lim[NH];
+      chunk_limits(j, lim);
+      f32x4 sacc[NH][2];
+      float scl[8];
+      score_only_f8<NH>(buf, ln, fq, e_one, e_lo, sacc, scl);
+      mfma_drain<NH>(sacc);
+      softmax_chunk_f8<NH, false>(sacc, pk, m_ref, l_run, lim, scl);
+      pin_pk<NH>(pk);
+      pv_only_f8<NH, FT>(buf, ln, pk, oacc);
+      __syncthreads();
+    }
+  }
+  mfma_drain_o<NH, FT>(oacc);
+
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    float l = l_run[h];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float lse = l > 0.f ? m_ref[h] + __builtin_amdgcn_logf(l) : -INFINITY;
+    if (gq == 0 && fslice == 0) a.lse_part[(int64_t)item * a.rows_per_seq + row0 + 16 * h + n] = lse;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t orow = (int64_t)item * a.rows_per_seq + row0 + 16 * h + n;
+    uint16_t* op = a.o_part + orow * kLatent + 16 * FT * fslice + 4 * gq;
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+      u16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(oacc[h][f][i] * inv);
+      *reinterpret_cast<u16x4*>(op + 16 * f) = v;
+    }
+  }
+}
+
 DecodeConfig decode_config(int rows_per_seq) {
   const int groups = rows_per_seq / 16;
   DecodeConfig c;
@@ -1456,9 +2344,9 @@ DecodeConfig decode_config(int rows_per_seq) {
   c.nbuf = 4;
   // rows per workgroup 128, 64, 32 or 16: the pipelined kernel with four
   // wavefronts of their own rows (feature split 1), or pairs / quartets of
-  // wavefronts sharing rows (split 2 / 4).  `waves` and `heads_per_wave`
-  // describe the four-stage kernel with the same rows per workgroup, which
-  // serves the FP8 cache at fewer than 128 rows.
+  // wavefronts sharing rows (split 2 / 4); the FP8 cache at 128 rows takes the
+  // eight-wavefront kernel.  16 * waves * heads_per_wave is the row count the
+  // launch and the split planner work with.
   if (groups % 8 == 0) {
     c.waves = 4;
     c.heads_per_wave = 2;
@@ -1482,19 +2370,6 @@ DecodeConfig decode_config(int rows_per_seq) {
   return c;
 }
 
-template <int NW, int NH>
-static hipError_t launch_t(int grid, bool fp8, const DecodeArgs& args,
-                          const int32_t* block_table, hipStream_t stream) {
-  if (fp8) {
-    hipLaunchKernelGGL((decode_kernel<NW, NH, true>), dim3(grid), dim3(NW * 64), 0, stream, args,
-                       block_table);
-  } else {
-    hipLaunchKernelGGL((decode_kernel<NW, NH, false>), dim3(grid), dim3(NW * 64), 0, stream,
-                       args, block_table);
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_abs, const void* cache,
                          const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
                          int heads, int q_len, PlanView plan, int max_items,
@@ -1515,32 +2390,48 @@ hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_ab
   args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
-  if (cfg.pipe && !(fp8 && cfg.pipe != 1)) {
-    // FP8 rows: the eight-wavefront kernel, same 128 rows per workgroup
-    if (fp8) return launch_t<8, 1>(grid, fp8, args, block_table, stream);
+  if (fp8) {
+    // 128 rows per workgroup: the eight-wavefront kernel (expansion to bf16
+    // in LDS); fewer rows: the pipelined kernel over the FP8 rows
     switch (cfg.pipe) {
       case 1:
-        hipLaunchKernelGGL((decode_pipe_kernel<2, 1>), dim3(grid), dim3(256), 0, stream, args,
+        hipLaunchKernelGGL((decode_kernel<8, 1, true>), dim3(grid), dim3(512), 0, stream, args,
                            block_table);
         break;
       case 2:
-        hipLaunchKernelGGL((decode_pipe_kernel<2, 2>), dim3(grid), dim3(256), 0, stream, args,
+        hipLaunchKernelGGL((decode_pipe_f8_kernel<2, 2>), dim3(grid), dim3(256), 0, stream, args,
                            block_table);
         break;
       case 3:
-        hipLaunchKernelGGL((decode_pipe_kernel<2, 4>), dim3(grid), dim3(256), 0, stream, args,
+        hipLaunchKernelGGL((decode_pipe_f8_kernel<2, 4>), dim3(grid), dim3(256), 0, stream, args,
                            block_table);
         break;
       default:
-        hipLaunchKernelGGL((decode_pipe_kernel<1, 4>), dim3(grid), dim3(256), 0, stream, args,
+        hipLaunchKernelGGL((decode_pipe_f8_kernel<1, 4>), dim3(grid), dim3(256), 0, stream, args,
                            block_table);
         break;
     }
     return hipGetLastError();
   }
-  if (cfg.waves == 2) return launch_t<2, 2>(grid, fp8, args, block_table, stream);
-  if (cfg.heads_per_wave == 2) return launch_t<1, 2>(grid, fp8, args, block_table, stream);
-  return launch_t<1, 1>(grid, fp8, args, block_table, stream);
+  switch (cfg.pipe) {
+    case 1:
+      hipLaunchKernelGGL((decode_pipe_kernel<2, 1>), dim3(grid), dim3(256), 0, stream, args,
+                         block_table);
+      break;
+    case 2:
+      hipLaunchKernelGGL((decode_pipe_kernel<2, 2>), dim3(grid), dim3(256), 0, stream, args,
+                         block_table);
+      break;
+    case 3:
+      hipLaunchKernelGGL((decode_pipe_kernel<2, 4>), dim3(grid), dim3(256), 0, stream, args,
+                         block_table);
+      break;
+    default:
+      hipLaunchKernelGGL((decode_pipe_kernel<1, 4>), dim3(grid), dim3(256), 0, stream, args,
+                         block_table);
+      break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace mla
