@@ -544,13 +544,19 @@ def main():
         if (rec.get("workload") == args.workload and rec.get("kernel_source_sha") == kernel_sha()
                 and rec.get("cache", "bf16") == args.cache):
             traffic = rec.get("bytes_per_launch")
-    dec_kernel = ("mla::decode_kernel (split-KV decode, FP8 rows, eight wavefronts)" if fp8 else
-                  "mla::decode_pipe_kernel (split-KV decode, pipelined)")
+    if not fp8:
+        dec_kernel = "mla::decode_pipe_kernel (split-KV decode, pipelined)"
+    elif (heads * q_len // 16) % 8 == 0:  # 128 query rows per workgroup
+        dec_kernel = "mla::decode_kernel (split-KV decode, FP8 rows, eight wavefronts)"
+    else:
+        dec_kernel = "mla::decode_pipe_f8_kernel (split-KV decode, FP8 rows, pipelined)"
     per_unit = ("656 B per cached position (FP8 row)" if fp8 else
                 "1152 B per cached position (576 bf16)")
-    if wl.decode_bytes(seq_lens, bsz, q_len, heads) / 8.0e12 < alg_flops / 2.5e15:
+    if alg_bytes / 8.0e12 < alg_flops / 2.5e15:
         # more flops per byte than the chip's ridge point (the multi-token
-        # shape): the decode kernel is priced against the bf16 matrix peak
+        # shape; the FP8 rows): the decode kernel is priced against the bf16
+        # matrix peak (the FP8 path runs its products at bf16 precision: two
+        # FP8 products per bf16 one)
         roof = {"kernel": dec_kernel, "bound": "mfma",
                 "achieved": round(dec_tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(dec_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic,
