@@ -191,8 +191,8 @@ def prefill_main(args):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    host_ahead(torch, args.steps, wall * 1e3 / args.steps, warm=step)
     mla.profile_enable(args.steps)
-    host_ahead(torch, args.steps)
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
@@ -341,8 +341,8 @@ def dsa_main(args):
         run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    host_ahead(torch, 2 * args.steps, wall * 1e3 / (2 * args.steps), warm=step)
     mla.profile_enable(2 * args.steps)
-    host_ahead(torch, 2 * args.steps)
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
@@ -496,7 +496,11 @@ def main():
         # each step timed alone with HIP events, the flush outside the events
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
-        host_ahead(torch, args.steps)
+        def flushed_run():
+            flush()
+            run()
+
+        host_ahead(torch, args.steps, 0.0, warm=flushed_run)
         for e0, e1 in evs:
             flush()
             e0.record()
@@ -516,12 +520,15 @@ def main():
     # the same steps again with HIP events recorded by the library around each
     # stage on its launch stream (the events themselves cost a few
     # microseconds, so they stay out of the timed loop above)
-    mla.profile_enable(args.steps)
-    host_ahead(torch, args.steps)
-    for _ in range(args.steps):
+    def flushed_step():
         if cold:
             flush()
         step()
+
+    host_ahead(torch, args.steps, 0.0 if cold else ms_step, warm=flushed_step)
+    mla.profile_enable(args.steps)
+    for _ in range(args.steps):
+        flushed_step()
     torch.cuda.synchronize()
     per_call = mla.profile_collect_calls(args.steps)
     mla.profile_enable(0)
@@ -661,14 +668,28 @@ def copy_ceiling(torch) -> float:
     return 2 * (COPY_MIB << 20) / (best * 1e-3) / 1e9
 
 
-def host_ahead(torch, n_calls: int) -> None:
-    """Queue a bounded GPU-side wait (torch.cuda._sleep: a spin of a few
-    milliseconds) ahead of profiled eager calls, so that the host has queued
-    them all before the GPU reaches them: the library's stage events then
-    time GPU work back to back, not the host's launch latency."""
+HOST_MS_PER_CALL = 0.1  # host time to queue one library call (a few launches and events)
+
+
+def host_ahead(torch, n_calls: int, gpu_ms_per_call: float, warm=None) -> None:
+    """Before event-timed eager calls: make sure the host has queued them all
+    before the GPU reaches them, so that the events time GPU work back to
+    back, not the host's launch latency.  Calls whose GPU time exceeds the
+    host's time to queue them keep the host ahead by themselves: then this
+    only synchronizes (a GPU-side wait before them would leave the chip idle
+    and its clocks low when the timed calls start).  Shorter calls get a
+    bounded GPU-side wait (torch.cuda._sleep: a spin of a few milliseconds),
+    followed by ``warm`` (the timed call itself, untimed) ten times, which
+    brings the clocks back up.  Call it before the timed calls' events are set
+    up."""
     torch.cuda.synchronize()
-    ms = min(50.0, 2.0 + 0.5 * n_calls)
+    if gpu_ms_per_call > HOST_MS_PER_CALL:
+        return
+    ms = min(50.0, 2.0 + 0.5 * (n_calls + 10))
     torch.cuda._sleep(int(ms * 1e-3 * 2.5e9))
+    if warm is not None:
+        for _ in range(10):
+            warm()
 
 
 def kernel_sha(files=("decode.hip", "mla_common.h")) -> str:

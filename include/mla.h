@@ -348,15 +348,18 @@ int mla_dsa_decode_fp8(const mla_dims* dims, const void* q, const void* kv_b, co
  * on its stream: before the prep kernel (query absorption + split plan),
  * before the split-KV decode kernel, before the merge + projection kernel, and
  * after it (for the step entry points the first stage also holds the
-insert).  Events come from a pool of max_calls sets created here
- * (hipEventCreate; no device memory); calls beyond the pool are not timed.
+ * insert).  Events come from a pool of max_calls sets created here
+ * (hipEventCreateWithFlags with hipEventDisableSystemFence: timing only, no
+ * cache write-back at the stage boundaries; no device memory); calls beyond
+ * the pool are not timed.
  * mla_profile_enable(0) releases the pool.  mla_profile_collect waits for the
  * recorded events and writes, per stage, the summed milliseconds over the
  * timed calls into stage_ms[3] (prep, decode, combine) and the call count into
  * *calls, then empties the pool for reuse.  mla_profile_collect_calls writes
  * each timed call's three stage times instead (stage_ms[3 * c + k] for call
- * c in order; MLA_ERR_SHAPE if more than max_calls calls were timed).  Each recorded event adds a few
- * microseconds to the stage it closes.  Not thread-safe; for benchmarks only.
+ * c in order; MLA_ERR_SHAPE if more than max_calls calls were timed).  Each
+ * recorded event adds a few microseconds to the stage it closes.  Not
+ * thread-safe; for benchmarks only.
  */
 int mla_profile_enable(int32_t max_calls);
 int mla_profile_collect(double* stage_ms, int32_t* calls);

@@ -171,8 +171,11 @@ int mla_profile_enable(int32_t max_calls) {
   if (max_calls <= 0) return MLA_OK;
   if (max_calls > 100000) return MLA_ERR_SHAPE;
   g_prof.ev.resize((size_t)max_calls * kMarks);
+  // timing-only events: no system-scope fence when recorded (a fence would
+  // write back and invalidate the caches at every stage boundary, which adds
+  // its own time to the stage and slows the next one)
   for (auto& e : g_prof.ev)
-    if (hipEventCreate(&e) != hipSuccess) return MLA_ERR_HIP;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return MLA_ERR_HIP;
   g_prof.max_calls = max_calls;
   return MLA_OK;
 }
