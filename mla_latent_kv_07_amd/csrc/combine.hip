@@ -52,17 +52,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   const int row_off = (wave / SP) * R;  // first row of this wavefront in the block
   const int ws = wave % SP;             // first split of this wavefront
 
-  // ---- W_UV rows of this wavefront's outputs d in [32w, 32w+32), all of K --
-  // (A operand of D^T = W_UV o_lat^T; independent of the merge, so loaded
-  // first and in flight during it)
+  // W_UV rows of this wavefront's outputs d in [32w, 32w+32), all of K (the
+  // A operand of D^T = W_UV o_lat^T): loaded right after the merge's first
+  // loads, so that they are in flight during the merge.  (Vector loads
+  // complete in order: loaded first, the merge's wait for its partial rows
+  // would also wait for all of W_UV.)
   const uint16_t* wuv = kv_b + ((int64_t)h * (kNope + kVdim) + kNope) * kLatent;
   bf16x8 aw[kLatent / 32][2];
-#pragma unroll
-  for (int ks = 0; ks < kLatent / 32; ++ks)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      aw[ks][mt] = *reinterpret_cast<const bf16x8*>(
-          wuv + (int64_t)(wave * 32 + mt * 16 + n) * kLatent + 32 * ks + 8 * g);
 
   // ---- merge: lane covers 8 columns of each of the wavefront's R rows ------
   // The split weights are lane-parallel (lane s <-> split s, 64 splits per
@@ -106,6 +102,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int k = 0; k < KB; ++k) v0[u][k] = part_row(u, ws + SP * k);
     }
+#pragma unroll
+    for (int ks = 0; ks < kLatent / 32; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        aw[ks][mt] = *reinterpret_cast<const bf16x8*>(
+            wuv + (int64_t)(wave * 32 + mt * 16 + n) * kLatent + 32 * ks + 8 * g);
     int nmax = 0;
 #pragma unroll
     for (int u = 0; u < R; ++u) nmax = max(nmax, ns[u]);
@@ -115,9 +117,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     for (int u = 0; u < R; ++u) {
       mx[u] = lse0[u];
       for (int s = lane + 64; s < ns[u]; s += 64) mx[u] = fmaxf(mx[u], lse_of(u, s));
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) mx[u] = fmaxf(mx[u], __shfl_xor(mx[u], o, 64));
     }
+    // (the rows' reductions interleaved: one exchange latency per step for
+    // all R rows)
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+      for (int u = 0; u < R; ++u) mx[u] = fmaxf(mx[u], __shfl_xor(mx[u], o, 64));
     float macc[R][8];
     float wsum[R];
     // weights of splits 0..63 (lane s <-> split s)
