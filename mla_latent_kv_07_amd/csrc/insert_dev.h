@@ -39,6 +39,37 @@ inline InsertArgs with_rope_freq(InsertArgs a) {
   return a;
 }
 
+// double -> bf16, rounded to nearest even, in integer arithmetic on the
+// double's bits: adding 2^44 - 1 plus the lowest kept bit and dropping the 45
+// low bits rounds the 52-bit mantissa to bf16's 7 (a carry moves into the
+// exponent, and past the largest exponent gives infinity), then the exponent
+// is rebiased from 1023 to 127.  That covers every result that is a normal
+// bf16 or an overflow (biased exponent 897 .. 1150) and magnitudes below
+// 2^-134, which round to zero; the rest (bf16's subnormal range, inf, NaN)
+// goes through f64_to_bf16.  Same value as f64_to_bf16 everywhere, without
+// its emulated round-toward-zero conversion; the other cases are taken only
+// when some lane of the wavefront needs them.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double d) {
+  const uint64_t u = (uint64_t)__double_as_longlong(d);
+  const uint32_t e = (uint32_t)(u >> 52) & 0x7ffu;
+  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+  const uint32_t t = (uint32_t)((u + 0x00000fffffffffffull + ((u >> 45) & 1u)) >> 45);
+  uint16_t r = (uint16_t)(sign | ((t & 0x3ffffu) - (896u << 7)));
+  const bool other = e - 897u > 1150u - 897u;
+  if (__builtin_amdgcn_ballot_w64(other) != 0) {
+    if (other) r = e <= 888u ? (uint16_t)sign : f64_to_bf16(d);
+  }
+  return r;
+}
+
+// float -> bf16, round to nearest even, NaN kept quiet (f32_to_bf16 as a
+// select instead of a branch).
+__device__ __forceinline__ uint16_t f32_to_bf16_sel(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : r);
+}
+
 // RoPE of one interleaved pair (re, im) = elements (2j, 2j+1) of a 64-wide
 // rotary part at position pos ("深度解读DeepSeek：源码解读 DeepSeek-V3",
 // section MLA, apply_rotary_emb with the complex freqs_cis of the Transformer
@@ -57,8 +88,8 @@ __device__ __forceinline__ uint32_t rotate_pair(uint32_t pair, double c, double 
 #pragma clang fp contract(off)
   const double re = (double)bf16_to_f32((uint16_t)(pair & 0xffffu));
   const double im = (double)bf16_to_f32((uint16_t)(pair >> 16));
-  const uint16_t o_re = f64_to_bf16(re * c - im * s);
-  const uint16_t o_im = f64_to_bf16(re * s + im * c);
+  const uint16_t o_re = f64_to_bf16_rne(re * c - im * s);
+  const uint16_t o_im = f64_to_bf16_rne(re * s + im * c);
   return (uint32_t)o_re | ((uint32_t)o_im << 16);
 }
 
@@ -82,8 +113,8 @@ __device__ __forceinline__ void rmsnorm_lane(const InsertArgs& a, const uint16_t
   const double denom = sqrt(ss / (double)kLatent + a.eps);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float nb = bf16_to_f32(f64_to_bf16(x[j] / denom));  // normalised row in bf16
-    y[j] = bf16_to_f32(f32_to_bf16(bf16_to_f32(wv[j]) * nb));  // exact product, one rounding
+    const float nb = bf16_to_f32(f64_to_bf16_rne(x[j] / denom));  // normalised row in bf16
+    y[j] = bf16_to_f32(f32_to_bf16_sel(bf16_to_f32(wv[j]) * nb));  // exact product, one rounding
   }
 }
 
@@ -106,7 +137,7 @@ __device__ __forceinline__ void insert_token_bf16(const InsertArgs& a, int token
   rmsnorm_lane(a, src, lane, y);
   u16x8 yv;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) yv[j] = f32_to_bf16(y[j]);  // exact: y holds bf16 values
+  for (int j = 0; j < 8; ++j) yv[j] = (uint16_t)(__float_as_uint(y[j]) >> 16);  // y holds bf16 values
   *reinterpret_cast<u16x8*>(dst + lane * 8) = yv;
   // k_pe: lane j < 32 rotates pair (2j, 2j+1)
   if (lane < kRope / 2) {

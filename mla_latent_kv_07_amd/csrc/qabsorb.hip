@@ -38,41 +38,42 @@ static_assert(kPlanThreads == 256, "the plan runs on one 256-thread workgroup");
 // Block 0: the split plan (independent work, hidden under the absorption).
 // Blocks 1 .. n_ins (MODE > 0): one per new token, its insert and q_pe.
 // Then 4H blocks: absorption of head k/4, latent columns (k%4)*128 .. +128.
-// q_abs's rope part of heads h0 .. h0 + 2 kQpeBatch - 1 (those below `heads`)
-// of query row `token`: q_pe rotated at the token's position (each head's 32
-// pairs rotated by the 32 angles of that position, see rope_angle), times q_scale,
-// rounded to bf16.  Lane L handles pair L % 32 of heads h0 + L / 32 + 2u.
-// The pairs are loaded first (load_query_pe), so their latency is paid once.
-constexpr int kQpeBatch = 16;
-static_assert(4 * 2 * kQpeBatch >= 128, "four wavefronts cover every head (heads <= 128)");
+// q_abs's rope part of query row `token`, for the heads of one of the
+// kQpeWaves wavefronts that do it: q_pe rotated at the token's position (each
+// head's 32 pairs rotated by the 32 angles of that position, see rope_angle),
+// times q_scale, rounded to bf16.  Lane L of wavefront slot w handles pair
+// L % 32 of heads 2w + L / 32 + 2 kQpeWaves u.  `heads` is even, so whether
+// head 2w + 2 kQpeWaves u + L / 32 exists is the same for both halves of the
+// wavefront: the per-head test is uniform (w is a scalar).  The pairs are
+// loaded first (load_query_pe), so their latency is paid once.
+constexpr int kQpeWaves = 3;
+constexpr int kQpeBatch = (128 + 2 * kQpeWaves - 1) / (2 * kQpeWaves);
 struct QueryPe {
   uint32_t pair[kQpeBatch];
 };
 
 __device__ __forceinline__ void load_query_pe(const uint16_t* __restrict__ q, int heads,
-                                              int token, int lane, int h0, QueryPe& qp) {
-  const int j = lane & 31;
+                                              int token, int lane, int w, QueryPe& qp) {
+  const uint16_t* src =
+      q + ((int64_t)token * heads + 2 * w + (lane >> 5)) * kQk + kNope + 2 * (lane & 31);
 #pragma unroll
-  for (int u = 0; u < kQpeBatch; ++u) {
-    const int h = h0 + (lane >> 5) + 2 * u;
-    const int64_t row = (int64_t)token * heads + min(h, heads - 1);
-    qp.pair[u] = *reinterpret_cast<const uint32_t*>(q + row * kQk + kNope + 2 * j);
-  }
+  for (int u = 0; u < kQpeBatch; ++u)
+    if (2 * w + 2 * kQpeWaves * u < heads)
+      qp.pair[u] = *reinterpret_cast<const uint32_t*>(src + u * 2 * kQpeWaves * kQk);
 }
 
 __device__ __forceinline__ void rotate_query_pe(const QueryPe& qp, int heads, float q_scale,
                                                 uint16_t* __restrict__ q_abs, int token, int lane,
-                                                int h0, double c, double s) {
-  const int j = lane & 31;
+                                                int w, double c, double s) {
+  uint16_t* dst =
+      q_abs + ((int64_t)token * heads + 2 * w + (lane >> 5)) * kEntry + kLatent + 2 * (lane & 31);
 #pragma unroll
   for (int u = 0; u < kQpeBatch; ++u) {
-    const int h = h0 + (lane >> 5) + 2 * u;
-    if (h < heads) {
-      const int64_t row = (int64_t)token * heads + h;
+    if (2 * w + 2 * kQpeWaves * u < heads) {
       const uint32_t rot = rotate_pair(qp.pair[u], c, s);
-      const uint32_t lo = f32_to_bf16(bf16_to_f32((uint16_t)(rot & 0xffffu)) * q_scale);
-      const uint32_t hi = f32_to_bf16(bf16_to_f32((uint16_t)(rot >> 16)) * q_scale);
-      *reinterpret_cast<uint32_t*>(q_abs + row * kEntry + kLatent + 2 * j) = lo | (hi << 16);
+      const uint32_t lo = f32_to_bf16_sel(bf16_to_f32((uint16_t)(rot & 0xffffu)) * q_scale);
+      const uint32_t hi = f32_to_bf16_sel(bf16_to_f32((uint16_t)(rot >> 16)) * q_scale);
+      *reinterpret_cast<uint32_t*>(dst + u * 2 * kQpeWaves * kEntry) = lo | (hi << 16);
     }
   }
 }
@@ -89,16 +90,15 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
     return;
   }
   if (MODE > 0 && (int)blockIdx.x <= n_ins) {
-    // one workgroup per new token: wavefront w rotates q_pe of heads
-    // w * 2 kQpeBatch .. (heads <= 128), wavefront 0 also inserts the token
+    // one workgroup per new token: wavefront 0 inserts the token, wavefronts
+    // 1 .. kQpeWaves rotate its q_pe of every head (heads <= 128); each
+    // computes the token's 32 angles, the same rotation for k_pe and q_pe
+    static_assert(kQpeWaves + 1 == 4, "the insert workgroup is four wavefronts");
     const int token = blockIdx.x - 1;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int h0 = wave * 2 * kQpeBatch;
     QueryPe qp;
-    if (h0 < heads) load_query_pe(q, heads, token, lane, h0, qp);
-    // the token's 32 angles, once: the same rotation serves its k_pe (the
-    // insert) and its q_pe
+    if (wave > 0) load_query_pe(q, heads, token, lane, wave - 1, qp);
     const int pos = token_pos(ia, token);
     double c, s;
     rope_angle(pos, ia.freq[lane & 31], c, s);
@@ -107,8 +107,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
         insert_token_bf16(ia, token, lane, pos, c, s);
       else
         insert_token_fp8(ia, token, lane, pos, c, s);
+    } else {
+      rotate_query_pe(qp, heads, q_scale, q_abs, token, lane, wave - 1, c, s);
     }
-    if (h0 < heads) rotate_query_pe(qp, heads, q_scale, q_abs, token, lane, h0, c, s);
     return;
   }
   MLA_LDS char* w_lds = (MLA_LDS char*)smem;
