@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   const int row_base = blockIdx.y * RB;  // first (b, i) row of this workgroup
   const int total_rows = batch * q_len;
   const int rows_per_seq = heads * q_len;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
@@ -53,12 +53,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   const int ws = wave % SP;             // first split of this wavefront
 
   // W_UV rows of this wavefront's outputs d in [32w, 32w+32), all of K (the
-  // A operand of D^T = W_UV o_lat^T): loaded right after the merge's first
-  // loads, so that they are in flight during the merge.  (Vector loads
-  // complete in order: loaded first, the merge's wait for its partial rows
-  // would also wait for all of W_UV.)
+  // A operand of D^T = W_UV o_lat^T), loaded into registers early so that
+  // they are in flight during the merge.  Loads complete in order, so where
+  // they go matters: with SP = 1 (one merge pass for the V3 shapes) right
+  // after the plan entries, overlapping that round trip; with SP > 1 (several
+  // passes) after the first pass's partial rows, which the merge needs first.
   const uint16_t* wuv = kv_b + ((int64_t)h * (kNope + kVdim) + kNope) * kLatent;
   bf16x8 aw[kLatent / 32][2];
+  auto load_wuv = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < kLatent / 32; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        aw[ks][mt] = *reinterpret_cast<const bf16x8*>(
+            wuv + (int64_t)(wave * 32 + mt * 16 + n) * kLatent + 32 * ks + 8 * g);
+  };
+  constexpr bool kWuvFirst = SP == 1;
 
   // ---- merge: lane covers 8 columns of each of the wavefront's R rows ------
   // The split weights are lane-parallel (lane s <-> split s, 64 splits per
@@ -69,16 +79,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     int s0[R], ns[R];
     int64_t srow[R];
     bool live[R];
+    // The plan entries of the R rows, lane u <-> row u, in two vector loads,
+    // read (the empty asm pins the wait for them) after any loads that can go
+    // out before them: waiting for the entries waits for nothing else.
+    static_assert(R <= 64, "one lane per row");
+    const int lrow = row_base + row_off + min(lane, R - 1);
+    const int lb = lrow < total_rows ? lrow / q_len : 0;
+    const int li = lrow < total_rows ? lrow - lb * q_len : 0;
+    int p_start = plan.seq_start[lb];
+    int p_count = plan.seq_count[lb];
+    if constexpr (kWuvFirst) load_wuv();
+    asm volatile("" : "+v"(p_start), "+v"(p_count) : : "memory");
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      const int bi = row_base + row_off + u;
-      live[u] = bi < total_rows;
-      const int b = live[u] ? bi / q_len : 0;
-      const int i = live[u] ? bi - b * q_len : 0;
-      srow[u] = i * heads + h;
-      s0[u] = plan.seq_start[b];
-      const int cnt = plan.seq_count[b];
-      ns[u] = live[u] ? cnt : 0;  // 0: every weight is 0
+      live[u] = row_base + row_off + u < total_rows;
+      srow[u] = __builtin_amdgcn_readlane(li, u) * heads + h;
+      s0[u] = __builtin_amdgcn_readlane(p_start, u);
+      ns[u] = live[u] ? __builtin_amdgcn_readlane(p_count, u) : 0;  // 0: every weight is 0
     }
     // Loads never sit in a branch: a split index past the row's last split is
     // clamped to that split (its weight there is 0), and a row past the end
@@ -88,26 +105,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
       const int64_t r = (int64_t)split_of(u, s) * rows_per_seq + srow[u];
       return *reinterpret_cast<const u16x8*>(o_part + r * kLatent + lane * 8);
     };
-    auto lse_of = [&](int u, int s) -> float {
-      const float v = lse_part[(int64_t)split_of(u, s) * rows_per_seq + srow[u]];
-      return s < ns[u] ? v : -INFINITY;
+    auto lse_raw = [&](int u, int s) -> float {
+      return lse_part[(int64_t)split_of(u, s) * rows_per_seq + srow[u]];
     };
-    // this wavefront's k-th split is ws + SP k; the first pass: the lse of
-    // splits 0..63 (lane s) and the partial rows of this wavefront's first KB
+    auto lse_of = [&](int u, int s) -> float { return s < ns[u] ? lse_raw(u, s) : -INFINITY; };
+    // this wavefront's k-th split is ws + SP k; the first pass: the partial
+    // rows of this wavefront's first KB splits, then the lse of splits 0..63
+    // (lane s); nothing waits before the last of them is issued.
     float lse0[R];
     u16x8 v0[R][KB];
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      lse0[u] = lse_of(u, lane);
+    for (int u = 0; u < R; ++u)
 #pragma unroll
       for (int k = 0; k < KB; ++k) v0[u][k] = part_row(u, ws + SP * k);
+#pragma unroll
+    for (int u = 0; u < R; ++u) lse0[u] = lse_raw(u, lane);
+    if constexpr (!kWuvFirst) {
+      asm volatile("" : : : "memory");  // W_UV behind the first pass's loads
+      load_wuv();
     }
+    // the lse values are used (masked past the row's last split) only from
+    // here on: no wait is scheduled between the loads above
 #pragma unroll
-    for (int ks = 0; ks < kLatent / 32; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        aw[ks][mt] = *reinterpret_cast<const bf16x8*>(
-            wuv + (int64_t)(wave * 32 + mt * 16 + n) * kLatent + 32 * ks + 8 * g);
+    for (int u = 0; u < R; ++u) {
+      asm volatile("" : "+v"(lse0[u]) : : "memory");
+      lse0[u] = lane < ns[u] ? lse0[u] : -INFINITY;
+    }
     int nmax = 0;
 #pragma unroll
     for (int u = 0; u < R; ++u) nmax = max(nmax, ns[u]);
