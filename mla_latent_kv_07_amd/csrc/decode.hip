@@ -134,6 +134,16 @@ __device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&off)[
   }
 }
 
+// A partial row's four values (an MFMA output tile's lane) times `inv`,
+// rounded to bf16 (nearest even) by the hardware conversion, two values per
+// instruction.
+__device__ __forceinline__ u16x4 scaled_bf16x4(f32x4 x, float inv) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  const bf16x4_t b = {(__bf16)(x[0] * inv), (__bf16)(x[1] * inv), (__bf16)(x[2] * inv),
+                      (__bf16)(x[3] * inv)};
+  return __builtin_bit_cast(u16x4, b);
+}
+
 // Expand the wavefront's FP8 rows of a chunk (RW = 32 / NW rows of
 // kFp8EntryBytes in its region of the ring slot `src`, see Dma) into the
 // bf16 chunk layout the compute reads (1152-byte rows, 16-byte pieces
@@ -843,10 +853,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     uint16_t* op = a.o_part + orow * kLatent + 16 * wave * FT + 4 * gq;
 #pragma unroll
     for (int f = 0; f < FT; ++f) {
-      u16x4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(oacc[g][f][i] * inv);
-      *reinterpret_cast<u16x4*>(op + 16 * f) = v;
+      *reinterpret_cast<u16x4*>(op + 16 * f) = scaled_bf16x4(oacc[g][f], inv);
     }
   }
 }
@@ -1454,10 +1461,7 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
     uint16_t* op = a.o_part + orow * kLatent + 16 * FT * fslice + 4 * gq;
 #pragma unroll
     for (int f = 0; f < FT; ++f) {
-      u16x4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(oacc[h][f][i] * inv);
-      *reinterpret_cast<u16x4*>(op + 16 * f) = v;
+      *reinterpret_cast<u16x4*>(op + 16 * f) = scaled_bf16x4(oacc[h][f], inv);
     }
   }
 }
@@ -2329,10 +2333,7 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_f8_kernel(
     uint16_t* op = a.o_part + orow * kLatent + 16 * FT * fslice + 4 * gq;
 #pragma unroll
     for (int f = 0; f < FT; ++f) {
-      u16x4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(oacc[h][f][i] * inv);
-      *reinterpret_cast<u16x4*>(op + 16 * f) = v;
+      *reinterpret_cast<u16x4*>(op + 16 * f) = scaled_bf16x4(oacc[h][f], inv);
     }
   }
 }
