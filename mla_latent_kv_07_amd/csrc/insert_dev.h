@@ -62,14 +62,6 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double d) {
   return r;
 }
 
-// float -> bf16, round to nearest even, NaN kept quiet (f32_to_bf16 as a
-// select instead of a branch).
-__device__ __forceinline__ uint16_t f32_to_bf16_sel(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : r);
-}
-
 // RoPE of one interleaved pair (re, im) = elements (2j, 2j+1) of a 64-wide
 // rotary part at position pos ("深度解读DeepSeek：源码解读 DeepSeek-V3",
 // section MLA, apply_rotary_emb with the complex freqs_cis of the Transformer
@@ -114,7 +106,7 @@ __device__ __forceinline__ void rmsnorm_lane(const InsertArgs& a, const uint16_t
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float nb = bf16_to_f32(f64_to_bf16_rne(x[j] / denom));  // normalised row in bf16
-    y[j] = bf16_to_f32(f32_to_bf16_sel(bf16_to_f32(wv[j]) * nb));  // exact product, one rounding
+    y[j] = bf16_to_f32(f32_to_bf16(bf16_to_f32(wv[j]) * nb));  // exact product, one rounding
   }
 }
 

@@ -37,10 +37,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // NaN stays NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  // NaN stays NaN (a select, not a branch: no exec-mask work per value)
+  return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? ((u >> 16) | 0x40u) : r);
 }
 // double -> bf16 with a single rounding: truncate to float, mark inexactness
 // in the lowest bit (round-to-odd), then round the float to bf16.  Float keeps

@@ -71,8 +71,8 @@ __device__ __forceinline__ void rotate_query_pe(const QueryPe& qp, int heads, fl
   for (int u = 0; u < kQpeBatch; ++u) {
     if (2 * w + 2 * kQpeWaves * u < heads) {
       const uint32_t rot = rotate_pair(qp.pair[u], c, s);
-      const uint32_t lo = f32_to_bf16_sel(bf16_to_f32((uint16_t)(rot & 0xffffu)) * q_scale);
-      const uint32_t hi = f32_to_bf16_sel(bf16_to_f32((uint16_t)(rot >> 16)) * q_scale);
+      const uint32_t lo = f32_to_bf16(bf16_to_f32((uint16_t)(rot & 0xffffu)) * q_scale);
+      const uint32_t hi = f32_to_bf16(bf16_to_f32((uint16_t)(rot >> 16)) * q_scale);
       *reinterpret_cast<uint32_t*>(dst + u * 2 * kQpeWaves * kEntry) = lo | (hi << 16);
     }
   }
