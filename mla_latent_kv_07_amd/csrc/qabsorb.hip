@@ -78,6 +78,15 @@ __device__ __forceinline__ void rotate_query_pe(const QueryPe& qp, int heads, fl
   }
 }
 
+// The absorption blocks start at the first multiple of 8 after the plan and
+// insert blocks (the blocks in between return at once), and absorption block
+// a = 8 s + x takes head x + 8 (s / 4), column chunk s % 4: the four chunks
+// of a head then have the same block id modulo 8, i.e. run on the same XCD
+// (blocks are dealt to the eight XCDs in turn), and read the head's query
+// rows through one L2.
+static_assert(kLatent / kQaCols == 4, "four column chunks per head");
+__host__ __device__ constexpr int absorb_base(int n_ins) { return (1 + n_ins + 7) & ~7; }
+
 template <int MODE>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ kv_b, int heads,
@@ -113,9 +122,11 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
     return;
   }
   MLA_LDS char* w_lds = (MLA_LDS char*)smem;
-  const int blk = blockIdx.x - 1 - (MODE > 0 ? n_ins : 0);
-  const int h = blk / (kLatent / kQaCols);
-  const int nc = blk % (kLatent / kQaCols);  // column chunk
+  const int base = absorb_base(MODE > 0 ? n_ins : 0);
+  if ((int)blockIdx.x < base) return;
+  const int ab = blockIdx.x - base;
+  const int h = (ab & 7) + 8 * (ab >> 5);  // heads % 8 == 0
+  const int nc = (ab >> 3) & 3;            // column chunk
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -217,7 +228,8 @@ hipError_t launch_prep(const uint16_t* q, const uint16_t* kv_b, int heads, int r
                        int slots, int max_items, int splits_hint, float item_cost_pages,
                        PlanView plan, hipStream_t stream) {
   PlanArgs pa{seq_lens, batch, max_pages, slots, max_items, splits_hint, item_cost_pages, plan};
-  hipLaunchKernelGGL(prep_kernel<0>, dim3(heads * (kLatent / kQaCols) + 1), dim3(256), 0, stream,
+  hipLaunchKernelGGL(prep_kernel<0>, dim3(absorb_base(0) + heads * (kLatent / kQaCols)), dim3(256),
+                     0, stream,
                      q, kv_b, heads, rows, q_scale, q_abs, pa, InsertArgs{}, 0);
   return hipGetLastError();
 }
@@ -229,7 +241,7 @@ hipError_t launch_prep_step(bool fp8, const InsertArgs& ia, const uint16_t* q,
                             PlanView plan, hipStream_t stream) {
   PlanArgs pa{seq_lens, batch, max_pages, slots, max_items, splits_hint, item_cost_pages, plan};
   const int n_ins = rows;  // one workgroup per new token
-  const dim3 grid(1 + n_ins + heads * (kLatent / kQaCols));
+  const dim3 grid(absorb_base(n_ins) + heads * (kLatent / kQaCols));
   if (fp8)
     hipLaunchKernelGGL(prep_kernel<2>, grid, dim3(256), 0, stream, q, kv_b, heads, rows, q_scale,
                        q_abs, pa, ia, n_ins);
