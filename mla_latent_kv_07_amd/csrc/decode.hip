@@ -1447,7 +1447,28 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
   }
   mfma_drain_o<NH, FT>(oacc);
 
-  // ---- finalise: each wavefront normalises its own rows --------------------
+  // ---- finalise: each wavefront normalises its own rows; the workgroup's
+  // rows then leave through LDS as whole 1 KB rows (a 16-byte piece per lane)
+  // rather than as the MFMA tiles' 32-byte pieces of 16 rows.  The ring is
+  // free here: every copy has landed and every wavefront is past its reads.
+  // Staged row r sits in ring slot r / 32 at (r % 32) kOutStride; the stride
+  // (8 dwords past a multiple of the 64 banks) spreads a tile's 8-byte writes
+  // over every bank.
+  constexpr int kOutStride = kLatent * 2 + 32;
+  static_assert(32 * kOutStride <= kBufBytes && kRowsWg <= 32 * NS, "staged rows fit the ring");
+  auto out_slot = [&](int r32) -> MLA_LDS char* {
+    return r32 == 0 ? ring(Slot<0>{})
+                    : r32 == 1 ? ring(Slot<1>{}) : r32 == 2 ? ring(Slot<2>{}) : ring(Slot<3>{});
+  };
+  const int wrow0 = (wave / FS) * 16 * NH;  // this wavefront's first row in the workgroup
+  // the lane indices again, from a value the compiler cannot move above the
+  // chunk loop (addresses derived from them would stay live through it)
+  int lane_f = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane_f));
+  const int n_f = lane_f & 15;
+  const int gq_f = lane_f >> 4;
+  // every row's sum and log-sum-exp first, then the tiles one by one
+  float inv[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     float l = l_run[h];
@@ -1455,14 +1476,30 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
     l += __shfl_xor(l, 32, 64);
     const float lse = l > 0.f ? m_ref[h] + __builtin_amdgcn_logf(l) : -INFINITY;
     // (the FS wavefronts of a row group hold the same sums)
-    if (gq == 0 && fslice == 0) a.lse_part[(int64_t)item * a.rows_per_seq + row0 + 16 * h + n] = lse;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t orow = (int64_t)item * a.rows_per_seq + row0 + 16 * h + n;
-    uint16_t* op = a.o_part + orow * kLatent + 16 * FT * fslice + 4 * gq;
+    if (gq_f == 0 && fslice == 0)
+      a.lse_part[(int64_t)item * a.rows_per_seq + row0 + 16 * h + n_f] = lse;
+    inv[h] = l > 0.f ? 1.f / l : 0.f;
+  }
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int r = wrow0 + 16 * h;
+    MLA_LDS char* dst = out_slot(r >> 5) + ((r & 31) + n_f) * kOutStride +
+                        2 * (16 * FT * fslice + 4 * gq_f);
+    // (each tile written as soon as it is converted: batching the writes
+    // would hold all converted tiles in registers at once)
 #pragma unroll
     for (int f = 0; f < FT; ++f) {
-      *reinterpret_cast<u16x4*>(op + 16 * f) = scaled_bf16x4(oacc[h][f], inv);
+      *reinterpret_cast<MLA_LDS u16x4*>(dst + 32 * f) = scaled_bf16x4(oacc[h][f], inv[h]);
+      asm volatile("" : : : "memory");
     }
+  }
+  __syncthreads();
+  uint16_t* orows = a.o_part + ((int64_t)item * a.rows_per_seq + rg * kRowsWg) * kLatent;
+#pragma unroll 8
+  for (int r = wave; r < kRowsWg; r += 4) {
+    const u16x8 v =
+        *reinterpret_cast<const MLA_LDS u16x8*>(out_slot(r >> 5) + (r & 31) * kOutStride + 16 * lane_f);
+    *reinterpret_cast<u16x8*>(orows + (int64_t)r * kLatent + 8 * lane_f) = v;
   }
 }
 
