@@ -845,15 +845,47 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
     }
   }
   __syncthreads();
+  if constexpr (FP8) {
+    // the rows leave through LDS as whole 1 KB rows (a 16-byte piece per
+    // lane) rather than as the tiles' 32-byte pieces of 16 rows: four row
+    // groups (64 rows, stride 1056 bytes as in decode_pipe_kernel) at a time
+    // in the staging buffer, free here like the ring
+    constexpr int kOutStride = kLatent * 2 + 32;
+    constexpr int kPassG = 4;
+    static_assert(G % kPassG == 0 && kPassG * 16 * kOutStride <= 2 * kBufBytes,
+                  "a pass's rows fit the staging buffer");
+    MLA_LDS char* st = (MLA_LDS char*)stage;
+    uint16_t* orows = a.o_part + ((int64_t)item * a.rows_per_seq + rows0) * kLatent;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float l = lbuf[g * 16 + n];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t orow = (int64_t)item * a.rows_per_seq + rows0 + 16 * g + n;
-    uint16_t* op = a.o_part + orow * kLatent + 16 * wave * FT + 4 * gq;
+    for (int p = 0; p < G / kPassG; ++p) {
 #pragma unroll
-    for (int f = 0; f < FT; ++f) {
-      *reinterpret_cast<u16x4*>(op + 16 * f) = scaled_bf16x4(oacc[g][f], inv);
+      for (int g = p * kPassG; g < (p + 1) * kPassG; ++g) {
+        const float l = lbuf[g * 16 + n];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        MLA_LDS char* dst =
+            st + (16 * (g - p * kPassG) + n) * kOutStride + 2 * (16 * wave * FT + 4 * gq);
+#pragma unroll
+        for (int f = 0; f < FT; ++f)
+          *reinterpret_cast<MLA_LDS u16x4*>(dst + 32 * f) = scaled_bf16x4(oacc[g][f], inv);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = wave; r < kPassG * 16; r += NW) {
+        const u16x8 v = *reinterpret_cast<const MLA_LDS u16x8*>(st + r * kOutStride + 16 * lane);
+        *reinterpret_cast<u16x8*>(orows + (int64_t)(p * kPassG * 16 + r) * kLatent + 8 * lane) = v;
+      }
+      if (p + 1 < G / kPassG) __syncthreads();  // the next pass overwrites the buffer
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float l = lbuf[g * 16 + n];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int64_t orow = (int64_t)item * a.rows_per_seq + rows0 + 16 * g + n;
+      uint16_t* op = a.o_part + orow * kLatent + 16 * wave * FT + 4 * gq;
+#pragma unroll
+      for (int f = 0; f < FT; ++f)
+        *reinterpret_cast<u16x4*>(op + 16 * f) = scaled_bf16x4(oacc[g][f], inv);
     }
   }
 }
@@ -2358,20 +2390,47 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_f8_kernel(
   }
   mfma_drain_o<NH, FT>(oacc);
 
+  // ---- finalise (as decode_pipe_kernel): the rows leave through LDS as
+  // whole 1 KB rows; 16 staged rows per 21 KB ring slot
+  constexpr int kOutStride = kLatent * 2 + 32;
+  static_assert(16 * kOutStride <= kF8SlotBytes && kRowsWg <= 16 * NS, "staged rows fit the ring");
+  auto out_slot = [&](int r16) -> MLA_LDS char* {
+    return r16 == 0 ? ring(Slot<0>{})
+                    : r16 == 1 ? ring(Slot<1>{}) : r16 == 2 ? ring(Slot<2>{}) : ring(Slot<3>{});
+  };
+  const int wrow0 = (wave / FS) * 16 * NH;
+  int lane_f = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane_f));
+  const int n_f = lane_f & 15;
+  const int gq_f = lane_f >> 4;
+  float inv[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     float l = l_run[h];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     const float lse = l > 0.f ? m_ref[h] + __builtin_amdgcn_logf(l) : -INFINITY;
-    if (gq == 0 && fslice == 0) a.lse_part[(int64_t)item * a.rows_per_seq + row0 + 16 * h + n] = lse;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t orow = (int64_t)item * a.rows_per_seq + row0 + 16 * h + n;
-    uint16_t* op = a.o_part + orow * kLatent + 16 * FT * fslice + 4 * gq;
+    if (gq_f == 0 && fslice == 0)
+      a.lse_part[(int64_t)item * a.rows_per_seq + row0 + 16 * h + n_f] = lse;
+    inv[h] = l > 0.f ? 1.f / l : 0.f;
+  }
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int r = wrow0 + 16 * h;
+    MLA_LDS char* dst = out_slot(r >> 4) + n_f * kOutStride + 2 * (16 * FT * fslice + 4 * gq_f);
 #pragma unroll
     for (int f = 0; f < FT; ++f) {
-      *reinterpret_cast<u16x4*>(op + 16 * f) = scaled_bf16x4(oacc[h][f], inv);
+      *reinterpret_cast<MLA_LDS u16x4*>(dst + 32 * f) = scaled_bf16x4(oacc[h][f], inv[h]);
+      asm volatile("" : : : "memory");
     }
+  }
+  __syncthreads();
+  uint16_t* orows = a.o_part + ((int64_t)item * a.rows_per_seq + rg * kRowsWg) * kLatent;
+#pragma unroll 8
+  for (int r = wave; r < kRowsWg; r += 4) {
+    const u16x8 v = *reinterpret_cast<const MLA_LDS u16x8*>(out_slot(r >> 4) +
+                                                          (r & 15) * kOutStride + 16 * lane_f);
+    *reinterpret_cast<u16x8*>(orows + (int64_t)r * kLatent + 8 * lane_f) = v;
   }
 }
 
