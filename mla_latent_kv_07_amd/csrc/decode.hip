@@ -1261,6 +1261,20 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
       asm volatile("" : "+v"(vbase[f4]));
     }
   }
+  // The item's block ids in registers, lane L of btv[k] holding page
+  // p0 + 64 k + L's: a chunk's block is then a lane read, not a scalar load
+  // (whose wait, lgkmcnt(0), would also wait for every LDS read in flight).
+  // Items of more than 256 pages read the table with scalar loads.  Loaded
+  // before the query rows: loads complete in order, so the first copies
+  // (which need the block ids) then wait for these few loads only.
+  const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
+  constexpr int kBtRegs = 4;
+  const int npages = p1 - p0;
+  const bool bt_regs = npages <= 64 * kBtRegs;
+  int btv[kBtRegs];
+#pragma unroll
+  for (int k = 0; k < kBtRegs; ++k)
+    btv[k] = (bt_regs && 64 * k + lane < npages) ? bt[p0 + 64 * k + lane] : 0;
   bf16x8 qreg[NH][18];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
@@ -1269,6 +1283,11 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qreg[h][ks] = qp[4 * ks];
   }
+  // (kept in registers: an indexed form of these would be moved to LDS;
+  // pinned only now, so that the wait for them comes after the query loads
+  // are issued)
+#pragma unroll
+  for (int k = 0; k < kBtRegs; ++k) asm volatile("" : "+v"(btv[k]));
   f32x4 oacc[NH][FT];
 #pragma unroll
   for (int h = 0; h < NH; ++h)
@@ -1287,24 +1306,9 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
   const int tok_end = min(p1 * kPage, len);
   const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
   const int jm = (tmax_min - tok_begin + 1) / kChunk;
-  const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
   const char* cache = reinterpret_cast<const char*>(a.cache);
   uint32_t doff[kPer];
   dma_offsets<NW, kPer, false>(wave, lane, doff);
-  // The item's block ids in registers, lane L of btv[k] holding page
-  // p0 + 64 k + L's: a chunk's block is then a lane read, not a scalar load
-  // (whose wait, lgkmcnt(0), would also wait for every LDS read in flight).
-  // Items of more than 256 pages read the table with scalar loads.
-  constexpr int kBtRegs = 4;
-  const int npages = p1 - p0;
-  const bool bt_regs = npages <= 64 * kBtRegs;
-  int btv[kBtRegs];
-#pragma unroll
-  for (int k = 0; k < kBtRegs; ++k) {
-    btv[k] = (bt_regs && 64 * k + lane < npages) ? bt[p0 + 64 * k + lane] : 0;
-    // (kept in registers: an indexed form of these would be moved to LDS)
-    asm volatile("" : "+v"(btv[k]));
-  }
   auto chunk_copy = [&](auto slot_c, int j) -> ChunkCopy {
     const bool real = j < nchunks;
     const int lp = real ? (j >> 1) : 0;  // page of the item (two chunks a page)
@@ -2202,12 +2206,24 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_f8_kernel(
   // scales in registers; then two wait states before any MFMA reads them
   int e_one = kE8m0One, e_lo = kE8m0Lo;
   asm volatile("" : "+v"(e_one), "+v"(e_lo));
+  // the block ids first (as decode_pipe_kernel): the query split below waits
+  // for its loads, and these then arrive with them rather than after
+  const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
+  constexpr int kBtRegs = 4;
+  const int npages = p1 - p0;
+  const bool bt_regs = npages <= 64 * kBtRegs;
+  int btv[kBtRegs];
+#pragma unroll
+  for (int k = 0; k < kBtRegs; ++k)
+    btv[k] = (bt_regs && 64 * k + lane < npages) ? bt[p0 + 64 * k + lane] : 0;
   F8Query<NH> fq;
 #pragma unroll
   for (int h = 0; h < NH; ++h)
     f8_split_query<NH>(a.q_abs + ((int64_t)b * a.rows_per_seq + row0 + 16 * h + n) * kEntry, g0,
                        g1, h, fq);
   asm volatile("s_nop 1" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < kBtRegs; ++k) asm volatile("" : "+v"(btv[k]));
   f32x4 oacc[NH][FT];
 #pragma unroll
   for (int h = 0; h < NH; ++h)
@@ -2226,19 +2242,9 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_f8_kernel(
   const int tok_end = min(p1 * kPage, len);
   const int nchunks = (tok_end - tok_begin + kChunk - 1) / kChunk;
   const int jm = (tmax_min - tok_begin + 1) / kChunk;
-  const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
   const char* cache = reinterpret_cast<const char*>(a.cache);
   uint32_t doff[kF8Per];
   dma_offsets_f8(wave, lane, doff);
-  constexpr int kBtRegs = 4;
-  const int npages = p1 - p0;
-  const bool bt_regs = npages <= 64 * kBtRegs;
-  int btv[kBtRegs];
-#pragma unroll
-  for (int k = 0; k < kBtRegs; ++k) {
-    btv[k] = (bt_regs && 64 * k + lane < npages) ? bt[p0 + 64 * k + lane] : 0;
-    asm volatile("" : "+v"(btv[k]));
-  }
   auto chunk_copy = [&](auto slot_c, int j) -> ChunkCopy {
     const bool real = j < nchunks;
     const int lp = real ? (j >> 1) : 0;
