@@ -144,6 +144,21 @@ __device__ __forceinline__ u16x4 scaled_bf16x4(f32x4 x, float inv) {
   return __builtin_bit_cast(u16x4, b);
 }
 
+// Partial rows staged in LDS, to be stored as whole rows.  A tile's 8-byte
+// writes are served 16 lanes at a time (one column unit of 16 rows) over 32
+// four-byte banks.  Rows are kStageStride apart, 4 dwords past a multiple of
+// 32 banks, so rows n and n + 8 of a group of 16 would meet; rows 8..15 of
+// every group therefore hold their 8-byte units in swapped pairs (unit u at
+// u ^ 1), and the 16 lanes cover the 32 banks once.  stage_swap(r): whether
+// staged row r is swapped; stage_read: a lane's 16 bytes (units 2l, 2l + 1)
+// of staged row r, in order.
+constexpr int kStageStride = kLatent * 2 + 16;
+__device__ __forceinline__ int stage_swap(int r) { return (r >> 3) & 1; }
+__device__ __forceinline__ u16x8 stage_read(const MLA_LDS char* rows, int r, int lane) {
+  const u16x8 v = *reinterpret_cast<const MLA_LDS u16x8*>(rows + r * kStageStride + 16 * lane);
+  return stage_swap(r) ? __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3) : v;
+}
+
 // Expand the wavefront's FP8 rows of a chunk (RW = 32 / NW rows of
 // kFp8EntryBytes in its region of the ring slot `src`, see Dma) into the
 // bf16 chunk layout the compute reads (1152-byte rows, 16-byte pieces
@@ -848,11 +863,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
   if constexpr (FP8) {
     // the rows leave through LDS as whole 1 KB rows (a 16-byte piece per
     // lane) rather than as the tiles' 32-byte pieces of 16 rows: four row
-    // groups (64 rows, stride 1056 bytes as in decode_pipe_kernel) at a time
-    // in the staging buffer, free here like the ring
-    constexpr int kOutStride = kLatent * 2 + 32;
+    // groups (64 rows, see kStageStride) at a time in the staging buffer,
+    // free here like the ring
     constexpr int kPassG = 4;
-    static_assert(G % kPassG == 0 && kPassG * 16 * kOutStride <= 2 * kBufBytes,
+    static_assert(G % kPassG == 0 && kPassG * 16 * kStageStride <= 2 * kBufBytes,
                   "a pass's rows fit the staging buffer");
     MLA_LDS char* st = (MLA_LDS char*)stage;
     uint16_t* orows = a.o_part + ((int64_t)item * a.rows_per_seq + rows0) * kLatent;
@@ -862,8 +876,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
       for (int g = p * kPassG; g < (p + 1) * kPassG; ++g) {
         const float l = lbuf[g * 16 + n];
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        MLA_LDS char* dst =
-            st + (16 * (g - p * kPassG) + n) * kOutStride + 2 * (16 * wave * FT + 4 * gq);
+        const int sr = 16 * (g - p * kPassG) + n;  // staged row
+        MLA_LDS char* dst = st + sr * kStageStride + 32 * wave * FT + 8 * (gq ^ stage_swap(sr));
 #pragma unroll
         for (int f = 0; f < FT; ++f)
           *reinterpret_cast<MLA_LDS u16x4*>(dst + 32 * f) = scaled_bf16x4(oacc[g][f], inv);
@@ -871,7 +885,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a,
       __syncthreads();
 #pragma unroll
       for (int r = wave; r < kPassG * 16; r += NW) {
-        const u16x8 v = *reinterpret_cast<const MLA_LDS u16x8*>(st + r * kOutStride + 16 * lane);
+        const u16x8 v = stage_read(st, r, lane);
         *reinterpret_cast<u16x8*>(orows + (int64_t)(p * kPassG * 16 + r) * kLatent + 8 * lane) = v;
       }
       if (p + 1 < G / kPassG) __syncthreads();  // the next pass overwrites the buffer
@@ -1487,11 +1501,9 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
   // rows then leave through LDS as whole 1 KB rows (a 16-byte piece per lane)
   // rather than as the MFMA tiles' 32-byte pieces of 16 rows.  The ring is
   // free here: every copy has landed and every wavefront is past its reads.
-  // Staged row r sits in ring slot r / 32 at (r % 32) kOutStride; the stride
-  // (8 dwords past a multiple of the 64 banks) spreads a tile's 8-byte writes
-  // over every bank.
-  constexpr int kOutStride = kLatent * 2 + 32;
-  static_assert(32 * kOutStride <= kBufBytes && kRowsWg <= 32 * NS, "staged rows fit the ring");
+  // Staged row r sits in ring slot r / 32 as its row r % 32 (see
+  // kStageStride).
+  static_assert(32 * kStageStride <= kBufBytes && kRowsWg <= 32 * NS, "staged rows fit the ring");
   auto out_slot = [&](int r32) -> MLA_LDS char* {
     return r32 == 0 ? ring(Slot<0>{})
                     : r32 == 1 ? ring(Slot<1>{}) : r32 == 2 ? ring(Slot<2>{}) : ring(Slot<3>{});
@@ -1519,8 +1531,9 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const int r = wrow0 + 16 * h;
-    MLA_LDS char* dst = out_slot(r >> 5) + ((r & 31) + n_f) * kOutStride +
-                        2 * (16 * FT * fslice + 4 * gq_f);
+    const int sr = (r & 31) + n_f;  // row within the slot
+    MLA_LDS char* dst =
+        out_slot(r >> 5) + sr * kStageStride + 32 * FT * fslice + 8 * (gq_f ^ stage_swap(sr));
     // (each tile written as soon as it is converted: batching the writes
     // would hold all converted tiles in registers at once)
 #pragma unroll
@@ -1533,8 +1546,7 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
   uint16_t* orows = a.o_part + ((int64_t)item * a.rows_per_seq + rg * kRowsWg) * kLatent;
 #pragma unroll 8
   for (int r = wave; r < kRowsWg; r += 4) {
-    const u16x8 v =
-        *reinterpret_cast<const MLA_LDS u16x8*>(out_slot(r >> 5) + (r & 31) * kOutStride + 16 * lane_f);
+    const u16x8 v = stage_read(out_slot(r >> 5), r & 31, lane_f);
     *reinterpret_cast<u16x8*>(orows + (int64_t)r * kLatent + 8 * lane_f) = v;
   }
 }
@@ -2398,8 +2410,7 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_f8_kernel(
 
   // ---- finalise (as decode_pipe_kernel): the rows leave through LDS as
   // whole 1 KB rows; 16 staged rows per 21 KB ring slot
-  constexpr int kOutStride = kLatent * 2 + 32;
-  static_assert(16 * kOutStride <= kF8SlotBytes && kRowsWg <= 16 * NS, "staged rows fit the ring");
+  static_assert(16 * kStageStride <= kF8SlotBytes && kRowsWg <= 16 * NS, "staged rows fit the ring");
   auto out_slot = [&](int r16) -> MLA_LDS char* {
     return r16 == 0 ? ring(Slot<0>{})
                     : r16 == 1 ? ring(Slot<1>{}) : r16 == 2 ? ring(Slot<2>{}) : ring(Slot<3>{});
@@ -2423,7 +2434,8 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_f8_kernel(
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const int r = wrow0 + 16 * h;
-    MLA_LDS char* dst = out_slot(r >> 4) + n_f * kOutStride + 2 * (16 * FT * fslice + 4 * gq_f);
+    MLA_LDS char* dst =
+        out_slot(r >> 4) + n_f * kStageStride + 32 * FT * fslice + 8 * (gq_f ^ stage_swap(n_f));
 #pragma unroll
     for (int f = 0; f < FT; ++f) {
       *reinterpret_cast<MLA_LDS u16x4*>(dst + 32 * f) = scaled_bf16x4(oacc[h][f], inv[h]);
@@ -2434,8 +2446,7 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_f8_kernel(
   uint16_t* orows = a.o_part + ((int64_t)item * a.rows_per_seq + rg * kRowsWg) * kLatent;
 #pragma unroll 8
   for (int r = wave; r < kRowsWg; r += 4) {
-    const u16x8 v = *reinterpret_cast<const MLA_LDS u16x8*>(out_slot(r >> 4) +
-                                                          (r & 15) * kOutStride + 16 * lane_f);
+    const u16x8 v = stage_read(out_slot(r >> 4), r & 15, lane_f);
     *reinterpret_cast<u16x8*>(orows + (int64_t)r * kLatent + 8 * lane_f) = v;
   }
 }
