@@ -161,7 +161,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
       for (int u = 0; u < R; ++u)
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
-          const float w = __shfl(w_l[u], (s + SP * k) & 63, 64);  // 0 beyond ns (lse -inf)
+          // (the split index is uniform: a lane read, not an LDS permute)
+          const float w = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l[u]), (s + SP * k) & 63));
+          // (0 beyond ns: lse -inf)
           wsum[u] = (first && k == 0) ? w : wsum[u] + w;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
