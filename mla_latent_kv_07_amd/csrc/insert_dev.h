@@ -40,24 +40,33 @@ inline InsertArgs with_rope_freq(InsertArgs a) {
 }
 
 // double -> bf16, rounded to nearest even, in integer arithmetic on the
-// double's bits: adding 2^44 - 1 plus the lowest kept bit and dropping the 45
-// low bits rounds the 52-bit mantissa to bf16's 7 (a carry moves into the
+// double's bits u: adding 2^44 - 1 plus the lowest kept bit and dropping the
+// 45 low bits rounds the 52-bit mantissa to bf16's 7 (a carry moves into the
 // exponent, and past the largest exponent gives infinity), then the exponent
 // is rebiased from 1023 to 127.  That covers every result that is a normal
-// bf16 or an overflow (biased exponent 897 .. 1150) and magnitudes below
-// 2^-134, which round to zero; the rest (bf16's subnormal range, inf, NaN)
-// goes through f64_to_bf16.  Same value as f64_to_bf16 everywhere, without
-// its emulated round-toward-zero conversion; the other cases are taken only
-// when some lane of the wavefront needs them.
-__device__ __forceinline__ uint16_t f64_to_bf16_rne(double d) {
-  const uint64_t u = (uint64_t)__double_as_longlong(d);
+// bf16 or an overflow to infinity (biased exponent 897 .. 1150) and
+// magnitudes below 2^-134, which round to a signed zero (exponent 0 .. 888).
+// `covered` is false for the rest (bf16's subnormal band 889 .. 896, and
+// 1151 .. 2047: beyond bf16's range, inf, NaN), whose value this does not
+// give.  Host and device code, so that it can be checked on the CPU.
+__host__ __device__ inline uint16_t f64_bits_to_bf16(uint64_t u, bool& covered) {
   const uint32_t e = (uint32_t)(u >> 52) & 0x7ffu;
   const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
   const uint32_t t = (uint32_t)((u + 0x00000fffffffffffull + ((u >> 45) & 1u)) >> 45);
-  uint16_t r = (uint16_t)(sign | ((t & 0x3ffffu) - (896u << 7)));
-  const bool other = e - 897u > 1150u - 897u;
-  if (__builtin_amdgcn_ballot_w64(other) != 0) {
-    if (other) r = e <= 888u ? (uint16_t)sign : f64_to_bf16(d);
+  covered = e <= 888u || e - 897u <= 1150u - 897u;
+  // (a mask, not a select: the zero case costs no branch around the rest)
+  const uint32_t keep = 0u - (uint32_t)(e > 888u);
+  return (uint16_t)(sign | (((t & 0x3ffffu) - (896u << 7)) & keep));
+}
+
+// f64_to_bf16's value without its emulated round-toward-zero conversion: the
+// integer rounding above, and f64_to_bf16 only when some lane of the
+// wavefront has an input it does not cover.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double d) {
+  bool covered;
+  uint16_t r = f64_bits_to_bf16((uint64_t)__double_as_longlong(d), covered);
+  if (__builtin_amdgcn_ballot_w64(!covered) != 0) {
+    if (!covered) r = f64_to_bf16(d);
   }
   return r;
 }
