@@ -28,13 +28,16 @@ constexpr int kCombRowBytes = kLatent * 2 + 16;  // padded LDS row (bank spread)
 // quarter of the splits each, for few rows with many splits).  Every
 // wavefront weighs its splits by exp2(lse - M) with M the row's maximum over
 // ALL splits, so the SP partial sums of a row simply add (through LDS).
-template <int RB, int SP>
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o_part,
-                                                      const float* __restrict__ lse_part,
-                                                      PlanView plan,
-                                                      const uint16_t* __restrict__ kv_b,
-                                                      int heads, int q_len, int batch,
-                                                      uint16_t* __restrict__ out) {
+//
+// LATE: W_UV is loaded only after the merge, so that its 128 registers are
+// not held through it and two workgroups fit on a CU (launch bounds of two
+// waves per SIMD): for launches of several workgroups per CU, where one
+// workgroup's merge hides the other's W_UV round trip.
+template <int RB, int SP, bool LATE = false>
+__global__ __launch_bounds__(256, LATE ? 2 : 1) void combine_kernel(
+    const uint16_t* __restrict__ o_part, const float* __restrict__ lse_part, PlanView plan,
+    const uint16_t* __restrict__ kv_b, int heads, int q_len, int batch,
+    uint16_t* __restrict__ out) {
   constexpr int R = RB * SP / 4;  // rows per wavefront
   static_assert(R * 4 == RB * SP && RB % R == 0, "four wavefronts: RB / R row groups x SP");
   constexpr int kPartBytes = SP > 1 ? 4 * R * kLatent * 4 : 16;  // fp32 partial sums
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
         aw[ks][mt] = *reinterpret_cast<const bf16x8*>(
             wuv + (int64_t)(wave * 32 + mt * 16 + n) * kLatent + 32 * ks + 8 * g);
   };
-  constexpr bool kWuvFirst = SP == 1;
+  constexpr bool kWuvFirst = SP == 1 && !LATE;
 
   // ---- merge: lane covers 8 columns of each of the wavefront's R rows ------
   // The split weights are lane-parallel (lane s <-> split s, 64 splits per
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
       for (int k = 0; k < KB; ++k) v0[u][k] = part_row(u, ws + SP * k);
 #pragma unroll
     for (int u = 0; u < R; ++u) lse0[u] = lse_raw(u, lane);
-    if constexpr (!kWuvFirst) {
+    if constexpr (!kWuvFirst && !LATE) {
       asm volatile("" : : : "memory");  // W_UV behind the first pass's loads
       load_wuv();
     }
@@ -243,6 +246,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   }
   __syncthreads();
 
+  if constexpr (LATE) load_wuv();
+
   // ---- projection: wave w computes d in [32w, 32w+32) for all rows --------
   constexpr int NT = (RB + 15) / 16;
   f32x4 acc[2][NT];
@@ -286,15 +291,24 @@ hipError_t launch_combine(const uint16_t* o_part, const float* lse_part, PlanVie
                           int cus, hipStream_t stream) {
   const int rows = batch * q_len;
   // the largest row block that still gives every CU a workgroup: W_UV (128
-  // KB per head) is read once per block, so fewer blocks read less
-  if (heads * ((rows + 31) / 32) >= cus) {
+  // KB per head) is read once per block, so fewer blocks read less; with two
+  // or more workgroups per CU the late-W_UV form runs two on a CU at once
+  if (heads * ((rows + 31) / 32) >= 2 * cus) {
+    hipLaunchKernelGGL((combine_kernel<32, 1, true>), dim3(heads, (rows + 31) / 32), dim3(256), 0,
+                       stream, o_part, lse_part, plan, kv_b, heads, q_len, batch, out);
+  } else if (heads * ((rows + 31) / 32) >= cus) {
     hipLaunchKernelGGL((combine_kernel<32, 1>), dim3(heads, (rows + 31) / 32), dim3(256), 0,
                        stream, o_part, lse_part, plan, kv_b, heads, q_len, batch, out);
   } else if (heads * ((rows + 15) / 16) >= cus) {
     hipLaunchKernelGGL((combine_kernel<16, 2>), dim3(heads, (rows + 15) / 16), dim3(256), 0,
                        stream, o_part, lse_part, plan, kv_b, heads, q_len, batch, out);
-  } else {
+  } else if (heads * ((rows + 7) / 8) >= cus) {
     hipLaunchKernelGGL((combine_kernel<8, 4>), dim3(heads, (rows + 7) / 8), dim3(256), 0, stream,
+                       o_part, lse_part, plan, kv_b, heads, q_len, batch, out);
+  } else {
+    // few rows (a small batch): four-row blocks, so twice as many CUs share
+    // the merge (each workgroup still reads its head's W_UV once)
+    hipLaunchKernelGGL((combine_kernel<4, 4>), dim3(heads, (rows + 3) / 4), dim3(256), 0, stream,
                        o_part, lse_part, plan, kv_b, heads, q_len, batch, out);
   }
   return hipGetLastError();
