@@ -287,8 +287,9 @@ def dsa_cpu_baseline(d, budget_s: float) -> dict:
 
 def dsa_main(args):
     """Sparse decode: one step = the insert of the new token (mla_cache_insert)
-    and mla_dsa_decode (index scores, top-k, gather of the kept rows, then
-    prep / decode / combine over them); q_pe arrives rotated.  value = new
+    and mla_dsa_decode (index scores, top-k, the kept rows' slot list or, for
+    the FP8 cache, a gather of the rows, then prep / decode / combine over
+    them); q_pe arrives rotated.  value = new
     tokens per second; the roofline reports the launch that takes the most
     time, against HBM bandwidth."""
     import numpy as np
@@ -358,18 +359,34 @@ def dsa_main(args):
     ms_step = wall * 1e3 / args.steps
     kept = int(np.minimum(seq_lens, top_k).sum())
     kept_lens = np.minimum(seq_lens, top_k)
+    # the library reads bf16 rows in place at 128 heads when a work item's
+    # slot list fits the decode kernel's LDS (at most 4096 kept positions a
+    # sequence) and the cache its 32-bit offsets; otherwise it gathers them
+    kp = (min(top_k, max_len) + 63) // 64
+    in_place = (not fp8 and heads == 128 and kp * 64 <= 4096
+                and d["cache"].shape[0] * 64 * 1152 <= 0xE0000000)
+    if in_place:
+        names = ("index", "topk", "slots", "prep", "decode", "combine")
+        stage = {names[i]: v for i, v in enumerate(stage.values())}
     launches = {
         "index": ("mla::index_score_kernel (FP8 index scores)",
                   wl.index_bytes(seq_lens, bsz, d["index_heads"]),
                   "136 B per cached position (128 B E4M3 key, 4 B scale, 4 B score)",
                   int(seq_lens.sum())),
-        "gather": ("mla::gather_kernel (kept rows into dense pages)", 2 * kept * row_bytes,
-                   f"{2 * row_bytes} B per kept position ({row_bytes} B read, {row_bytes} B "
-                   f"written)", kept),
-        "decode": ("mla::decode_kernel (split-KV decode over the kept rows)",
+        "decode": ("mla::decode_pipe_kernel (split-KV decode over the kept rows, read in place)"
+                   if in_place else "mla::decode_kernel (split-KV decode over the kept rows)",
                    kept * row_bytes, f"{row_bytes} B per kept position "
                    f"({'FP8 row' if fp8 else '576 bf16'})", kept),
     }
+    if in_place:
+        launches["slots"] = ("mla::slot_kernel (cache rows of the kept positions)", 12 * kept,
+                             "12 B per kept position (index and block id read, row written)",
+                             kept)
+    else:
+        launches["gather"] = ("mla::gather_kernel (kept rows into dense pages)",
+                              2 * kept * row_bytes,
+                              f"{2 * row_bytes} B per kept position ({row_bytes} B read, "
+                              f"{row_bytes} B written)", kept)
     dom = max(launches, key=lambda k: stage[k])
     kname, kbytes, per_unit, units = launches[dom]
     gbs = kbytes / (stage[dom] * 1e-3) / 1e9
@@ -383,8 +400,10 @@ def dsa_main(args):
                    "context": "8192 each", "top_k": top_k, "index_heads": d["index_heads"],
                    "page": 64, "kv_lora": 512, "rope": 64,
                    "step": ("mla_cache_insert_fp8 + mla_dsa_decode_fp8" if fp8 else
-                            "mla_cache_insert + mla_dsa_decode") + " (index, top-k, gather, "
-                           "prep, decode, combine)",
+                            "mla_cache_insert + mla_dsa_decode")
+                           + (" (index, top-k, slot list, prep, decode over the kept rows in "
+                              "place, combine)" if in_place else
+                              " (index, top-k, gather, prep, decode, combine)"),
                    "cache": args.cache, "launch": "eager" if args.eager else "hip graph"},
         "stage_ms": {k: round(v, 4) for k, v in stage.items()},
         "stage_gbs": {k: round(launches[k][1] / (stage[k] * 1e-3) / 1e9, 1) for k in launches},

@@ -72,6 +72,13 @@ struct DecodeArgs {
   int q_len;
   int rows_per_seq;
   int row_groups;
+  // Rows in place (the sparse decode): slot list of cache row indices, one
+  // per kept position (rank), `slot_stride` apart per sequence; the cache is
+  // then one buffer of `cache_bytes` bytes.  nullptr: paged through the block
+  // table.
+  const int32_t* slots;
+  int slot_stride;
+  uint32_t cache_bytes;
 };
 
 constexpr int kChunk = 32;                     // positions per LDS stage
@@ -244,7 +251,54 @@ constexpr int kSgDsRead = 0x100;
 struct ChunkCopy {
   __amdgpu_buffer_rsrc_t rsrc;
   MLA_LDS char* dst;
+  uint32_t srow;  // rows in place: lane r holds row r's byte offset in the cache
 };
+
+// Rows in place: the slot list of a work item is staged in LDS (at most
+// kSlotCap positions: 16 KB beside the 144 KB ring), and a row past the end
+// gets an offset beyond any cache buffer, so its copies write zeros.
+constexpr int kSlotCap = 4096;
+constexpr uint32_t kSlotOob = 0xF0000000u;
+constexpr uint32_t kSlotMaxCacheBytes = 0xE0000000u;
+
+// Rows in place, four wavefronts: wavefront w copies rows 8w .. 8w+7 of the
+// chunk (9 KB of the slot: copies k = 9w + i, i = 0..8, each filling LDS
+// pieces 64k .. 64k+63 as in the paged layout).  Copy i's lanes cover rows
+// 8w + row_lo(i) and, from lane row_split(i) on, the next one: both are
+// constants, so a copy's two row offsets are lane reads at fixed lanes of a
+// register whose lane r holds row 8w + r's cache offset.
+constexpr int kRowWaveBytes = 9 * 1024;
+constexpr int row_lo(int i) { return (64 * i) / kChunk16; }
+constexpr int row_split(int i) { return kChunk16 * (row_lo(i) + 1) - 64 * i; }
+static_assert(8 * kEntryBytes == kRowWaveBytes, "a wavefront's nine copies are its eight rows");
+
+// Per lane and copy i of the wavefront's nine: the piece within the row
+// (offset / 16, 7 bits) and whether the lane is in the copy's second row (bit
+// 7), three 8-bit fields a register: off[i / 3] bits 8 (i % 3) .. +7
+// (off[3..8] are left unused).  No lane index stays live through the chunk
+// loop.
+__device__ __forceinline__ void dma_row_offsets(int wave, int lane, uint32_t (&off)[9]) {
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const int q = 64 * i + lane;  // piece within the wavefront's eight rows
+    const int r = q / kChunk16;
+    const int col = q - r * kChunk16;
+    const uint32_t f = (uint32_t)((col ^ swz(8 * wave + r)) | (r > row_lo(i) ? 128 : 0));
+    off[i / 3] = i % 3 == 0 ? f : off[i / 3] | (f << (8 * (i % 3)));
+  }
+}
+
+template <int I>
+__device__ __forceinline__ void row_piece(const ChunkCopy& c, const uint32_t* roff, int wave) {
+  constexpr int lo = row_lo(I);
+  constexpr int hi = lo + 1 < 8 ? lo + 1 : lo;
+  const uint32_t s0 = __builtin_amdgcn_readlane(c.srow, lo);
+  const uint32_t s1 = __builtin_amdgcn_readlane(c.srow, hi);
+  const uint32_t f = __builtin_amdgcn_ubfe(roff[I / 3], 8 * (I % 3), 8);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, c.dst + wave * kRowWaveBytes + I * 1024, 16,
+                                           (f & 128 ? s1 : s0) + 16 * (f & 127), 0, 0,
+                                           kCopyPolicy);
+}
 
 // Copy instruction i of the wavefront's share of a chunk (see load_chunk).
 // (WB, ST: Dma::kWaveBase, Dma::kStride)
@@ -1006,26 +1060,28 @@ constexpr int kFusedAhead = 6;  // LDS reads issued six units ahead
 // The first fused_pre(FT) units are P.V units: they read only the chunk
 // whose probabilities are known, so their LDS reads are issued at the end of
 // the previous interval, before its barrier (their latency hides under it).
-constexpr int fused_pre(int ft) { return ft - 6 < kFusedAhead ? ft - 6 : kFusedAhead; }
+constexpr int fused_pre(int ft, int ah = kFusedAhead) { return ft - 6 < ah ? ft - 6 : ah; }
 // Then the score k-steps: on every other unit of 36 (32 tiles), or on the
 // units that leave six after the last k-step (fewer tiles).
-constexpr int fused_span(int ft) { return ft == 32 ? 36 : kFusedScore + ft - fused_pre(ft) - 6; }
+constexpr int fused_span(int ft, int ah = kFusedAhead) {
+  return ft == 32 ? 36 : kFusedScore + ft - fused_pre(ft, ah) - 6;
+}
 // After unit fused_mid(FT) (the last score k-step) the scores are complete:
 // the softmax of the next chunk runs in pieces between the remaining units.
-constexpr int fused_mid(int ft) {
-  return fused_pre(ft) + (kFusedScore - 1) * fused_span(ft) / kFusedScore;
+constexpr int fused_mid(int ft, int ah = kFusedAhead) {
+  return fused_pre(ft, ah) + (kFusedScore - 1) * fused_span(ft, ah) / kFusedScore;
 }
-template <int FT>
+template <int FT, int AH = kFusedAhead>
 struct FusedMap {
   static constexpr int kUnits = kFusedScore + FT;
-  static_assert(fused_mid(FT) + 6 <= kUnits, "softmax pieces fit after the last k-step");
+  static_assert(fused_mid(FT, AH) + 6 <= kUnits, "softmax pieces fit after the last k-step");
   int kind[kUnits];  // 0: score k-step, 1: P.V feature tile
   int idx[kUnits];   // the k-step or the tile
   int copy[kUnits];  // copy instructions issued at this unit
   constexpr FusedMap(int ncopies) : kind(), idx(), copy() {
     int s = 0, p = 0;
     for (int u = 0; u < kUnits; ++u) {
-      if (s < kFusedScore && u == fused_pre(FT) + s * fused_span(FT) / kFusedScore) {
+      if (s < kFusedScore && u == fused_pre(FT, AH) + s * fused_span(FT, AH) / kFusedScore) {
         kind[u] = 0;
         idx[u] = s++;
       } else {
@@ -1051,11 +1107,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 // chunk at (be, bo), or a P.V feature tile of V^T from the chunk at pv (tile f
 // of the wavefront's slice at vbase[f & 3] + 128 (f >> 2); vbase holds the
 // slice's offset).
-template <int V, int FT>
+template <int V, int FT, int AH = kFusedAhead>
 __device__ __forceinline__ void fused_reads(bf16x8 (&rb)[2], const MLA_LDS char* be,
                                             const MLA_LDS char* bo, const MLA_LDS char* pv,
                                             const int (&vbase)[4]) {
-  constexpr FusedMap<FT> m(0);
+  constexpr FusedMap<FT, AH> m(0);
   constexpr int i = m.idx[V];
   if constexpr (m.kind[V] == 0) {
 #pragma unroll
@@ -1079,37 +1135,37 @@ __device__ __forceinline__ void fused_reads(bf16x8 (&rb)[2], const MLA_LDS char*
 // runs between the units (the next chunk's softmax, see the kernel).
 // The LDS reads of the first fused_pre(FT) units (P.V tiles of the chunk at
 // pv), issued ahead of the interval.
-template <int FT>
-__device__ __forceinline__ void fused_prefetch(bf16x8 (&rb)[kFusedAhead + 1][2],
+template <int FT, int AH = kFusedAhead>
+__device__ __forceinline__ void fused_prefetch(bf16x8 (&rb)[AH + 1][2],
                                                const MLA_LDS char* pv, const int (&vbase)[4]) {
-  static_for<0, fused_pre(FT)>([&](auto v_c) __attribute__((always_inline)) {
+  static_for<0, fused_pre(FT, AH)>([&](auto v_c) __attribute__((always_inline)) {
     constexpr int v = decltype(v_c)::value;
-    fused_reads<v, FT>(rb[v % (kFusedAhead + 1)], nullptr, nullptr, pv, vbase);
+    fused_reads<v, FT, AH>(rb[v % (AH + 1)], nullptr, nullptr, pv, vbase);
   });
 }
 
 // (rb: the read-ahead registers, the first fused_pre(FT) units' reads already
 // issued by fused_prefetch)
-template <int NH, int FT, int KPER, int WB, int ST, class Mid>
+template <int NH, int FT, int KPER, int WB, int ST, bool SLOT, int AH, class Mid>
 __device__ __forceinline__ void fused_interval(const MLA_LDS char* pv, const int (&vbase)[4],
                                                const bf16x8 (&pk)[NH], f32x4 (&oacc)[NH][FT],
                                                const MLA_LDS char* sc, int sbase_even,
                                                int sbase_odd, const bf16x8 (&qreg)[NH][18],
                                                f32x4 (&sacc)[NH][2], const ChunkCopy& cc,
                                                const uint32_t* off, int wave,
-                                               bf16x8 (&rb)[kFusedAhead + 1][2], Mid&& mid) {
-  using M = FusedMap<FT>;
+                                               bf16x8 (&rb)[AH + 1][2], Mid&& mid) {
+  using M = FusedMap<FT, AH>;
   constexpr M m(KPER);
   constexpr int U = M::kUnits;
   const MLA_LDS char* be = sc + sbase_even;
   const MLA_LDS char* bo = sc + sbase_odd;
-  static_for<fused_pre(FT), kFusedAhead>([&](auto v_c) __attribute__((always_inline)) {
+  static_for<fused_pre(FT, AH), AH>([&](auto v_c) __attribute__((always_inline)) {
     constexpr int v = decltype(v_c)::value;
-    fused_reads<v, FT>(rb[v % (kFusedAhead + 1)], be, bo, pv, vbase);
+    fused_reads<v, FT, AH>(rb[v % (AH + 1)], be, bo, pv, vbase);
   });
   static_for<0, U>([&](auto u_c) __attribute__((always_inline)) {
     constexpr int u = decltype(u_c)::value;
-    constexpr int r = u % (kFusedAhead + 1);
+    constexpr int r = u % (AH + 1);
     constexpr int i = m.idx[u];
     constexpr int c0 = [] {
       constexpr M mm(KPER);
@@ -1117,10 +1173,17 @@ __device__ __forceinline__ void fused_interval(const MLA_LDS char* pv, const int
       for (int k = 0; k < u; ++k) c += mm.copy[k];
       return c;
     }();
+    if constexpr (SLOT) {
+      static_assert(KPER == 9, "nine copies a wavefront");
+      static_for<0, m.copy[u]>([&](auto c_c) __attribute__((always_inline)) {
+        row_piece<c0 + decltype(c_c)::value>(cc, off, wave);
+      });
+    } else {
 #pragma unroll
-    for (int c = 0; c < m.copy[u]; ++c) copy_piece<WB, ST>(cc, off, c0 + c, wave);
-    if constexpr (u + kFusedAhead < U)
-      fused_reads<u + kFusedAhead, FT>(rb[(u + kFusedAhead) % (kFusedAhead + 1)], be, bo, pv,
+      for (int c = 0; c < m.copy[u]; ++c) copy_piece<WB, ST>(cc, off, c0 + c, wave);
+    }
+    if constexpr (u + AH < U)
+      fused_reads<u + AH, FT, AH>(rb[(u + AH) % (AH + 1)], be, bo, pv,
                                        vbase);
     if constexpr (m.kind[u] == 0) {
       score_step<NH>(i, rb[r], qreg, sacc);
@@ -1128,7 +1191,7 @@ __device__ __forceinline__ void fused_interval(const MLA_LDS char* pv, const int
 #pragma unroll
       for (int h = 0; h < NH; ++h) mfma_o(oacc[h][i], rb[r][0], pk[h]);
     }
-    if constexpr (u >= fused_mid(FT)) {
+    if constexpr (u >= fused_mid(FT, AH)) {
       // the next chunk's softmax in pieces between the remaining P.V units
       __builtin_amdgcn_sched_barrier(0);
       mid(u_c);
@@ -1207,13 +1270,18 @@ __device__ __forceinline__ void pv_only(const MLA_LDS char* buf, const int (&vba
 // wavefronts share the same NH row groups (each scores them, so each has the
 // probabilities) and take 32 / FS feature tiles each; the workgroup covers
 // (4 / FS) NH 16 rows.
-template <int NH, int FS>
+// SLOT: the rows of each chunk are scattered cache rows named by a slot list
+// (the kept rows of the sparse decode, read in place).
+template <int NH, int FS, bool SLOT = false>
 __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
                                                              const int32_t* __restrict__ block_table) {
   constexpr int NW = 4;
   constexpr int NS = 4;
   using D = Dma<NW, false>;
   constexpr int kPer = D::kPerWave;
+  // LDS read-ahead of the fused intervals, in units (the in-place form's
+  // copy addressing takes the registers of one unit)
+  constexpr int AH = SLOT ? kFusedAhead - 1 : kFusedAhead;
   static_assert(D::kSlotBytes == kBufBytes, "the chunk's copies fill the slot exactly");
   static_assert(NS * kBufBytes <= 160 * 1024, "the ring fits in LDS");
   static_assert(2 * kPer <= 63, "copies in flight within the 6-bit vmcnt");
@@ -1221,6 +1289,8 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
   __shared__ __attribute__((aligned(1024))) char ring1[kBufBytes];
   __shared__ __attribute__((aligned(1024))) char ring2[kBufBytes];
   __shared__ __attribute__((aligned(1024))) char ring3[kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t slot_lds[SLOT ? kSlotCap : 1];
+  static_assert(!SLOT || NS * kBufBytes + 4 * kSlotCap <= 160 * 1024, "slot list beside the ring");
   auto ring = [&](auto slot_c) -> MLA_LDS char* {
     constexpr int S = decltype(slot_c)::value % NS;
     if constexpr (S == 0) return (MLA_LDS char*)ring0;
@@ -1284,11 +1354,23 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
   const int32_t* bt = block_table + (int64_t)b * a.bt_stride;
   constexpr int kBtRegs = 4;
   const int npages = p1 - p0;
-  const bool bt_regs = npages <= 64 * kBtRegs;
+  const bool bt_regs = !SLOT && npages <= 64 * kBtRegs;
   int btv[kBtRegs];
 #pragma unroll
   for (int k = 0; k < kBtRegs; ++k)
     btv[k] = (bt_regs && 64 * k + lane < npages) ? bt[p0 + 64 * k + lane] : 0;
+  // rows in place: the item's slot list into LDS (4 bytes a lane, a
+  // wavefront-uniform number of copies; lanes past the item's end write
+  // zeros), waited for after the query loads are issued
+  const int slot_n = min(p1 * kPage, len) - p0 * kPage;
+  if constexpr (SLOT) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(a.slots + (int64_t)b * a.slot_stride + p0 * kPage), (short)0,
+        4 * slot_n, kRsrcWord3);
+    for (int c = wave; 64 * c < slot_n; c += 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MLA_LDS char*)slot_lds + 256 * c, 4,
+                                               4 * lane + 256 * c, 0, 0, 0);
+  }
   bf16x8 qreg[NH][18];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
@@ -1300,8 +1382,10 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
   // (kept in registers: an indexed form of these would be moved to LDS;
   // pinned only now, so that the wait for them comes after the query loads
   // are issued)
+  if constexpr (!SLOT) {
 #pragma unroll
-  for (int k = 0; k < kBtRegs; ++k) asm volatile("" : "+v"(btv[k]));
+    for (int k = 0; k < kBtRegs; ++k) asm volatile("" : "+v"(btv[k]));
+  }
   f32x4 oacc[NH][FT];
 #pragma unroll
   for (int h = 0; h < NH; ++h)
@@ -1322,8 +1406,28 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
   const int jm = (tmax_min - tok_begin + 1) / kChunk;
   const char* cache = reinterpret_cast<const char*>(a.cache);
   uint32_t doff[kPer];
-  dma_offsets<NW, kPer, false>(wave, lane, doff);
+  if constexpr (SLOT) {
+    static_assert(kPer == 9, "nine copies a wavefront");
+    dma_row_offsets(wave, lane, doff);
+  } else {
+    dma_offsets<NW, kPer, false>(wave, lane, doff);
+  }
+  const __amdgpu_buffer_rsrc_t cache_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(cache), (short)0,
+                                        SLOT ? (int)a.cache_bytes : 0, kRsrcWord3);
   auto chunk_copy = [&](auto slot_c, int j) -> ChunkCopy {
+    if constexpr (SLOT) {
+      // lane r (r < 8; the others repeat them): row 8 wave + r of chunk j,
+      // from the staged slot list
+      // (the lane index recomputed here: held through the chunk loop for
+      // the restart pass it would take a register)
+      int lane_r = threadIdx.x & 7;
+      asm volatile("" : "+v"(lane_r));
+      const int r = kChunk * j + 8 * wave + lane_r;
+      const uint32_t sv = slot_lds[min(r, kSlotCap - 1)];
+      return ChunkCopy{cache_rsrc, ring(slot_c),
+                       r < slot_n ? sv * (uint32_t)kEntryBytes : kSlotOob};
+    }
     const bool real = j < nchunks;
     const int lp = real ? (j >> 1) : 0;  // page of the item (two chunks a page)
     int64_t blk;
@@ -1347,14 +1451,20 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
     const char* src = cache + (blk * kPage + (t % kPage)) * (int64_t)kEntryBytes;
     return ChunkCopy{
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, bytes, kRsrcWord3),
-        ring(slot_c)};
+        ring(slot_c), 0u};
   };
   auto issue_all = [&](const ChunkCopy& cc) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) copy_piece<D::kWaveBase, D::kStride>(cc, doff, i, wave);
+    for (int i = 0; i < kPer; ++i) {
+      if constexpr (!SLOT) copy_piece<D::kWaveBase, D::kStride>(cc, doff, i, wave);
+    }
+    if constexpr (SLOT)
+      static_for<0, 9>([&](auto i_c) __attribute__((always_inline)) {
+        row_piece<decltype(i_c)::value>(cc, doff, wave);
+      });
   };
   // read-ahead registers of the fused intervals (see fused_prefetch)
-  bf16x8 rb[kFusedAhead + 1][2];
+  bf16x8 rb[AH + 1][2];
   auto chunk_limits = [&](int j, int (&lim)[NH]) {
     const int t0 = tok_begin + j * kChunk;
 #pragma unroll
@@ -1375,6 +1485,12 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
   using T = std::true_type;
   using F = std::false_type;
   // prologue: chunks 0..2 in flight; the scores and softmax of chunk 0
+  if constexpr (SLOT) {
+    // the slot list has landed once at most the query loads are pending;
+    // the barrier makes every wavefront's part of it visible
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<NH * 18>());
+    ring_barrier();
+  }
   issue_all(chunk_copy(Slot<0>{}, 0));
   issue_all(chunk_copy(Slot<1>{}, 1));
   issue_all(chunk_copy(Slot<2>{}, 2));
@@ -1386,7 +1502,7 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
     mfma_drain<NH>(sacc);
     softmax(sacc, 0, T{});
   }
-  if (1 < nchunks) fused_prefetch<FT>(rb, ring(Slot<0>{}), vbase);
+  if (1 < nchunks) fused_prefetch<FT, AH>(rb, ring(Slot<0>{}), vbase);
   // interval j: P.V of chunk j (slot j % 4) with the scores of chunk j+1
   // (slot (j+1) % 4); chunk j+3 goes into slot (j+3) % 4, chunk j-1's.
   auto interval = [&](auto s_c, int j) __attribute__((always_inline)) {
@@ -1404,13 +1520,13 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
       float psum[NH];
       int lim[NH];
       chunk_limits(j + 1, lim);
-      fused_interval<NH, FT, kPer, D::kWaveBase, D::kStride>(
+      fused_interval<NH, FT, kPer, D::kWaveBase, D::kStride, SLOT, AH>(
           ring(Slot<S>{}), vbase, pk, oacc, ring(Slot<S + 1>{}), sbase_even, sbase_odd, qreg,
           sacc, cc, doff, wave, rb, [&](auto u_c) __attribute__((always_inline)) {
             // after the last score unit: the wait states, then one piece per
             // P.V unit (the mask is applied to every chunk: no branch splits
             // the interval, and only chunks at the causal limit change)
-            constexpr int k = decltype(u_c)::value - fused_mid(FT);
+            constexpr int k = decltype(u_c)::value - fused_mid(FT, AH);
             if constexpr (k == 0) mfma_drain<NH>(sacc);
             if constexpr (k >= 1 && k <= 2 * NH)
               softmax_piece<NH, (k - 1) / 2, (k - 1) % 2>(sacc, pk_next, m_ref, psum, lim);
@@ -1426,7 +1542,7 @@ __global__ __launch_bounds__(256, 1) void decode_pipe_kernel(DecodeArgs a,
 #pragma unroll
       for (int h = 0; h < NH; ++h) pk[h] = pk_next[h];
       // the next interval's first P.V reads (chunk j+1), before its barrier
-      if (j + 2 < nchunks) fused_prefetch<FT>(rb, ring(Slot<S + 1>{}), vbase);
+      if (j + 2 < nchunks) fused_prefetch<FT, AH>(rb, ring(Slot<S + 1>{}), vbase);
     } else if (j < nchunks) {
       issue_all(cc);
       pv_only<NH, FT>(ring(Slot<S>{}), vbase, pk, oacc);
@@ -2488,8 +2604,12 @@ hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_ab
                          const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
                          int heads, int q_len, PlanView plan, int max_items,
                          uint16_t* o_part, float* lse_part,
-                         int* restart_flags, hipStream_t stream) {
+                         int* restart_flags, hipStream_t stream,
+                         const int32_t* slots, int slot_stride, uint32_t cache_bytes) {
   DecodeArgs args;
+  args.slots = slots;
+  args.slot_stride = slot_stride;
+  args.cache_bytes = cache_bytes;
   args.restart_flag = restart_flags;
   args.q_abs = q_abs;
   args.cache = cache;
@@ -2504,6 +2624,12 @@ hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_ab
   args.row_groups = args.rows_per_seq / (16 * cfg.waves * cfg.heads_per_wave);
   const int items8 = (max_items + 7) / 8;
   const int grid = items8 * 8 * args.row_groups;
+  if (slots) {
+    if (fp8 || cfg.pipe != 1 || cache_bytes > kSlotMaxCacheBytes) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_pipe_kernel<2, 1, true>), dim3(grid), dim3(256), 0, stream, args,
+                       block_table);
+    return hipGetLastError();
+  }
   if (fp8) {
     // 128 rows per workgroup: the eight-wavefront kernel (expansion to bf16
     // in LDS); fewer rows: the pipelined kernel over the FP8 rows
@@ -2547,5 +2673,8 @@ hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_ab
   }
   return hipGetLastError();
 }
+
+int decode_slot_cap() { return kSlotCap; }
+uint32_t decode_slot_cache_limit() { return kSlotMaxCacheBytes; }
 
 }  // namespace mla

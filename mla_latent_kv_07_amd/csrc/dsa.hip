@@ -389,6 +389,21 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ ca
   }
 }
 
+// Slot list of the kept rows: one thread per kept rank, the block-table
+// lookup the gather does, without the row copy (the decode then reads the
+// rows where they are).
+__global__ __launch_bounds__(256) void slot_kernel(const int32_t* __restrict__ block_table,
+                                                   int bt_stride, const int32_t* __restrict__ kept,
+                                                   int top_k, const int32_t* __restrict__ counts,
+                                                   int kpages, int32_t* __restrict__ slots) {
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= counts[b]) return;
+  const int p = kept[(int64_t)b * top_k + j];
+  slots[(int64_t)b * kpages * kPage + j] =
+      block_table[(int64_t)b * bt_stride + p / kPage] * kPage + p % kPage;
+}
+
 hipError_t launch_index_scores(const uint8_t* index_q, const float* index_w, int index_heads,
                                const uint8_t* index_k, const float* index_k_scale,
                                const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
@@ -421,6 +436,14 @@ hipError_t launch_gather(bool fp8, const void* cache, const int32_t* block_table
     hipLaunchKernelGGL(gather_kernel<kEntryBytes>, grid, dim3(256), 0, stream,
                        static_cast<const char*>(cache), block_table, bt_stride, kept, top_k, counts,
                        kpages, static_cast<char*>(dense), dense_bt);
+  return hipGetLastError();
+}
+
+hipError_t launch_slots(const int32_t* block_table, int bt_stride, const int32_t* kept, int top_k,
+                        const int32_t* counts, int batch, int kpages, int32_t* slots,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(slot_kernel, dim3((top_k + 255) / 256, batch), dim3(256), 0, stream,
+                     block_table, bt_stride, kept, top_k, counts, kpages, slots);
   return hipGetLastError();
 }
 

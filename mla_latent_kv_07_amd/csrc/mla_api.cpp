@@ -309,7 +309,7 @@ int decode_any(bool fp8, const InsertArgs* ins, const mla_dims* dims, const void
                const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
                int32_t batch, int32_t q_len, int32_t max_seq_len, float softmax_scale, void* out,
                void* workspace, size_t workspace_bytes, int32_t num_splits_hint, void* stream,
-               int item_cap = 0) {
+               int item_cap = 0, const int32_t* slots = nullptr) {
   int st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (batch < 0 || batch > kMaxBatch || q_len < 1 || q_len > kMaxQLen || max_seq_len < q_len ||
@@ -325,7 +325,8 @@ int decode_any(bool fp8, const InsertArgs* ins, const mla_dims* dims, const void
   const int heads = dims->heads;
   const Layout L = make_layout(heads, batch, q_len, num_splits_hint, item_cap);
   if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
-  if (debug_checks()) {
+  // (rows in place: the slot list comes from a checked block table)
+  if (debug_checks() && !slots) {
     st = check_all_pages(block_table, bt_stride, seq_lens, batch, q_len, max_seq_len, num_blocks,
                          static_cast<hipStream_t>(stream));
     if (st != MLA_OK) return st;
@@ -367,7 +368,8 @@ int decode_any(bool fp8, const InsertArgs* ins, const mla_dims* dims, const void
     e = launch_decode(L.cfg, fp8, q_abs, cache, block_table, bt_stride,
                       seq_lens, heads, q_len, plan,
                       L.max_items, o_part, lse_part,
-                      reinterpret_cast<int*>(ws + L.off_flags), s);
+                      reinterpret_cast<int*>(ws + L.off_flags), s, slots, bt_stride * kPage,
+                      (uint32_t)((int64_t)num_blocks * kPageBytes));
   prof_mark(pc, 2, s);
   if (e == hipSuccess)
     e = launch_combine(o_part, lse_part, plan, static_cast<const uint16_t*>(kv_b), heads, q_len,
@@ -668,6 +670,23 @@ int dsa_any(bool fp8, const mla_dims* dims, const void* q, const void* kv_b, con
   if (e == hipSuccess)
     e = launch_topk(scores, lpad, seq_lens, max_seq_len, batch, top_k, kept, counts, s);
   prof_mark(pc, 2, s);
+  // bf16 rows at 128 rows per workgroup are read in place (a slot list, no
+  // copy) when a work item's slot list fits the kernel's LDS and the cache
+  // its 32-bit buffer offsets; otherwise they are gathered into dense pages
+  const bool in_place = !fp8 && decode_config(dims->heads).pipe == 1 &&
+                        kp * kPage <= decode_slot_cap() &&
+                        (int64_t)num_blocks * kPageBytes <= (int64_t)decode_slot_cache_limit();
+  if (in_place) {
+    int32_t* slots = reinterpret_cast<int32_t*>(dense);  // batch x kp x 64 entries
+    if (e == hipSuccess)
+      e = launch_slots(block_table, bt_stride, kept, top_k, counts, batch, kp, slots, s);
+    prof_mark(pc, 3, s);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    return decode_any(false, nullptr, dims, q, kv_b, cache, num_blocks, slots, kp, counts, batch,
+                      1, ks, softmax_scale, out, ws + L.off_dec,
+                      make_layout(dims->heads, batch, 1, num_splits_hint).total, num_splits_hint,
+                      stream, 0, slots);
+  }
   if (e == hipSuccess)
     e = launch_gather(fp8, cache, block_table, bt_stride, kept, top_k, counts, batch, kp, dense,
                       dense_bt, s);

@@ -98,12 +98,20 @@ struct DecodeConfig {
 };
 DecodeConfig decode_config(int rows_per_seq);
 
-// cache: bf16 rows [.., 64, 576], or FP8 rows [.., 64, 656] when fp8
+// cache: bf16 rows [.., 64, 576], or FP8 rows [.., 64, 656] when fp8.
+// slots != nullptr: rows in place (bf16, 128 rows per workgroup only): the
+// positions of sequence b are cache rows slots[b * slot_stride + t] of a
+// cache of cache_bytes bytes (below decode_slot_cache_limit()), the block
+// table is not read, and an item spans at most decode_slot_cap() positions.
 hipError_t launch_decode(const DecodeConfig& cfg, bool fp8, const uint16_t* q_abs, const void* cache,
                          const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
                          int heads, int q_len, PlanView plan, int max_items,
                          uint16_t* o_part, float* lse_part,
-                         int* restart_flags, hipStream_t stream);
+                         int* restart_flags, hipStream_t stream,
+                         const int32_t* slots = nullptr, int slot_stride = 0,
+                         uint32_t cache_bytes = 0);
+int decode_slot_cap();
+uint32_t decode_slot_cache_limit();
 
 // prefill in the expanded form (prefill.hip): expansion of K/V into kx/vx
 // (bf16 [B][H][lpad][192] / [B][H][lpad][128]), then causal attention; `mid`
@@ -129,6 +137,11 @@ hipError_t launch_topk(const float* scores, int lpad, const int32_t* seq_lens, i
 hipError_t launch_gather(bool fp8, const void* cache, const int32_t* block_table, int bt_stride,
                          const int32_t* kept, int top_k, const int32_t* counts, int batch,
                          int kpages, void* dense, int32_t* dense_bt, hipStream_t stream);
+// The kept rows' cache row indices (block * 64 + slot), for the decode that
+// reads them in place: slots[b * kpages * 64 + j] for rank j < counts[b].
+hipError_t launch_slots(const int32_t* block_table, int bt_stride, const int32_t* kept, int top_k,
+                        const int32_t* counts, int batch, int kpages, int32_t* slots,
+                        hipStream_t stream);
 
 // The no-allocation entry point's device scratch (scratch.hip): its size and
 // the address of the current device's copy.

@@ -145,6 +145,10 @@ SMALL = [
     ("k1", 2, 16, [77, 1], 1, 16),
     # longer than the 16384 positions top-k holds in registers: the re-read path
     ("long_reread", 2, 16, [20000, 300], 3000, 8),
+    # 128 heads: the kept rows read in place (slot list) ...
+    ("h128_in_place", 3, 128, [2500, 40, 700], 1000, 16),
+    # ... and gathered when a sequence keeps more than 4096 positions
+    ("h128_gather_k4200", 2, 128, [4500, 300], 4200, 8),
 ]
 
 
@@ -225,9 +229,9 @@ def test_dsa_keep_all_equals_dense_decode():
 
 def test_dsa_v3_b64_l8192_k2048_sampled():
     """The full-size sparse workload (64 sequences of 8192 cached tokens, 128
-    heads, 64 index heads, top-2048) in the benchmark's launch configuration;
-    every sequence's selection checked, the decode of eight sampled sequences
-    against the oracle."""
+    heads, 64 index heads, top-2048) in the benchmark's launch configuration
+    (kept rows read in place); every sequence's selection and every output
+    element against the oracle."""
     torch = _torch()
     say("dsa v3_b64_l8192 top-2048")
     d = wl.make_workload("v3_b64_l8192")
@@ -237,7 +241,7 @@ def test_dsa_v3_b64_l8192_k2048_sampled():
     scores, idx2, counts = run_select(d, ix, 2048, torch)
     assert np.array_equal(idx, idx2)
     check_selection(d, ix, 2048, scores, idx, counts, range(d["batch"]))
-    check_decode(d, cache, got, idx, 2048, [0, 9, 17, 30, 38, 45, 54, 63])
+    check_decode(d, cache, got, idx, 2048, range(d["batch"]))
     assert np.all(np.isfinite(got))
 
 
