@@ -360,3 +360,16 @@ def test_dsa_decode_split_hint(hint):
     _, idx2, _ = run_select(d, ix, 1500, torch)
     assert np.array_equal(idx, idx2)
     check_decode(d, cache, got, idx, 1500, range(3))
+
+
+def test_dsa_in_place_full_slot_list():
+    """Kept rows read in place with one work item per sequence of 4096 kept
+    positions (num_splits_hint 1): the largest slot list the decode stages
+    (64 pages); the decode within the bound of the oracle."""
+    torch = _torch()
+    say("dsa in place, 4096 kept positions in one item")
+    d = wl.make_inputs(2, 1, 128, [5000, 4100], permute=True, seed=87)
+    ix = wl.make_index_inputs(d, index_heads=16, seed=88)
+    cache = filled(d)
+    got, idx = run_decode(d, cache, ix, 4096, torch, hint=1)
+    check_decode(d, cache, got, idx, 4096, range(2))
