@@ -378,11 +378,7 @@ def dsa_main(args):
                    kept * row_bytes, f"{row_bytes} B per kept position "
                    f"({'FP8 row' if fp8 else '576 bf16'})", kept),
     }
-    if in_place:
-        launches["slots"] = ("mla::slot_kernel (cache rows of the kept positions)", 12 * kept,
-                             "12 B per kept position (index and block id read, row written)",
-                             kept)
-    else:
+    if not in_place:  # (in place, the top-k launch writes the slot list: no launch of its own)
         launches["gather"] = ("mla::gather_kernel (kept rows into dense pages)",
                               2 * kept * row_bytes,
                               f"{2 * row_bytes} B per kept position ({row_bytes} B read, "

@@ -244,8 +244,14 @@ __device__ __forceinline__ void select_digit(const float* sc, int lo, int cnt,
 template <bool REGS>
 __device__ __forceinline__ void topk_body(const float* sc, int len, int kk, int32_t* ob,
                                           int* hist, int* wave_sums, uint32_t* s_prefix,
-                                          int* s_rem) {
+                                          int* s_rem, const int32_t* btb, int32_t* sl) {
   const int tid = threadIdx.x;
+  // a kept position at its rank, and (sl != nullptr: the decode reads the kept
+  // rows in place) its cache row index at the same rank
+  auto put = [&](int rank, int pos) {
+    ob[rank] = pos;
+    if (sl) sl[rank] = btb[pos / kPage] * kPage + pos % kPage;
+  };
   // thread t owns the contiguous positions [lo, lo + cnt)
   const int per = (len + kTopkThreads - 1) / kTopkThreads;
   const int lo = min(tid * per, len);
@@ -290,10 +296,10 @@ __device__ __forceinline__ void topk_body(const float* sc, int len, int kk, int3
       if (i < cnt) {
         const uint32_t k = key[i];
         if (k > thr) {
-          ob[g + min(e, need_eq)] = lo + i;
+          put(g + min(e, need_eq), lo + i);
           ++g;
         } else if (k == thr) {
-          if (e < need_eq) ob[g + e] = lo + i;
+          if (e < need_eq) put(g + e, lo + i);
           ++e;
         }
       }
@@ -302,10 +308,10 @@ __device__ __forceinline__ void topk_body(const float* sc, int len, int kk, int3
     for (int i = 0; i < cnt; ++i) {
       const uint32_t k = score_key(sc[lo + i]);
       if (k > thr) {
-        ob[g + min(e, need_eq)] = lo + i;
+        put(g + min(e, need_eq), lo + i);
         ++g;
       } else if (k == thr) {
-        if (e < need_eq) ob[g + e] = lo + i;
+        if (e < need_eq) put(g + e, lo + i);
         ++e;
       }
     }
@@ -321,7 +327,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
                                                             const int32_t* __restrict__ seq_lens,
                                                             int max_len, int top_k,
                                                             int32_t* __restrict__ out,
-                                                            int32_t* __restrict__ counts) {
+                                                            int32_t* __restrict__ counts,
+                                                            const int32_t* __restrict__ block_table,
+                                                            int bt_stride,
+                                                            int32_t* __restrict__ slots,
+                                                            int slot_stride) {
   __shared__ int hist[256];
   __shared__ int wave_sums[kTopkThreads / 64];
   __shared__ uint32_t s_prefix;
@@ -332,11 +342,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   const int kk = min(top_k, len);
   const float* sc = scores + (int64_t)b * lpad;
   int32_t* ob = out + (int64_t)b * top_k;
+  const int32_t* btb = slots ? block_table + (int64_t)b * bt_stride : nullptr;
+  int32_t* sl = slots ? slots + (int64_t)b * slot_stride : nullptr;
   if (kk > 0) {  // uniform
     if (len <= kTopkThreads * kTopkRegs)
-      topk_body<true>(sc, len, kk, ob, hist, wave_sums, &s_prefix, &s_rem);
+      topk_body<true>(sc, len, kk, ob, hist, wave_sums, &s_prefix, &s_rem, btb, sl);
     else
-      topk_body<false>(sc, len, kk, ob, hist, wave_sums, &s_prefix, &s_rem);
+      topk_body<false>(sc, len, kk, ob, hist, wave_sums, &s_prefix, &s_rem, btb, sl);
   }
   for (int s = kk + tid; s < top_k; s += kTopkThreads) ob[s] = -1;
   if (tid == 0 && counts) counts[b] = kk;
@@ -389,21 +401,6 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ ca
   }
 }
 
-// Slot list of the kept rows: one thread per kept rank, the block-table
-// lookup the gather does, without the row copy (the decode then reads the
-// rows where they are).
-__global__ __launch_bounds__(256) void slot_kernel(const int32_t* __restrict__ block_table,
-                                                   int bt_stride, const int32_t* __restrict__ kept,
-                                                   int top_k, const int32_t* __restrict__ counts,
-                                                   int kpages, int32_t* __restrict__ slots) {
-  const int b = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= counts[b]) return;
-  const int p = kept[(int64_t)b * top_k + j];
-  slots[(int64_t)b * kpages * kPage + j] =
-      block_table[(int64_t)b * bt_stride + p / kPage] * kPage + p % kPage;
-}
-
 hipError_t launch_index_scores(const uint8_t* index_q, const float* index_w, int index_heads,
                                const uint8_t* index_k, const float* index_k_scale,
                                const int32_t* block_table, int bt_stride, const int32_t* seq_lens,
@@ -418,9 +415,12 @@ hipError_t launch_index_scores(const uint8_t* index_q, const float* index_w, int
 }
 
 hipError_t launch_topk(const float* scores, int lpad, const int32_t* seq_lens, int max_seq_len,
-                       int batch, int top_k, int32_t* kept, int32_t* counts, hipStream_t stream) {
+                       int batch, int top_k, int32_t* kept, int32_t* counts, hipStream_t stream,
+                       const int32_t* block_table, int bt_stride, int32_t* slots,
+                       int slot_stride) {
   hipLaunchKernelGGL(topk_kernel, dim3(batch), dim3(kTopkThreads), 0, stream, scores, lpad,
-                     seq_lens, max_seq_len, top_k, kept, counts);
+                     seq_lens, max_seq_len, top_k, kept, counts, block_table, bt_stride, slots,
+                     slot_stride);
   return hipGetLastError();
 }
 
@@ -439,12 +439,5 @@ hipError_t launch_gather(bool fp8, const void* cache, const int32_t* block_table
   return hipGetLastError();
 }
 
-hipError_t launch_slots(const int32_t* block_table, int bt_stride, const int32_t* kept, int top_k,
-                        const int32_t* counts, int batch, int kpages, int32_t* slots,
-                        hipStream_t stream) {
-  hipLaunchKernelGGL(slot_kernel, dim3((top_k + 255) / 256, batch), dim3(256), 0, stream,
-                     block_table, bt_stride, kept, top_k, counts, kpages, slots);
-  return hipGetLastError();
-}
 
 }  // namespace mla

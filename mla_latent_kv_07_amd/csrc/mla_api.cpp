@@ -161,6 +161,17 @@ void prof_mark(int call, int k, hipStream_t s) {
 
 }  // namespace
 
+// The top-k launch (dsa.hip); slots != nullptr: also each kept position's
+// cache row index (block * 64 + slot, through block_table) at
+// slots[b * slot_stride + rank], for the decode that reads the kept rows in
+// place.
+namespace mla {
+hipError_t launch_topk(const float* scores, int lpad, const int32_t* seq_lens, int max_seq_len,
+                       int batch, int top_k, int32_t* kept, int32_t* counts, hipStream_t stream,
+                       const int32_t* block_table, int bt_stride, int32_t* slots,
+                       int slot_stride);
+}  // namespace mla
+
 extern "C" {
 
 int mla_profile_enable(int32_t max_calls) {
@@ -299,6 +310,7 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t q
     return 0;
   return make_layout(dims->heads, batch, q_len, num_splits_hint).total;
 }
+
 
 namespace {
 
@@ -604,8 +616,9 @@ int mla_dsa_select(int32_t index_heads, const void* index_q, const float* index_
                                      static_cast<const uint8_t*>(index_k), index_k_scale,
                                      block_table, bt_stride, seq_lens, batch, max_seq_len, scores,
                                      scores_stride, s);
-  if (e == hipSuccess) e = launch_topk(scores, scores_stride, seq_lens, max_seq_len, batch, top_k, indices,
-                                       counts, s);
+  if (e == hipSuccess)
+    e = launch_topk(scores, scores_stride, seq_lens, max_seq_len, batch, top_k, indices, counts, s,
+                    nullptr, 0, nullptr, 0);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -667,19 +680,21 @@ int dsa_any(bool fp8, const mla_dims* dims, const void* q, const void* kv_b, con
                                      block_table, bt_stride, seq_lens, batch, max_seq_len, scores,
                                      lpad, s);
   prof_mark(pc, 1, s);
-  if (e == hipSuccess)
-    e = launch_topk(scores, lpad, seq_lens, max_seq_len, batch, top_k, kept, counts, s);
-  prof_mark(pc, 2, s);
   // bf16 rows at 128 rows per workgroup are read in place (a slot list, no
-  // copy) when a work item's slot list fits the kernel's LDS and the cache
-  // its 32-bit buffer offsets; otherwise they are gathered into dense pages
+  // copy, written by the top-k launch) when a work item's slot list fits the
+  // decode kernel's LDS and the cache its 32-bit buffer offsets; otherwise
+  // they are gathered into dense pages
   const bool in_place = !fp8 && decode_config(dims->heads).pipe == 1 &&
                         kp * kPage <= decode_slot_cap() &&
                         (int64_t)num_blocks * kPageBytes <= (int64_t)decode_slot_cache_limit();
+  int32_t* slots = reinterpret_cast<int32_t*>(dense);  // batch x kp x 64 entries
+  if (e == hipSuccess)
+    e = launch_topk(scores, lpad, seq_lens, max_seq_len, batch, top_k, kept, counts, s,
+                    in_place ? block_table : nullptr, bt_stride, in_place ? slots : nullptr,
+                    kp * kPage);
+  prof_mark(pc, 2, s);
   if (in_place) {
-    int32_t* slots = reinterpret_cast<int32_t*>(dense);  // batch x kp x 64 entries
-    if (e == hipSuccess)
-      e = launch_slots(block_table, bt_stride, kept, top_k, counts, batch, kp, slots, s);
+    // (the slot list came with the top-k launch)
     prof_mark(pc, 3, s);
     if (e != hipSuccess) return MLA_ERR_HIP;
     return decode_any(false, nullptr, dims, q, kv_b, cache, num_blocks, slots, kp, counts, batch,
