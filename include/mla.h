@@ -315,13 +315,13 @@ int mla_prefill(const mla_dims* dims, const void* q, const void* kv_b, const voi
  *   index_*, top_k: as mla_dsa_select
  *   indices_out  int32 [B, top_k] or NULL: the kept positions
  *   workspace    device memory, >= mla_dsa_workspace_bytes; overwritten
- * Launches on `stream`: index scores, top-k, then either the kept rows'
- * slot list (mla_dsa_decode at 128 heads, at most 4096 kept positions per
- * sequence and a cache of at most 3.5 GiB: the decode reads the kept rows in
- * place) or a gather of the kept rows into dense pages (otherwise, and for
- * mla_dsa_decode_fp8), then the three decode launches.  With profiling
- * enabled a call takes two profile slots: (index scores, top-k, slot list
- * or gather), then (prep, decode, combine).
+ * Launches on `stream`: index scores, then top-k, which for mla_dsa_decode
+ * at 128 heads (at most 4096 kept positions per sequence, a cache of at most
+ * 3.5 GiB) also writes the kept rows' slot list so that the decode reads them
+ * in place; otherwise (and for mla_dsa_decode_fp8) a gather of the kept rows
+ * into dense pages follows; then the three decode launches.  With profiling
+ * enabled a call takes two profile slots: (index scores, top-k, gather or
+ * nothing), then (prep, decode, combine).
  */
 int mla_dsa_select(int32_t index_heads, const void* index_q, const float* index_w,
                    const void* index_k, const float* index_k_scale, const int32_t* block_table,
